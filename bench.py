@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed fp8 MoE FFN layer on one MI355X.
+
+Headline workload: the span-8 decode step (8 rows of one request: 1 committed
+token + 7 drafts; hidden 6144, 256 routed experts top-8, inter 2048 fp8 e4m3
+with 128x128 block scales, one bf16 shared expert of inter 2048).  A step is
+one moe_layer call.  Expert weights are rotated over several device replicas
+so every step reads its weights from HBM, as the pages time the layer with
+every call's weights read from HBM (mstar PR #388, decode table note).
+
+Also measured: the 4096-token prefill over 4 stacked layers with independent
+weights (prefill TFLOPS), and the CPU oracle on the decode step (baseline).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "MoE-layer µs and expert-weight HBM GB/s (% peak), 8-row span step; prefill TFLOPS"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- HIP events via the runtime
+class HipEvents:
+    def __init__(self, n):
+        # the runtime torch already loaded (same soname), never a second copy
+        self.rt = C.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = C.c_void_p()
+            if self.rt.hipEventCreate(C.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h)
+
+    def elapsed_ms(self, a, b) -> float:
+        self.rt.hipEventSynchronize(b)
+        out = C.c_float()
+        if self.rt.hipEventElapsedTime(C.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for h in self.ev:
+            self.rt.hipEventDestroy(h)
+
+
+# ----------------------------------------------------------------------------- device layers
+def device_layer(cfg, layer, torch, moe, replicas=1):
+    """Stream a seeded layer to the GPU expert by expert; `replicas` copies."""
+    import synth
+    d = cfg.dims
+    E, I, H = d.n_experts, d.inter, d.hidden
+    dev = "cuda"
+    reps = []
+    for _ in range(replicas):
+        reps.append(dict(
+            wg=torch.empty((E, I, H), dtype=torch.uint8, device=dev), wu=torch.empty((E, I, H), dtype=torch.uint8, device=dev),
+            wd=torch.empty((E, H, I), dtype=torch.uint8, device=dev),
+            sg=torch.empty((E, I // 128, H // 128), dtype=torch.float32, device=dev),
+            su=torch.empty((E, I // 128, H // 128), dtype=torch.float32, device=dev),
+            sd=torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=dev)))
+    r0 = reps[0]
+
+    def put(e, t):
+        r0["wg"][e].copy_(torch.from_numpy(t["gate"]))
+        r0["wu"][e].copy_(torch.from_numpy(t["up"]))
+        r0["wd"][e].copy_(torch.from_numpy(t["down"]))
+        r0["sg"][e].copy_(torch.from_numpy(t["s_gate"]))
+        r0["su"][e].copy_(torch.from_numpy(t["s_up"]))
+        r0["sd"][e].copy_(torch.from_numpy(t["s_down"]))
+
+    synth.for_each_expert(cfg, layer, put)
+    for r in reps[1:]:
+        for k in r:
+            r[k].copy_(r0[k])
+    sh = synth.shared_expert(cfg, layer)
+    t16 = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)
+    out = []
+    for r in reps:
+        out.append(dict(
+            experts=moe.Experts(r["wg"], r["wu"], r["wd"], r["sg"], r["su"], r["sd"]),
+            shared=moe.Shared(t16(sh["gate"]), t16(sh["up"]), t16(sh["down"])),
+            router_w=t16(synth.router_weight(cfg, layer)),
+            bias=torch.from_numpy(synth.router_bias(cfg, layer)).to(dev)))
+    torch.cuda.synchronize()
+    return out
+
+
+def decode_bytes(nu, d, m):
+    """Algorithmic HBM bytes of one layer step: union experts' fp8 weights and
+    block scales, the bf16 shared expert, the router, x in and y out."""
+    H, I, Is, E = d.hidden, d.inter, d.shared_inter, d.n_experts
+    per_expert = 3 * I * H + 4 * (3 * (I // 128) * (H // 128))
+    routed = nu * per_expert
+    fixed = 3 * Is * H * 2 + E * H * 2 + 4 * E + 2 * m * H * 2
+    return routed, fixed
+
+
+def gateup_bytes(nu, d, m):
+    """Algorithmic bytes of the gate/up kernel: gate and up codes + scales of
+    the union experts, the shared gate/up bf16 weights, x codes and bf16 x."""
+    H, I, Is = d.hidden, d.inter, d.shared_inter
+    return nu * (2 * I * H + 4 * 2 * (I // 128) * (H // 128)) + 2 * Is * H * 2 + m * H * 3 + m * (H // 128) * 4
+
+
+def down_decode_bytes(nu, d, m):
+    H, I, Is = d.hidden, d.inter, d.shared_inter
+    return nu * (I * H + 4 * (H // 128) * (I // 128)) + H * Is * 2 + m * H * 2
+
+
+def layer_flops(d, m_real, slots):
+    H, I, Is = d.hidden, d.inter, d.shared_inter
+    fp8 = 2.0 * slots * (2 * I * H + I * H)
+    bf16 = 2.0 * m_real * 3 * Is * H
+    router = 2.0 * m_real * d.n_experts * H
+    return fp8, bf16, router
+
+
+def cpu_info():
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    model = platform.processor()
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return threads, model
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4, help="device copies of the decode layer's weights")
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs the layer on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path has no inter-GPU sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import sparse_moe_ffn_02_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = moe.load()
+    torch.cuda.set_device(0)
+
+    # ---------------- decode: span-8 step
+    cfg = synth.CONFIGS["span8"]
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.n_experts, d.top_k, d.inter, d.shared_inter, d.routed_scale)
+    t0 = time.time()
+    log(f"[bench] generating span8 layer (seed {cfg.seed}) x{args.replicas} replicas")
+    reps = device_layer(cfg, 0, torch, moe, replicas=args.replicas)
+    log(f"[bench] layer ready in {time.time() - t0:.1f}s")
+    x_np, mask_np = synth.activations(cfg)
+    M = cfg.rows
+    x = torch.from_numpy(x_np.view(np.int16)).cuda()
+    mask = torch.from_numpy(mask_np).cuda()
+    ws = moe.workspace(md, M)
+    y = torch.empty((M, d.hidden), dtype=torch.int16, device="cuda")
+    rt = moe.Routing.empty(md, M)
+
+    def step(i):
+        r = reps[i % len(reps)]
+        moe.layer(md, x, mask, r["router_w"], r["bias"], r["experts"], r["shared"], y, rt, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nu = int(rt.n_union.item())
+    slots = int(rt.offs[nu].item())
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+    rt_lib = ev.rt
+    rt_lib.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+    torch.cuda.synchronize()
+    rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+    for i in range(args.steps):
+        step(i)
+    rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+    torch.cuda.synchronize()
+    ms_step = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.steps
+    routed_b, fixed_b = decode_bytes(nu, d, M)
+    total_b = routed_b + fixed_b
+    gbs = total_b / (ms_step * 1e-3) / 1e9
+    log(f"[bench] span8: {ms_step * 1e3:.1f} us/step, |U|={nu}, {total_b / 1e6:.1f} MB -> {gbs:.0f} GB/s")
+
+    # traced pass: per-kernel HIP events, same steps, same stream
+    nk = 16
+    tev = HipEvents(2 * nk * args.steps)
+    pairs = (C.c_void_p * (2 * nk * args.steps))(*[h.value for h in tev.ev])
+    kid = (C.c_int32 * (nk * args.steps))()
+    cnt = C.c_int32(0)
+    assert lib.moe_trace_set(pairs, nk * args.steps, kid, C.byref(cnt)) == 0
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    lib.moe_trace_set(None, 0, None, None)
+    per = {}
+    for i in range(cnt.value):
+        name = lib.moe_kernel_name(kid[i]).decode()
+        per.setdefault(name, []).append(tev.elapsed_ms(tev.ev[2 * i], tev.ev[2 * i + 1]))
+    kern_us = {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
+    tev.close()
+    dom = max(kern_us, key=lambda k: kern_us[k])
+    dom_bytes = {"gateup": gateup_bytes(nu, d, M), "down_combine_decode": down_decode_bytes(nu, d, M)}.get(dom)
+    if dom_bytes is None:
+        dom_bytes = total_b
+    dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+    log(f"[bench] kernels (us): " + ", ".join(f"{k}={v:.1f}" for k, v in kern_us.items()))
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "span-8 decode step: 8 rows of one request (1 committed + 7 drafts), hidden 6144, "
+                               "256 routed experts top-8, inter 2048 fp8 e4m3 128x128 block scales, "
+                               "1 bf16 shared expert inter 2048; weights rotated over "
+                               f"{args.replicas} device replicas (read from HBM every step)",
+                   "rows": M, "union_experts": nu, "slots": slots, "seed": cfg.seed},
+        "layer_us": round(ms_step * 1e3, 2),
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "bytes_per_step": total_b,
+        "routed_weight_bytes": routed_b,
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+    # ---------------- CPU oracle baseline on the same decode step
+    if not args.no_cpu_baseline:
+        import oracle
+        threads, model = cpu_info()
+        host = {}
+
+        def expert(e):
+            if e not in host:
+                r = reps[0]["experts"]
+                host[e] = {k: getattr(r, a)[e].cpu().numpy() for k, a in
+                           (("gate", "w_gate"), ("up", "w_up"), ("down", "w_down"),
+                            ("s_gate", "s_gate"), ("s_up", "s_up"), ("s_down", "s_down"))}
+            return host[e]
+        sh = synth.shared_expert(cfg, 0)
+        wr = synth.router_weight(cfg, 0)
+        b = synth.router_bias(cfg, 0)
+        for e in rt.union_ids[:nu].cpu().numpy():
+            expert(int(e))
+        log(f"[bench] CPU oracle on the span8 step ({threads} threads)")
+        c0 = time.time()
+        oracle.layer(x_np, mask_np, wr, b, d.top_k, d.routed_scale, expert, sh)
+        cpu_s = time.time() - c0
+        result["cpu_baseline"] = {"value": round(total_b / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"one whole span-8 step ({M} rows, |U|={nu}) in {cpu_s:.2f} s on "
+                                            f"{model}; float64 numpy",
+                                  "seconds": round(cpu_s, 3)}
+        log(f"[bench] oracle: {cpu_s:.2f} s")
+    del reps
+    torch.cuda.empty_cache()
+
+    # ---------------- prefill: 4096 tokens over 4 stacked layers
+    if not args.no_prefill:
+        pcfg = synth.CONFIGS["prefill4096x4"]
+        layers = []
+        for l in range(pcfg.n_layers):
+            t0 = time.time()
+            layers.append(device_layer(pcfg, l, torch, moe, replicas=1)[0])
+            log(f"[bench] prefill layer {l} ready in {time.time() - t0:.1f}s")
+        Mp = pcfg.rows
+        xs = [torch.from_numpy(synth.activations(pcfg, layer=l)[0].view(np.int16)).cuda() for l in range(pcfg.n_layers)]
+        wsp = moe.workspace(md, Mp)
+        yp = torch.empty((Mp, d.hidden), dtype=torch.int16, device="cuda")
+        rts = [moe.Routing.empty(md, Mp) for _ in layers]
+
+        def pstep():
+            for l, L in enumerate(layers):
+                moe.layer(md, xs[l], None, L["router_w"], L["bias"], L["experts"], L["shared"], yp, rts[l], wsp)
+
+        pstep()
+        torch.cuda.synchronize()
+        rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+        for _ in range(args.prefill_steps):
+            pstep()
+        rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+        torch.cuda.synchronize()
+        ms_p = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.prefill_steps
+        f8 = f16 = fr = 0.0
+        pbytes = 0
+        loads = []
+        for l in range(pcfg.n_layers):
+            nu_l = int(rts[l].n_union.item())
+            sl = int(rts[l].offs[nu_l].item())
+            a, b_, c_ = layer_flops(d, Mp, sl)
+            f8 += a; f16 += b_; fr += c_
+            rb, fb = decode_bytes(nu_l, d, Mp)
+            pbytes += rb + fb
+            loads.append(np.diff(rts[l].offs[:nu_l + 1].cpu().numpy()))
+        t_s = ms_p * 1e-3
+        result["prefill"] = {
+            "workload": "4096-token prefill chunk over 4 stacked MoE layers (independent seeded weights, per-layer "
+                        "seeded inputs), Zipf(1.1) router bias, same layer shape",
+            "ms_per_step": round(ms_p, 4), "ms_per_layer": round(ms_p / pcfg.n_layers, 4),
+            "tflops_total": round((f8 + f16 + fr) / t_s / 1e12, 2),
+            "tflops_fp8": round(f8 / t_s / 1e12, 2),
+            "fp8_mfma_frac": round(f8 / t_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "mfma_composite_frac": round((f8 / 1e12 / FP8_PEAK_TFLOPS + f16 / 1e12 / BF16_PEAK_TFLOPS) / t_s, 4),
+            "hbm_frac": round(pbytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
+            "expert_rows_max": int(max(l.max() for l in loads)),
+            "expert_rows_mean": round(float(np.mean([l.mean() for l in loads])), 1),
+        }
+        log(f"[bench] prefill4096x4: {ms_p:.2f} ms/step, {result['prefill']['tflops_total']} TFLOPS")
+    ev.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

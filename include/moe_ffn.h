@@ -1,0 +1,192 @@
+/*
+ * moe_ffn.h -- C ABI of the routed fp8 mixture-of-experts FFN layer on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the routed MoE block of a GLM-5.2-style model: a noaux-tc
+ * router (a score per expert plus an e_score_correction_bias used for
+ * selection only, top-k; mstar PR #388 "Speed up GLM-5.2 with fp8 kernels and
+ * one-graph MTP", router notes; MoE-Infinity PR #140, "[256] router bias"),
+ * the step's expert union and GEMM / SiLU / GEMM phases with fixed-order
+ * reductions and zero-filled pad rows (openinfer PR #610 "TP8 span row
+ * mapping", description and "Gates"), routed experts stored as an fp8 e4m3
+ * [gate_proj, up_proj, down_proj] triple with block scales (MoE-Infinity
+ * PR #140, fp8 store and expert-node commits), activations quantized to e4m3
+ * per 128 columns (mstar PR #388, FlashInfer crossover note), and a bf16
+ * shared expert added to every row.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer unless its comment says "host".  The
+ *   caller allocates and owns all memory; the library never allocates, frees
+ *   or keeps a pointer after a call returns.
+ * - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   No call synchronizes the host, so calls are safe inside stream capture.
+ *   Calls that share a workspace or outputs on different streams race.
+ * - Matrices are row-major and dense.  Device pointers must be 16-byte
+ *   aligned.  bf16 values are passed as uint16_t bit patterns; e4m3 values as
+ *   uint8_t codes (OCP FP8 e4m3fn: bias 7, max 448, no infinities).
+ * - `row_mask` (device, uint8 [M]) marks real rows with 1 and pad rows with
+ *   0; NULL means every row is real.  Kernels read it at run time, so one
+ *   captured graph serves every mask.  A pad row's input is never read; its
+ *   outputs are written as +0.0 (ids -1, weights 0).
+ * - Return value: MOE_OK or an error status.  All arguments are checked on
+ *   the host before anything is enqueued; a call that returns an error other
+ *   than MOE_ELAUNCH enqueued nothing.  M == 0 returns MOE_OK and enqueues
+ *   nothing.
+ *
+ * Numerics (the same procedure for every row, whatever its slot, the other
+ * rows of the step or the number of rows, so a row's bits never depend on
+ * its neighbours):
+ * - logits in float64 (exact bf16 products), score c = sigmoid(l) + bias,
+ *   top-k of c with exact ties to the lower id, ids listed ascending,
+ *   w = routed_scale * sigmoid(l_j) / sum of the selected sigmoids;
+ * - activation quantization per row and 128-column block:
+ *   s = fl32(amax / 448) (1 for an all-zero block), code = round-to-nearest-
+ *   even saturating e4m3 of fl32(v / s);
+ * - GEMMs accumulate in fp32: per 128-deep K-block one fp8 MFMA partial,
+ *   then acc = fma(s_act * s_w, partial, acc) in ascending K-block order;
+ * - h = silu(gate) * up in fp32, requantized per 1x128 block as above;
+ * - y = bf16(fma chain over the row's experts in ascending id, + shared).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL 1       /* null required pointer, bad dims, misaligned pointer, M < 0 */
+#define MOE_EUNSUPPORTED 2 /* n_experts > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOPK or > n_experts, M > MOE_MAX_ROWS */
+#define MOE_EWORKSPACE 3   /* ws_bytes smaller than moe_workspace_bytes() for this M */
+#define MOE_ELAUNCH 4      /* a kernel launch failed (hipGetLastError after each launch) */
+
+#define MOE_MAX_ROWS 16384
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+
+/* Layer dimensions (host struct).  hidden, inter and shared_inter must be
+ * multiples of 128; shared_inter may be 0 (no shared expert). */
+typedef struct {
+  int32_t hidden;       /* H */
+  int32_t n_experts;    /* E, 1..256 */
+  int32_t top_k;        /* k, 1..min(16, E) */
+  int32_t inter;        /* I, routed expert intermediate size */
+  int32_t shared_inter; /* I_s, shared expert intermediate size, 0 = none */
+  float routed_scale;   /* factor applied to the renormalized top-k weights (2.5 for GLM-5.2) */
+} moe_dims;
+
+/* Router parameters (device). */
+typedef struct {
+  const uint16_t* w;  /* bf16 [E, H] */
+  const float* bias;  /* fp32 [E], e_score_correction_bias, used for selection only */
+} moe_router_w;
+
+/* Routed experts (device): e4m3 codes, output-major with K contiguous, and
+ * one fp32 scale per 128x128 block.  All six pointers are required: an fp8
+ * expert without its scales is refused (MOE_EINVAL). */
+typedef struct {
+  const uint8_t* w_gate; /* [E, I, H] */
+  const uint8_t* w_up;   /* [E, I, H] */
+  const uint8_t* w_down; /* [E, H, I] */
+  const float* s_gate;   /* [E, I/128, H/128] */
+  const float* s_up;     /* [E, I/128, H/128] */
+  const float* s_down;   /* [E, H/128, I/128] */
+} moe_expert_w;
+
+/* Shared expert (device): bf16, output-major. */
+typedef struct {
+  const uint16_t* w_gate; /* [I_s, H] */
+  const uint16_t* w_up;   /* [I_s, H] */
+  const uint16_t* w_down; /* [H, I_s] */
+} moe_shared_w;
+
+/* Routing of one step (device buffers, written by moe_route / moe_layer and
+ * read by moe_ffn_fp8).  Slots number the (row, pick) pairs expert by expert
+ * in union order; inside an expert its rows are ascending. */
+typedef struct {
+  int32_t* topk_ids;  /* [M, k] expert ids, ascending per row; -1 for pads */
+  float* topk_w;      /* [M, k] weights in the same order; 0 for pads */
+  int32_t* n_union;   /* [1] number of experts picked by any real row */
+  int32_t* union_ids; /* [E] first n_union entries: the union, ascending */
+  int32_t* offs;      /* [E + 1] slot offsets: expert union_ids[u] owns slots [offs[u], offs[u+1]) */
+  int32_t* rows;      /* [M * k] row of each slot */
+  int32_t* slot_of;   /* [M, k] slot of (row, pick); -1 for pads */
+} moe_routing;
+
+/* Optional copies of the quantized activations (device; NULL fields or a
+ * NULL struct = not written).  Slot order as in moe_routing. */
+typedef struct {
+  uint8_t* x_codes; /* [M, H] e4m3 codes of x (real rows) */
+  float* x_scales;  /* [M, H/128] */
+  uint8_t* h_codes; /* [M * k, I] e4m3 codes of silu(gate)*up per slot */
+  float* h_scales;  /* [M * k, I/128] */
+} moe_taps;
+
+/* Device workspace bytes needed by moe_route / moe_ffn_fp8 / moe_layer for
+ * any M <= max_rows.  Returns 0 for invalid dims or max_rows outside
+ * [0, MOE_MAX_ROWS]. */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_rows);
+
+/* Router and union (mstar PR #388 router notes; openinfer PR #610 "Gates"):
+ * logits, sigmoid + bias top-k, weights, the ascending expert union and the
+ * per-expert row lists.  x: bf16 [M, H].  Writes every field of *out. */
+int moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+              const moe_router_w* router, moe_routing* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed experts only (openinfer PR #610 "What": union / GEMM / SiLU / GEMM
+ * phases): quantize x, gate/up GEMMs, SiLU*up with 1x128 requantization,
+ * down GEMM, fixed-order weighted combine.  `in` may come from moe_route or
+ * from any producer of the same layout; a malformed routing (n_union or
+ * offsets out of range, union not ascending) contributes nothing.
+ * y: bf16 [M, H], routed part only (no shared expert); pad rows +0.0. */
+int moe_ffn_fp8(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+                const moe_routing* in, const moe_expert_w* experts, uint16_t* y, moe_taps* taps, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* The whole layer: moe_route, then the routed experts and the bf16 shared
+ * expert (shared may be NULL only when dims->shared_inter == 0).
+ * y: bf16 [M, H]; the routing is written to *out. */
+int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+              const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
+              moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream);
+
+/* The 1x128 activation quantization step on its own (mstar PR #388,
+ * FlashInfer crossover note): rows x cols values (fp32 if is_bf16 == 0, else
+ * bf16 bits) -> e4m3 codes [rows, cols] and fp32 scales [rows, cols/128].
+ * cols must be a multiple of 128. */
+int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
+                  void* stream);
+
+/* Kernel timing hook for measurement (host).  The pages time one layer's
+ * experts per call with every call's weights read from HBM (mstar PR #388,
+ * decode table note); this hook times each kernel of a call.  While a table
+ * is set, every kernel the library enqueues is bracketed by
+ * hipEventRecord(pairs[i].start) and hipEventRecord(pairs[i].stop) on the
+ * launch stream, kernel_ids[i] receives the kernel's id and *count is
+ * incremented, until *count reaches capacity.  The events (hipEvent_t) and
+ * the three arrays are the caller's and must outlive the traced calls.
+ * pairs == NULL switches tracing off.  Process-wide, not thread-safe:
+ * measurement only.  Returns MOE_EINVAL for capacity < 0 or a NULL ids or
+ * count with a non-NULL table. */
+typedef struct {
+  void* start; /* hipEvent_t */
+  void* stop;  /* hipEvent_t */
+} moe_event_pair;
+int moe_trace_set(moe_event_pair* pairs, int32_t capacity, int32_t* kernel_ids, int32_t* count);
+
+/* Name of a kernel id reported by moe_trace_set (static string; "?" if unknown). */
+const char* moe_kernel_name(int32_t kernel_id);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

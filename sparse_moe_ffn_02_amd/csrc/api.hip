@@ -1,0 +1,312 @@
+// C ABI of the MoE FFN library: argument checks, workspace layout and the
+// launch sequence of each entry point.  Nothing here allocates, frees or
+// synchronizes; every check happens before the first launch.
+#include <math.h>
+#include <string.h>
+
+#include "moe_ffn.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t sched, mtile, logits, rowbits, xq, xs, hbuf, hq, hs, gsh, ush, hsh, S, D, total;
+};
+
+Layout make_layout(const moe_dims& d, int M) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t m = (size_t)M, H = d.hidden, E = d.n_experts, K = d.top_k, I = d.inter, Is = d.shared_inter;
+  L.sched = take(SCHED_WORDS * sizeof(int32_t));
+  L.mtile = take((E + 1) * sizeof(int32_t));
+  L.logits = take(m * E * sizeof(double));
+  L.rowbits = take(m * ((E + 31) / 32) * sizeof(uint32_t));
+  L.xq = take(m * H);
+  L.xs = take(m * (H / 128) * sizeof(float));
+  L.hbuf = take(m * K * I * sizeof(float));
+  L.hq = take(m * K * I);
+  L.hs = take(m * K * (I / 128) * sizeof(float));
+  L.gsh = take(m * Is * sizeof(float));
+  L.ush = take(m * Is * sizeof(float));
+  L.hsh = take(m * Is * sizeof(uint16_t));
+  const bool generic = M > kDecodeMaxRows;
+  L.S = take(generic ? m * H * sizeof(float) : 0);
+  L.D = take(generic ? m * K * H * sizeof(float) : 0);
+  L.total = off;
+  return L;
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->hidden % 128 || d->inter <= 0 || d->inter % 128) return MOE_EINVAL;
+  if (d->shared_inter < 0 || d->shared_inter % 128) return MOE_EINVAL;
+  if (d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
+  if (!isfinite(d->routed_scale)) return MOE_EINVAL;
+  if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->n_experts) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_rows(int32_t M) {
+  if (M < 0) return MOE_EINVAL;
+  if (M > MOE_MAX_ROWS) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// required device pointer with the given alignment
+inline bool ok_ptr(const void* p, size_t a) { return p != nullptr && aligned(p, a); }
+// optional device pointer
+inline bool ok_opt(const void* p, size_t a) { return p == nullptr || aligned(p, a); }
+
+int check_routing(const moe_routing* r) {
+  if (!r) return MOE_EINVAL;
+  if (!ok_ptr(r->topk_ids, 4) || !ok_ptr(r->topk_w, 4) || !ok_ptr(r->n_union, 4) || !ok_ptr(r->union_ids, 4) ||
+      !ok_ptr(r->offs, 4) || !ok_ptr(r->rows, 4) || !ok_ptr(r->slot_of, 4))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int check_experts(const moe_expert_w* w) {
+  if (!w) return MOE_EINVAL;
+  if (!ok_ptr(w->w_gate, 16) || !ok_ptr(w->w_up, 16) || !ok_ptr(w->w_down, 16)) return MOE_EINVAL;
+  if (!ok_ptr(w->s_gate, 4) || !ok_ptr(w->s_up, 4) || !ok_ptr(w->s_down, 4)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int check_taps(const moe_taps* t) {
+  if (!t) return MOE_OK;
+  if (!ok_opt(t->x_codes, 16) || !ok_opt(t->x_scales, 4) || !ok_opt(t->h_codes, 16) || !ok_opt(t->h_scales, 4))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+RouteArgs route_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t* mask, const moe_router_w& rw,
+                     const moe_routing& out, char* ws, const Layout& L) {
+  RouteArgs a;
+  a.x = x;
+  a.mask = mask;
+  a.wr = rw.w;
+  a.bias = rw.bias;
+  a.M = M;
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.K = d.top_k;
+  a.scale = d.routed_scale;
+  a.logits = reinterpret_cast<double*>(ws + L.logits);
+  a.rowbits = reinterpret_cast<uint32_t*>(ws + L.rowbits);
+  a.ids = out.topk_ids;
+  a.w = out.topk_w;
+  a.n_union = out.n_union;
+  a.union_ids = out.union_ids;
+  a.offs = out.offs;
+  a.rows = out.rows;
+  a.slot_of = out.slot_of;
+  a.sched = reinterpret_cast<int32_t*>(ws + L.sched);
+  a.mtile_offs = reinterpret_cast<int32_t*>(ws + L.mtile);
+  return a;
+}
+
+FfnArgs ffn_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t* mask, const moe_routing& rt,
+                 const moe_expert_w& ew, const moe_shared_w* sw, uint16_t* y, const moe_taps* taps, char* ws,
+                 const Layout& L) {
+  FfnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.M = M;
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.K = d.top_k;
+  a.I = d.inter;
+  a.Is = sw ? d.shared_inter : 0;
+  a.x = x;
+  a.mask = mask;
+  a.ids = rt.topk_ids;
+  a.w = rt.topk_w;
+  a.n_union = rt.n_union;
+  a.union_ids = rt.union_ids;
+  a.offs = rt.offs;
+  a.rows = rt.rows;
+  a.slot_of = rt.slot_of;
+  a.wg = ew.w_gate;
+  a.wu = ew.w_up;
+  a.wd = ew.w_down;
+  a.sg = ew.s_gate;
+  a.su = ew.s_up;
+  a.sd = ew.s_down;
+  if (sw) {
+    a.wsg = sw->w_gate;
+    a.wsu = sw->w_up;
+    a.wsd = sw->w_down;
+  }
+  a.sched = reinterpret_cast<int32_t*>(ws + L.sched);
+  a.mtile_offs = reinterpret_cast<int32_t*>(ws + L.mtile);
+  a.xq = (taps && taps->x_codes) ? taps->x_codes : reinterpret_cast<uint8_t*>(ws + L.xq);
+  a.xs = (taps && taps->x_scales) ? taps->x_scales : reinterpret_cast<float*>(ws + L.xs);
+  a.hbuf = reinterpret_cast<float*>(ws + L.hbuf);
+  a.hq = (taps && taps->h_codes) ? taps->h_codes : reinterpret_cast<uint8_t*>(ws + L.hq);
+  a.hs = (taps && taps->h_scales) ? taps->h_scales : reinterpret_cast<float*>(ws + L.hs);
+  a.gsh = reinterpret_cast<float*>(ws + L.gsh);
+  a.ush = reinterpret_cast<float*>(ws + L.ush);
+  a.hsh = reinterpret_cast<uint16_t*>(ws + L.hsh);
+  a.S = reinterpret_cast<float*>(ws + L.S);
+  a.D = reinterpret_cast<float*>(ws + L.D);
+  a.y = y;
+  return a;
+}
+
+struct Tracer {
+  moe_event_pair* pairs = nullptr;
+  int32_t cap = 0;
+  int32_t* ids = nullptr;
+  int32_t* count = nullptr;
+};
+Tracer g_trace;
+
+const char* const kKernelNames[KID_COUNT] = {
+    "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
+    "down_combine_decode", "down", "combine", "quant",
+};
+
+}  // namespace
+
+namespace moe {
+
+void trace_before(hipStream_t s) {
+  if (g_trace.pairs && *g_trace.count < g_trace.cap)
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_trace.pairs[*g_trace.count].start), s);
+}
+
+void trace_after(int kid, hipStream_t s) {
+  if (g_trace.pairs && *g_trace.count < g_trace.cap) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_trace.pairs[*g_trace.count].stop), s);
+    g_trace.ids[*g_trace.count] = kid;
+    ++*g_trace.count;
+  }
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_trace_set(moe_event_pair* pairs, int32_t capacity, int32_t* kernel_ids, int32_t* count) {
+  if (pairs == nullptr) {
+    g_trace = Tracer();
+    return MOE_OK;
+  }
+  if (capacity < 0 || kernel_ids == nullptr || count == nullptr) return MOE_EINVAL;
+  g_trace.pairs = pairs;
+  g_trace.cap = capacity;
+  g_trace.ids = kernel_ids;
+  g_trace.count = count;
+  return MOE_OK;
+}
+
+const char* moe_kernel_name(int32_t kernel_id) {
+  return (kernel_id >= 0 && kernel_id < KID_COUNT) ? kKernelNames[kernel_id] : "?";
+}
+
+
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_rows) {
+  if (check_dims(dims) != MOE_OK || check_rows(max_rows) != MOE_OK) return 0;
+  return make_layout(*dims, max_rows).total;
+}
+
+int moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+              const moe_router_w* router, moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_rows(M)) != MOE_OK) return st;
+  if (!router || !ok_ptr(router->w, 16) || !ok_ptr(router->bias, 4)) return MOE_EINVAL;
+  if (!ok_ptr(x, 16) || (st = check_routing(out)) != MOE_OK) return st != MOE_OK ? st : MOE_EINVAL;
+  if (!ok_ptr(ws, 16)) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  const Layout L = make_layout(*dims, M);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const RouteArgs a = route_args(*dims, M, x, row_mask, *router, *out, static_cast<char*>(ws), L);
+  return to_status(launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_ffn_fp8(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+                const moe_routing* in, const moe_expert_w* experts, uint16_t* y, moe_taps* taps, void* ws,
+                size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_rows(M)) != MOE_OK) return st;
+  if ((st = check_routing(in)) != MOE_OK) return st;
+  if ((st = check_experts(experts)) != MOE_OK) return st;
+  if ((st = check_taps(taps)) != MOE_OK) return st;
+  if (!ok_ptr(x, 16) || !ok_ptr(y, 16) || !ok_ptr(ws, 16)) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  const Layout L = make_layout(*dims, M);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  const FfnArgs a = ffn_args(*dims, M, x, row_mask, *in, *experts, nullptr, y, taps, static_cast<char*>(ws), L);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = to_status(launch_quant_x(a, s))) != MOE_OK) return st;
+  if ((st = to_status(launch_plan(a, s))) != MOE_OK) return st;
+  return to_status(launch_ffn(a, s));
+}
+
+int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+              const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
+              moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_rows(M)) != MOE_OK) return st;
+  if (!router || !ok_ptr(router->w, 16) || !ok_ptr(router->bias, 4)) return MOE_EINVAL;
+  if ((st = check_routing(out)) != MOE_OK) return st;
+  if ((st = check_experts(experts)) != MOE_OK) return st;
+  if ((st = check_taps(taps)) != MOE_OK) return st;
+  if (dims->shared_inter > 0) {
+    if (!shared || !ok_ptr(shared->w_gate, 16) || !ok_ptr(shared->w_up, 16) || !ok_ptr(shared->w_down, 16))
+      return MOE_EINVAL;
+  } else {
+    shared = nullptr;
+  }
+  if (!ok_ptr(x, 16) || !ok_ptr(y, 16) || !ok_ptr(ws, 16)) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  const Layout L = make_layout(*dims, M);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* w = static_cast<char*>(ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RouteArgs ra = route_args(*dims, M, x, row_mask, *router, *out, w, L);
+  if ((st = to_status(launch_route(ra, s))) != MOE_OK) return st;
+  const FfnArgs a = ffn_args(*dims, M, x, row_mask, *out, *experts, shared, y, taps, w, L);
+  if ((st = to_status(launch_quant_x(a, s))) != MOE_OK) return st;
+  return to_status(launch_ffn(a, s));
+}
+
+int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
+                  void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128) return MOE_EINVAL;
+  if (rows > MOE_MAX_ROWS * MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(in, 16) || !ok_ptr(codes, 16) || !ok_ptr(scales, 4)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  return to_status(
+      launch_quant_generic(in, is_bf16 ? 1 : 0, rows, cols, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported size";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device-side helpers shared by every kernel of the MoE FFN library (gfx950).
+//
+// Everything that decides a bit of a result lives here once, so that the
+// decode and prefill kernels compute each output element by the same
+// procedure: the e4m3 encoder, the bf16 rounding, the SiLU product, the
+// per-K-block scale step and the MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kBlk = 128;       // quantization block (1x128 activations, 128x128 weights)
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MFMA
+// fp8 e4m3 x e4m3 -> fp32, 16x16 output, K = 128, zero initial accumulator.
+// Operand layout (both operands): lane l holds 32 consecutive K values of
+// row/column (l % 16), starting at K = 32 * (l / 16).
+// Output layout: lane l holds C[4 * (l / 16) + i][l % 16], i = 0..3.
+__device__ __forceinline__ v4f mfma_fp8_k128(const v8i& a, const v8i& b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// bf16 x bf16 -> fp32, 16x16 output, K = 32, accumulating into c.
+// Operand layout: lane l holds 8 consecutive K values of row/column (l % 16)
+// starting at K = 8 * (l / 16).  Output layout as above.
+__device__ __forceinline__ v4f mfma_bf16_k32(const v4i& a, const v4i& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
+                                                 c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Finite fp32 -> OCP e4m3 (bias 7, max 448) code, round to nearest even,
+// magnitudes at or above 448 saturate to 448.  Integer arithmetic only.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x43e00000u) {                 // |v| >= 448
+    code = 0x7eu;
+  } else if (a < 0x3c800000u) {           // |v| < 2^-6: grid of 2^-9
+    // |v| * 2^9 < 8 is exact; rintf rounds to nearest even.
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t e = (a >> 23) - 127u + 7u;          // biased e4m3 exponent, 1..15
+    const uint32_t mant = (a & 0x7fffffu) | 0x800000u; // 24-bit significand
+    uint32_t q = mant >> 20;                           // 4 significant bits, 8..15
+    const uint32_t rem = mant & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;   // may reach 16: carries
+    code = (e << 3) + q - 8u;
+  }
+  return code | sign;
+}
+
+// Per-block quantization scale: s = fl32(amax / 448), s = 1 for a zero block.
+__device__ __forceinline__ float quant_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+}
+
+// Code of one value under scale s (zero blocks give code 0 via v = 0).
+__device__ __forceinline__ uint32_t quant_code(float v, float s) {
+  return f32_to_e4m3(__fdiv_rn(v, s));
+}
+
+// h = silu(g) * u in fp32, silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float s = __fdiv_rn(g, 1.0f + expf(-g));
+  return s * u;
+}
+
+// One K-block step of a block-scaled accumulation:
+// acc = fma(s_a * s_w, partial, acc) for the 4 outputs of a lane.
+__device__ __forceinline__ void scale_acc(v4f& acc, const v4f& p, float sa, float sw) {
+  const float ss = sa * sw;
+  acc[0] = __builtin_fmaf(ss, p[0], acc[0]);
+  acc[1] = __builtin_fmaf(ss, p[1], acc[1]);
+  acc[2] = __builtin_fmaf(ss, p[2], acc[2]);
+  acc[3] = __builtin_fmaf(ss, p[3], acc[3]);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,93 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMTile = 16;          // slots (or rows) per MFMA column tile
+constexpr int kDecodeMaxRows = 16;  // rows served by the fused decode down/combine kernel
+
+// sched[] words written by the union / plan kernels and read by the FFN kernels
+enum { SCHED_NUNION = 0, SCHED_MTILES = 1, SCHED_SLOTS = 2, SCHED_BAD = 3, SCHED_WORDS = 8 };
+
+struct RouteArgs {
+  const uint16_t* x;       // bf16 [M, H]
+  const uint8_t* mask;     // [M] or null
+  const uint16_t* wr;      // bf16 [E, H]
+  const float* bias;       // [E]
+  int M, H, E, K;
+  float scale;
+  double* logits;          // ws [M, E]
+  uint32_t* rowbits;       // ws [M, ceil(E/32)]
+  int32_t* ids;            // [M, K]
+  float* w;                // [M, K]
+  int32_t* n_union;        // [1]
+  int32_t* union_ids;      // [E]
+  int32_t* offs;           // [E + 1]
+  int32_t* rows;           // [M * K]
+  int32_t* slot_of;        // [M, K]
+  int32_t* sched;          // ws [SCHED_WORDS]
+  int32_t* mtile_offs;     // ws [E + 1]
+};
+
+struct FfnArgs {
+  int M, H, E, K, I, Is;
+  const uint16_t* x;       // bf16 [M, H]
+  const uint8_t* mask;     // [M] or null
+  // routing
+  const int32_t* ids;      // [M, K]
+  const float* w;          // [M, K]
+  const int32_t* n_union;
+  const int32_t* union_ids;
+  const int32_t* offs;
+  const int32_t* rows;
+  const int32_t* slot_of;
+  // routed expert weights
+  const uint8_t *wg, *wu, *wd;
+  const float *sg, *su, *sd;
+  // shared expert (null when Is == 0)
+  const uint16_t *wsg, *wsu, *wsd;
+  // workspace
+  int32_t* sched;
+  int32_t* mtile_offs;
+  uint8_t* xq; float* xs;  // [M, H], [M, H/128]
+  float* hbuf;             // [M*K, I]
+  uint8_t* hq; float* hs;  // [M*K, I], [M*K, I/128]
+  float* gsh; float* ush;  // shared gate/up outputs [M, Is] (fp32)
+  uint16_t* hsh;           // [M, Is] bf16 shared h
+  float* S;                // [M, H]
+  float* D;                // [M*K, H]
+  uint16_t* y;             // bf16 [M, H]
+};
+
+// Kernel ids reported by the timing hook (moe_trace_set).
+enum KernelId {
+  KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
+  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_COUNT
+};
+
+void trace_before(hipStream_t s);
+void trace_after(int kid, hipStream_t s);
+
+// Launch, capture the launch status, record the timing events when tracing,
+// and return the status from the enclosing launcher on failure.
+#define MOE_LAUNCH(kid, kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                           \
+    ::moe::trace_before(stream);                                                 \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);         \
+    const hipError_t moe_launch_err_ = hipGetLastError();                        \
+    ::moe::trace_after(kid, stream);                                             \
+    if (moe_launch_err_ != hipSuccess) return moe_launch_err_;                   \
+  } while (0)
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_plan(const FfnArgs& a, hipStream_t s);
+hipError_t launch_quant_x(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
+                                hipStream_t s);
+
+}  // namespace moe

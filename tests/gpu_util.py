@@ -1,0 +1,199 @@
+"""Helpers for the GPU parity tests: upload seeded layers, run the HIP path
+through the C ABI, and compare against the CPU oracle."""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_moe_ffn_02_amd as moe
+import synth
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def t16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def t8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def tf(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def ti(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def mdims(d: synth.Dims) -> moe.Dims:
+    return moe.Dims(d.hidden, d.n_experts, d.top_k, d.inter, d.shared_inter, d.routed_scale)
+
+
+class GpuLayer:
+    """A synth.Layer resident in device memory, plus host copies for the oracle."""
+
+    def __init__(self, lay: synth.Layer):
+        self.host = lay
+        self.dims = mdims(lay.dims)
+        self.router_w = t16(lay.router_w)
+        self.bias = tf(lay.bias)
+        self.experts = moe.Experts(t8(lay.w_gate), t8(lay.w_up), t8(lay.w_down), tf(lay.s_gate), tf(lay.s_up),
+                                   tf(lay.s_down))
+        self.shared = (moe.Shared(t16(lay.shared["gate"]), t16(lay.shared["up"]), t16(lay.shared["down"]))
+                       if lay.shared else None)
+
+    def with_bias(self, bias: np.ndarray) -> "GpuLayer":
+        """Same weights, another correction bias (e.g. the Zipf-skewed one)."""
+        other = GpuLayer.__new__(GpuLayer)
+        other.__dict__.update(self.__dict__)
+        other.host = synth.Layer(**{**self.host.__dict__, "bias": bias})
+        other.bias = tf(bias)
+        return other
+
+    def expert_fn(self):
+        h = self.host
+
+        def get(e):
+            return {"gate": h.w_gate[e], "s_gate": h.s_gate[e], "up": h.w_up[e], "s_up": h.s_up[e],
+                    "down": h.w_down[e], "s_down": h.s_down[e]}
+        return get
+
+
+def np16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_layer(gl: GpuLayer, x_bits: np.ndarray, mask: Optional[np.ndarray], shared: bool = True,
+              ws_rows: Optional[int] = None) -> Dict[str, np.ndarray]:
+    m = x_bits.shape[0]
+    d = gl.dims
+    x = t16(x_bits)
+    mk = t8(mask.astype(np.uint8)) if mask is not None else None
+    ws = moe.workspace(d, ws_rows or m)
+    y = torch.full((m, d.hidden), -1, dtype=torch.int16, device=DEV)       # 0xFFFF poison
+    rt = moe.Routing.empty(d, m)
+    for t in (rt.topk_ids, rt.union_ids, rt.offs, rt.rows, rt.slot_of, rt.n_union):
+        t.fill_(-7)
+    tp = moe.Taps.empty(d, m)
+    moe.layer(d, x, mk, gl.router_w, gl.bias, gl.experts, gl.shared if shared else None, y, rt, ws, tp)
+    torch.cuda.synchronize()
+    nu = int(rt.n_union.item())
+    return dict(y=np16(y), ids=rt.topk_ids.cpu().numpy(), w=rt.topk_w.cpu().numpy(), n_union=nu,
+                union_ids=rt.union_ids.cpu().numpy()[:nu], offs=rt.offs.cpu().numpy()[:nu + 1],
+                rows=rt.rows.cpu().numpy(), slot_of=rt.slot_of.cpu().numpy(),
+                x_codes=tp.x_codes.cpu().numpy(), x_scales=tp.x_scales.cpu().numpy(),
+                h_codes=tp.h_codes.cpu().numpy(), h_scales=tp.h_scales.cpu().numpy())
+
+
+def run_ffn(gl: GpuLayer, x_bits: np.ndarray, mask: Optional[np.ndarray], rt: oracle.Routing) -> Dict[str, np.ndarray]:
+    """moe_ffn_fp8 on a routing produced by the oracle (uploaded as-is)."""
+    m = x_bits.shape[0]
+    d = gl.dims
+    k = d.top_k
+    nu = rt.n_union
+    uid = np.zeros(d.n_experts, np.int32)
+    uid[:nu] = rt.union_ids
+    offs = np.zeros(d.n_experts + 1, np.int32)
+    offs[:nu + 1] = rt.offs
+    rows = np.zeros(max(1, m * k), np.int32)
+    rows[:rt.rows.size] = rt.rows
+    routing = moe.Routing(ti(rt.ids), tf(rt.w.astype(np.float32)), ti(np.array([nu])), ti(uid), ti(offs), ti(rows),
+                          ti(rt.slot_of))
+    ws = moe.workspace(d, m)
+    y = torch.full((m, d.hidden), -1, dtype=torch.int16, device=DEV)
+    tp = moe.Taps.empty(d, m)
+    moe.ffn_fp8(d, t16(x_bits), t8(mask.astype(np.uint8)) if mask is not None else None, routing, gl.experts, y, ws,
+                tp)
+    torch.cuda.synchronize()
+    return dict(y=np16(y), h_codes=tp.h_codes.cpu().numpy(), h_scales=tp.h_scales.cpu().numpy(),
+                x_codes=tp.x_codes.cpu().numpy(), x_scales=tp.x_scales.cpu().numpy())
+
+
+def run_oracle(gl: GpuLayer, x_bits, mask, rows=None, shared=True) -> oracle.LayerOut:
+    d = gl.host.dims
+    return oracle.layer(x_bits, mask if mask is not None else np.ones(x_bits.shape[0], np.uint8), gl.host.router_w,
+                        gl.host.bias, d.top_k, d.routed_scale, gl.expert_fn(),
+                        gl.host.shared if (shared and gl.host.shared) else None, rows=rows)
+
+
+# ---------------------------------------------------------------- comparisons
+
+REL_TOL = 2e-2        # per-row max error / max |y_ref|, fp32 accumulation and bf16 output
+
+
+def assert_routing_equal(g: Dict[str, np.ndarray], o: oracle.Routing, mask: np.ndarray):
+    assert np.array_equal(g["ids"], o.ids), "topk ids differ"
+    assert g["n_union"] == o.n_union
+    assert np.array_equal(g["union_ids"], o.union_ids), "union differs"
+    assert np.array_equal(g["offs"], o.offs), "offsets differ"
+    slots = int(o.offs[-1]) if o.n_union else 0
+    assert np.array_equal(g["rows"][:slots], o.rows), "row compaction differs"
+    assert np.array_equal(g["slot_of"], o.slot_of), "slot_of differs"
+    real = mask != 0
+    # fp32 weights against the float64 oracle: within one fp32 rounding
+    wo = o.w[real]
+    wg = g["w"][real].astype(np.float64)
+    assert np.all(np.abs(wg - wo) <= 2.0 ** -23 * np.abs(wo) + 1e-30)
+    assert (g["w"][~real] == 0).all()
+
+
+def y_row_errors(y_bits: np.ndarray, y_ref: np.ndarray, rows) -> np.ndarray:
+    yg = oracle.decode_bf16(y_bits[rows])
+    yr = y_ref[rows]
+    return np.abs(yg - yr).max(axis=1) / np.maximum(np.abs(yr).max(axis=1), 1e-30)
+
+
+def assert_y_close(y_bits, out: oracle.LayerOut, rows=None, tol=REL_TOL) -> float:
+    rows = out.evaluated if rows is None else rows
+    err = y_row_errors(y_bits, out.y_ref, rows)
+    assert np.isfinite(err).all()
+    assert (err <= tol).all(), f"row errors {err.max():.3e} > {tol}"
+    return float(err.max())
+
+
+def _adjacent(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    zero = {0x00, 0x80, 0x01, 0x81}
+    same_sign = (a & 0x80) == (b & 0x80)
+    near_zero = np.isin(a, list(zero)) & np.isin(b, list(zero))
+    return (same_sign & (np.abs(a.astype(int) - b.astype(int)) <= 1)) | near_zero
+
+
+def compare_h_codes(g_codes: np.ndarray, g_scales: np.ndarray, out: oracle.LayerOut, max_frac=1e-2,
+                    scale_tol=2.0 ** -10):
+    """Layer-level h codes.
+
+    The requantization itself is bit-exact (checked on its own against the
+    oracle's fl32(h)).  Upstream, the gfx950 fp8 MFMA returns each 128-term
+    partial within 2^-15 of sum|a*b| (measured; not a correctly rounded fp32
+    sum), so G and U move by ~1e-5 relative and an h value lying that close to
+    an e4m3 rounding midpoint lands on the neighbouring code.  Allowed: every
+    difference is an adjacent code, at most 1% of codes differ, and block
+    scales (amax / 448) agree within 2^-10 relative."""
+    n = 0
+    bad = 0
+    worst = 0.0
+    for s, oc in out.h_codes.items():
+        gc = g_codes[s]
+        diff = gc != oc
+        bad += int(diff.sum())
+        n += oc.size
+        assert _adjacent(gc[diff], oc[diff]).all(), f"non-adjacent h code flip at slot {s}"
+        gs = g_scales[s].astype(np.float64)
+        os_ = out.h_scales[s].astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(gs - os_) / os_)))
+    say(f"h codes: {bad} of {n} differ (adjacent); worst scale rel diff {worst:.2e}")
+    assert worst <= scale_tol, f"h scales differ by {worst:.2e}"
+    assert bad <= max(2, max_frac * n), f"{bad} of {n} h codes differ"
+    return bad, n

@@ -1,0 +1,195 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/moe_ffn.h declares,
+and reject bad arguments with the documented status before enqueuing any
+work.  Only error paths and M == 0 are exercised here, so no kernel is ever
+launched and the fake (aligned, non-null) device addresses are never used.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_moe_ffn_02_amd as moe
+from sparse_moe_ffn_02_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+FAKE = 0x7f0000000000          # 256-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from sparse_moe_ffn_02_amd.build import build
+        build()
+    return L.load()
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(moe_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_str(0) == b"ok"
+    for s in range(1, 5):
+        assert lib.moe_status_str(s) not in (b"ok", b"unknown status")
+    assert lib.moe_status_str(99) == b"unknown status"
+
+
+GLM = moe.Dims(6144, 256, 8, 2048, 2048, 2.5)
+
+
+def _dims(**kw):
+    d = dict(hidden=6144, n_experts=256, top_k=8, inter=2048, shared_inter=2048, routed_scale=2.5)
+    d.update(kw)
+    return L.CDims(**d)
+
+
+def test_workspace_bytes(lib):
+    d = _dims()
+    b8 = lib.moe_workspace_bytes(C.byref(d), 8)
+    b16 = lib.moe_workspace_bytes(C.byref(d), 16)
+    b4096 = lib.moe_workspace_bytes(C.byref(d), 4096)
+    assert 0 < b8 <= b16 < b4096
+    # the generic path keeps fp32 D [M*k, H]
+    assert b4096 >= 4096 * 8 * 6144 * 4
+    assert lib.moe_workspace_bytes(C.byref(d), -1) == 0
+    assert lib.moe_workspace_bytes(C.byref(d), L.MAX_ROWS + 1) == 0
+    assert lib.moe_workspace_bytes(None, 8) == 0
+    assert lib.moe_workspace_bytes(C.byref(_dims(hidden=100)), 8) == 0
+
+
+def _routing():
+    return L.CRouting(*([FAKE] * 7))
+
+
+def _experts(**kw):
+    f = dict(w_gate=FAKE, w_up=FAKE, w_down=FAKE, s_gate=FAKE, s_up=FAKE, s_down=FAKE)
+    f.update(kw)
+    return L.CExperts(**f)
+
+
+def _layer(lib, d, m, *, x=FAKE, router=None, experts=None, shared=None, y=FAKE, ws=FAKE, ws_bytes=1 << 40,
+           routing=None, taps=None):
+    router = router or L.CRouter(FAKE, FAKE)
+    experts = experts or _experts()
+    shared = shared if shared is not None else L.CShared(FAKE, FAKE, FAKE)
+    routing = routing or _routing()
+    return lib.moe_layer(C.byref(d), m, x, None, C.byref(router), C.byref(experts), C.byref(shared), y,
+                         C.byref(routing), C.byref(taps) if taps is not None else None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=0), L.MOE_EINVAL),
+    (dict(hidden=6000), L.MOE_EINVAL),
+    (dict(inter=2000), L.MOE_EINVAL),
+    (dict(shared_inter=100), L.MOE_EINVAL),
+    (dict(shared_inter=-128), L.MOE_EINVAL),
+    (dict(n_experts=0), L.MOE_EINVAL),
+    (dict(top_k=0), L.MOE_EINVAL),
+    (dict(routed_scale=float("nan")), L.MOE_EINVAL),
+    (dict(n_experts=512), L.MOE_EUNSUPPORTED),
+    (dict(top_k=17), L.MOE_EUNSUPPORTED),
+    (dict(n_experts=4, top_k=8), L.MOE_EUNSUPPORTED),
+])
+def test_layer_rejects_bad_dims(lib, kw, status):
+    assert _layer(lib, _dims(**kw), 8) == status
+
+
+def test_layer_rejects_bad_rows_and_pointers(lib):
+    d = _dims()
+    assert _layer(lib, d, -1) == L.MOE_EINVAL
+    assert _layer(lib, d, L.MAX_ROWS + 1) == L.MOE_EUNSUPPORTED
+    assert _layer(lib, d, 8, x=None) == L.MOE_EINVAL
+    assert _layer(lib, d, 8, x=FAKE + 2) == L.MOE_EINVAL          # misaligned
+    assert _layer(lib, d, 8, y=None) == L.MOE_EINVAL
+    assert _layer(lib, d, 8, ws=None) == L.MOE_EINVAL
+    assert _layer(lib, d, 8, router=L.CRouter(FAKE, None)) == L.MOE_EINVAL
+    # missing scales are refused, never read as unscaled weights
+    assert _layer(lib, d, 8, experts=_experts(s_down=None)) == L.MOE_EINVAL
+    assert _layer(lib, d, 8, experts=_experts(w_up=None)) == L.MOE_EINVAL
+    # shared expert required when shared_inter > 0
+    assert lib.moe_layer(C.byref(d), 8, FAKE, None, C.byref(L.CRouter(FAKE, FAKE)), C.byref(_experts()), None,
+                         FAKE, C.byref(_routing()), None, FAKE, 1 << 40, None) == L.MOE_EINVAL
+    bad_rt = _routing()
+    bad_rt.offs = None
+    assert _layer(lib, d, 8, routing=bad_rt) == L.MOE_EINVAL
+    bad_taps = L.CTaps(FAKE + 1, None, None, None)
+    assert _layer(lib, d, 8, taps=bad_taps) == L.MOE_EINVAL
+
+
+def test_workspace_too_small(lib):
+    d = _dims()
+    need = lib.moe_workspace_bytes(C.byref(d), 8)
+    assert _layer(lib, d, 8, ws_bytes=need - 1) == L.MOE_EWORKSPACE
+    need4k = lib.moe_workspace_bytes(C.byref(d), 4096)
+    assert _layer(lib, d, 4096, ws_bytes=need4k - 256) == L.MOE_EWORKSPACE
+
+
+def test_zero_rows_is_ok_without_launch(lib):
+    d = _dims()
+    assert _layer(lib, d, 0, ws_bytes=0) == L.MOE_OK
+    rt = _routing()
+    assert lib.moe_route(C.byref(d), 0, FAKE, None, C.byref(L.CRouter(FAKE, FAKE)), C.byref(rt), FAKE, 0,
+                         None) == L.MOE_OK
+    assert lib.moe_ffn_fp8(C.byref(d), 0, FAKE, None, C.byref(rt), C.byref(_experts()), FAKE, None, FAKE, 0,
+                           None) == L.MOE_OK
+    assert lib.moe_quant_fp8(FAKE, 0, 0, 128, FAKE, FAKE, None) == L.MOE_OK
+
+
+def test_route_and_ffn_reject(lib):
+    d = _dims()
+    rt = _routing()
+    assert lib.moe_route(C.byref(d), 8, FAKE, None, None, C.byref(rt), FAKE, 1 << 40, None) == L.MOE_EINVAL
+    assert lib.moe_route(C.byref(d), 8, FAKE, None, C.byref(L.CRouter(FAKE, FAKE)), None, FAKE, 1 << 40,
+                         None) == L.MOE_EINVAL
+    assert lib.moe_ffn_fp8(C.byref(d), 8, FAKE, None, None, C.byref(_experts()), FAKE, None, FAKE, 1 << 40,
+                           None) == L.MOE_EINVAL
+    assert lib.moe_ffn_fp8(C.byref(d), 8, FAKE, None, C.byref(rt), C.byref(_experts(s_gate=None)), FAKE, None,
+                           FAKE, 1 << 40, None) == L.MOE_EINVAL
+    assert lib.moe_ffn_fp8(C.byref(_dims(top_k=300)), 8, FAKE, None, C.byref(rt), C.byref(_experts()), FAKE, None,
+                           FAKE, 1 << 40, None) == L.MOE_EUNSUPPORTED
+
+
+def test_quant_rejects(lib):
+    assert lib.moe_quant_fp8(FAKE, 0, 4, 100, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_quant_fp8(FAKE, 0, -1, 128, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_quant_fp8(None, 0, 4, 128, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_quant_fp8(FAKE, 0, 4, 128, FAKE, None, None) == L.MOE_EINVAL
+
+
+def test_trace_hook_arguments(lib):
+    ids = (C.c_int32 * 4)()
+    cnt = C.c_int32(0)
+    pairs = (C.c_void_p * 8)()
+    assert lib.moe_trace_set(pairs, -1, ids, C.byref(cnt)) == L.MOE_EINVAL
+    assert lib.moe_trace_set(pairs, 4, None, C.byref(cnt)) == L.MOE_EINVAL
+    assert lib.moe_trace_set(pairs, 4, ids, None) == L.MOE_EINVAL
+    assert lib.moe_trace_set(None, 0, None, None) == L.MOE_OK
+    assert lib.moe_kernel_name(5) == b"gateup"
+    assert lib.moe_kernel_name(-1) == b"?" and lib.moe_kernel_name(1000) == b"?"
+
+
+def test_binding_raises_on_error(lib):
+    import torch
+    x = torch.zeros((8, 6144), dtype=torch.int16)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.quant_fp8(torch.zeros((4, 100), dtype=torch.float32), torch.zeros((4, 100), dtype=torch.uint8),
+                      torch.zeros((4, 1), dtype=torch.float32))
+    assert ei.value.status == L.MOE_EINVAL

@@ -1,0 +1,219 @@
+"""GPU parity of the HIP path against the CPU oracle on the tiny layer
+(H=512, 16 experts top-4, I=256, shared I=256) and on ragged / edge row
+counts.  Every call goes through the C ABI (libmoe_ffn.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_02_amd as moe
+import synth
+from gpu_util import (GpuLayer, assert_routing_equal, assert_y_close, compare_h_codes, run_ffn, run_layer,
+                      run_oracle, say, t16, tf)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load()
+    cfg = synth.CONFIGS["tiny"]
+    gl = GpuLayer(synth.make_layer(cfg, threads=4))
+    x, mask = synth.activations(cfg)
+    return cfg, gl, x, mask
+
+
+def _rows(cfg, m, seed):
+    rng = np.random.default_rng(seed)
+    return synth.to_bf16_bits(rng.standard_normal((m, cfg.dims.hidden)).astype(np.float32))
+
+
+def test_quant_unit_bit_exact():
+    """moe_quant_fp8 on fp32 values spanning every e4m3 regime equals the oracle rule."""
+    rng = np.random.default_rng(21)
+    r, c = 64, 1024
+    v = (rng.standard_normal((r, c)) * np.exp(rng.uniform(-20, 20, (r, 1)))).astype(np.float32)
+    v[3, :128] = 0.0                      # zero block
+    v[4, 128:256] = -0.0
+    v[5, :] = np.where(rng.random(c) < 0.5, 0.0, v[5, :])
+    # blocks of exact e4m3 values x power-of-two scales, including midpoints
+    finite = np.array([x for x in range(256) if x not in (0x7F, 0xFF)], np.uint8)
+    codes = rng.choice(finite, size=(8, c)).astype(np.uint8)
+    codes[:, ::128] = 0x7E
+    v[8:16] = (oracle.decode_e4m3(codes) * 2.0 ** -7).astype(np.float32)
+    mids = (oracle.E4M3_TABLE[1:0x7E] + oracle.E4M3_TABLE[2:0x7F]) / 2
+    v[16, :mids.size] = mids.astype(np.float32)
+    v[16, 127] = 448.0
+    say("quant unit", v.shape)
+    gc = torch.empty((r, c), dtype=torch.uint8, device="cuda")
+    gs = torch.empty((r, c // 128), dtype=torch.float32, device="cuda")
+    moe.quant_fp8(tf(v), gc, gs)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quant_1x128(v)
+    assert np.array_equal(gs.cpu().numpy(), os_)
+    assert np.array_equal(gc.cpu().numpy(), oc)
+    # bf16 input path
+    xb = synth.to_bf16_bits(v)
+    moe.quant_fp8(t16(xb), gc, gs)
+    torch.cuda.synchronize()
+    oc2, os2 = oracle.quant_1x128(oracle.decode_bf16(xb).astype(np.float32))
+    assert np.array_equal(gs.cpu().numpy(), os2)
+    assert np.array_equal(gc.cpu().numpy(), oc2)
+
+
+def test_layer_parity(tiny):
+    cfg, gl, x, mask = tiny
+    say("tiny layer M=8")
+    g = run_layer(gl, x, mask)
+    o = run_oracle(gl, x, mask)
+    assert_routing_equal(g, o.routing, mask)
+    assert np.array_equal(g["x_codes"], o.x_codes)
+    assert np.array_equal(g["x_scales"], o.x_scales)
+    bad, n = compare_h_codes(g["h_codes"], g["h_scales"], o)
+    err = assert_y_close(g["y"], o)
+    say(f"tiny layer: max row rel err {err:.3e}, h code flips {bad}/{n}")
+
+
+def test_h_requant_unit_bit_exact(tiny):
+    """The GPU requantization fed the oracle's fl32(h) gives the oracle's codes."""
+    cfg, gl, x, mask = tiny
+    o = run_oracle(gl, x, mask)
+    xq, xs = oracle.quant_rows(x, mask)
+    ew = gl.expert_fn()
+    hs = []
+    for u, e in enumerate(o.routing.union_ids):
+        lo, hi = o.routing.offs[u], o.routing.offs[u + 1]
+        rr = o.routing.rows[lo:hi]
+        g = oracle.block_gemm(xq[rr], xs[rr], ew(int(e))["gate"], ew(int(e))["s_gate"])
+        uu = oracle.block_gemm(xq[rr], xs[rr], ew(int(e))["up"], ew(int(e))["s_up"])
+        hs.append((oracle.silu(g) * uu).astype(np.float32))
+    h32 = np.concatenate(hs)
+    gc = torch.empty(h32.shape, dtype=torch.uint8, device="cuda")
+    gsc = torch.empty((h32.shape[0], h32.shape[1] // 128), dtype=torch.float32, device="cuda")
+    moe.quant_fp8(tf(h32), gc, gsc)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quant_1x128(h32)
+    assert np.array_equal(gc.cpu().numpy(), oc)
+    assert np.array_equal(gsc.cpu().numpy(), os_)
+    for s in range(h32.shape[0]):
+        assert np.array_equal(o.h_codes[s], oc[s])
+
+
+def test_ffn_fp8_with_oracle_routing(tiny):
+    cfg, gl, x, mask = tiny
+    o = run_oracle(gl, x, mask, shared=False)
+    g = run_ffn(gl, x, mask, o.routing)
+    compare_h_codes(g["h_codes"], g["h_scales"], o)
+    err = assert_y_close(g["y"], o)
+    say(f"ffn_fp8 (routed only): max row rel err {err:.3e}")
+
+
+def test_pads_zero_under_nan_poison(tiny):
+    cfg, gl, x, mask = tiny
+    m2 = mask.copy()
+    m2[[1, 6]] = 0
+    xn = x.copy()
+    xn[[1, 6]] = 0x7FC0
+    xz = x.copy()
+    xz[[1, 6]] = 0
+    gn = run_layer(gl, xn, m2)
+    gz = run_layer(gl, xz, m2)
+    assert not gn["y"][[1, 6]].any()
+    assert np.array_equal(gn["y"], gz["y"])
+    assert (gn["ids"][[1, 6]] == -1).all() and (gn["slot_of"][[1, 6]] == -1).all()
+    o = run_oracle(gl, xn, m2)
+    assert_routing_equal(gn, o.routing, m2)
+    assert_y_close(gn["y"], o)
+
+
+def test_invariants_slot_permutation_companions_repeat(tiny):
+    cfg, gl, x, mask = tiny
+    base = run_layer(gl, x, mask)
+    again = run_layer(gl, x, mask)
+    assert np.array_equal(base["y"], again["y"])                     # repeat
+    perm = np.array([3, 7, 0, 5, 1, 6, 2, 4])
+    p = run_layer(gl, x[perm], mask[perm])
+    assert np.array_equal(p["y"], base["y"][perm])                   # slot permutation
+    assert np.array_equal(p["ids"], base["ids"][perm])
+    x2 = x.copy()
+    x2[[0, 2, 5]] = _rows(cfg, 3, 5)
+    c = run_layer(gl, x2, mask)
+    for r in (1, 3, 4, 6, 7):
+        assert np.array_equal(c["y"][r], base["y"][r])               # companion rows
+
+
+def test_decode_and_generic_paths_give_identical_rows(tiny):
+    """The same rows inside an 8-row step (fused decode kernels) and inside a
+    40-row step (grouped kernels + combine) give identical bits."""
+    cfg, gl, x, mask = tiny
+    base = run_layer(gl, x, mask)
+    big = _rows(cfg, 40, 9)
+    where = np.array([0, 7, 13, 21, 22, 30, 38, 39])
+    big[where] = x
+    g = run_layer(gl, big, np.ones(40, np.uint8))
+    assert np.array_equal(g["y"][where], base["y"])
+    assert np.array_equal(g["ids"][where], base["ids"])
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 17, 37, 200])
+def test_ragged_row_counts(tiny, m):
+    cfg, gl, _, _ = tiny
+    x = _rows(cfg, m, 100 + m)
+    mask = np.ones(m, np.uint8)
+    if m > 2:
+        mask[m // 2] = 0
+        x[m // 2] = 0x7FC0
+    say(f"tiny ragged M={m}")
+    g = run_layer(gl, x, mask)
+    o = run_oracle(gl, x, mask)
+    assert_routing_equal(g, o.routing, mask)
+    assert np.array_equal(g["x_codes"][mask != 0], o.x_codes[mask != 0])
+    compare_h_codes(g["h_codes"], g["h_scales"], o)
+    assert_y_close(g["y"], o)
+    assert not g["y"][mask == 0].any()
+
+
+def test_all_pad_rows(tiny):
+    cfg, gl, x, _ = tiny
+    mask = np.zeros(8, np.uint8)
+    xn = np.full_like(x, 0x7FC0)
+    g = run_layer(gl, xn, mask)
+    assert g["n_union"] == 0
+    assert not g["y"].any()
+    assert (g["ids"] == -1).all()
+
+
+def test_zero_rows_tie_to_lower_ids(tiny):
+    """All-zero inputs make every logit 0; with a zero bias every score ties and
+    the lowest ids win."""
+    cfg, gl, x, mask = tiny
+    zb = torch.zeros_like(gl.bias)
+    saved = gl.bias
+    gl.bias = zb
+    try:
+        x0 = np.zeros_like(x)
+        g = run_layer(gl, x0, mask)
+    finally:
+        gl.bias = saved
+    k = cfg.dims.top_k
+    assert (g["ids"] == np.arange(k)).all()
+    assert np.allclose(g["w"], cfg.dims.routed_scale / k, rtol=0, atol=1e-7)
+
+
+def test_malformed_routing_contributes_nothing(tiny):
+    cfg, gl, x, mask = tiny
+    o = run_oracle(gl, x, mask, shared=False)
+    bad = oracle.Routing(o.routing.ids, o.routing.w, o.routing.union_ids[::-1].copy(), o.routing.offs,
+                         o.routing.rows, o.routing.slot_of)          # union not ascending
+    g = run_ffn(gl, x, mask, bad)
+    assert not g["y"].any()
+
+
+def test_workspace_reuse_across_sizes(tiny):
+    """One workspace sized for the largest M serves smaller calls."""
+    cfg, gl, x, mask = tiny
+    a = run_layer(gl, x, mask, ws_rows=300)
+    b = run_layer(gl, x, mask)
+    assert np.array_equal(a["y"], b["y"])
