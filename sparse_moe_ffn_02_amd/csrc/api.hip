@@ -16,7 +16,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t sched, mtile, logits, rowbits, xq, xs, hbuf, hq, hs, gsh, ush, hsh, S, D, total;
+  size_t sched, mtile, logits, rowbits, xq, xs, hbuf, hq, hs, hsh, S, D, total;
 };
 
 Layout make_layout(const moe_dims& d, int M) {
@@ -37,12 +37,9 @@ Layout make_layout(const moe_dims& d, int M) {
   L.hbuf = take(m * K * I * sizeof(float));
   L.hq = take(m * K * I);
   L.hs = take(m * K * (I / 128) * sizeof(float));
-  L.gsh = take(m * Is * sizeof(float));
-  L.ush = take(m * Is * sizeof(float));
   L.hsh = take(m * Is * sizeof(uint16_t));
-  const bool generic = M > kDecodeMaxRows;
-  L.S = take(generic ? m * H * sizeof(float) : 0);
-  L.D = take(generic ? m * K * H * sizeof(float) : 0);
+  L.S = take(m * H * sizeof(float));
+  L.D = take(m * K * H * sizeof(float));
   L.total = off;
   return L;
 }
@@ -158,8 +155,6 @@ FfnArgs ffn_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t* mas
   a.hbuf = reinterpret_cast<float*>(ws + L.hbuf);
   a.hq = (taps && taps->h_codes) ? taps->h_codes : reinterpret_cast<uint8_t*>(ws + L.hq);
   a.hs = (taps && taps->h_scales) ? taps->h_scales : reinterpret_cast<float*>(ws + L.hs);
-  a.gsh = reinterpret_cast<float*>(ws + L.gsh);
-  a.ush = reinterpret_cast<float*>(ws + L.ush);
   a.hsh = reinterpret_cast<uint16_t*>(ws + L.hsh);
   a.S = reinterpret_cast<float*>(ws + L.S);
   a.D = reinterpret_cast<float*>(ws + L.D);
@@ -177,7 +172,7 @@ Tracer g_trace;
 
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
-    "down_combine_decode", "down", "combine", "quant",
+    "down_combine_decode", "down", "combine", "quant", "route_small",
 };
 
 }  // namespace
@@ -235,8 +230,19 @@ int moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
   if (M == 0) return MOE_OK;
   const Layout L = make_layout(*dims, M);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
-  const RouteArgs a = route_args(*dims, M, x, row_mask, *router, *out, static_cast<char*>(ws), L);
-  return to_status(launch_route(a, static_cast<hipStream_t>(stream)));
+  char* w = static_cast<char*>(ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RouteArgs a = route_args(*dims, M, x, row_mask, *router, *out, w, L);
+  FfnArgs p;
+  memset(&p, 0, sizeof(p));
+  p.M = M;
+  p.H = dims->hidden;
+  p.x = x;
+  p.mask = row_mask;
+  p.xq = reinterpret_cast<uint8_t*>(w + L.xq);
+  p.xs = reinterpret_cast<float*>(w + L.xs);
+  if ((st = to_status(launch_prep(p, s))) != MOE_OK) return st;
+  return to_status(launch_route(a, s));
 }
 
 int moe_ffn_fp8(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
@@ -254,7 +260,7 @@ int moe_ffn_fp8(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
   const FfnArgs a = ffn_args(*dims, M, x, row_mask, *in, *experts, nullptr, y, taps, static_cast<char*>(ws), L);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = to_status(launch_quant_x(a, s))) != MOE_OK) return st;
+  if ((st = to_status(launch_prep(a, s))) != MOE_OK) return st;
   if ((st = to_status(launch_plan(a, s))) != MOE_OK) return st;
   return to_status(launch_ffn(a, s));
 }
@@ -282,9 +288,9 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
   char* w = static_cast<char*>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const RouteArgs ra = route_args(*dims, M, x, row_mask, *router, *out, w, L);
-  if ((st = to_status(launch_route(ra, s))) != MOE_OK) return st;
   const FfnArgs a = ffn_args(*dims, M, x, row_mask, *out, *experts, shared, y, taps, w, L);
-  if ((st = to_status(launch_quant_x(a, s))) != MOE_OK) return st;
+  if ((st = to_status(launch_prep(a, s))) != MOE_OK) return st;
+  if ((st = to_status(launch_route(ra, s))) != MOE_OK) return st;
   return to_status(launch_ffn(a, s));
 }
 

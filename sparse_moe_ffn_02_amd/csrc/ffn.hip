@@ -18,12 +18,13 @@
 //   combine      acc = fma(w_j, D[slot(r, j)], acc) for j ascending, then
 //                + S[r] when the shared expert is present, then bf16 RNE.
 // Which tile, wave or kernel computes an element never changes its bits.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kPersistentBlocks = 512;   // 256 CUs x 2 workgroups of 4 waves
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const uint4 lo = *reinterpret_cast<const uint4*>(p);
@@ -84,32 +85,28 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* in, const uint8_t* 
   quant_block<T>(in + (size_t)r * C + b * kBlk, codes + (size_t)r * C + b * kBlk, scales + (size_t)r * nb + b, lane);
 }
 
-// After gate/up: requantize routed h per (slot, block) for the slots in use,
-// and form the shared expert's h_s = bf16(silu(g) * u) for real rows.
+// First kernel of every call: quantize x (real rows).
+__global__ __launch_bounds__(256) void k_prep(const uint16_t* x, const uint8_t* mask, int M, int H, uint8_t* xq,
+                                              float* xs) {
+  const int lane = threadIdx.x & 63;
+  const int nb = H / kBlk;
+  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = (int)(item / nb);
+  const int b = (int)(item % nb);
+  if (r >= M || !row_real(mask, r)) return;
+  quant_block<uint16_t>(x + (size_t)r * H + b * kBlk, xq + (size_t)r * H + b * kBlk, xs + (size_t)r * nb + b, lane);
+}
+
+// After gate/up: requantize routed h per (slot, block) for the slots in use.
 __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nbI = a.I / kBlk;
-  const long n_routed = (long)a.M * a.K * nbI;
-  if (item < n_routed) {
-    const int slot = (int)(item / nbI);
-    const int b = (int)(item % nbI);
-    if (slot >= a.sched[SCHED_SLOTS]) return;
-    quant_block<float>(a.hbuf + (size_t)slot * a.I + b * kBlk, a.hq + (size_t)slot * a.I + b * kBlk,
-                       a.hs + (size_t)slot * nbI + b, lane);
-    return;
-  }
-  if (a.Is == 0) return;
-  const long it = item - n_routed;
-  const int nbS = a.Is / kBlk;
-  const int r = (int)(it / nbS);
-  const int b = (int)(it % nbS);
-  if (r >= a.M || !row_real(a.mask, r)) return;
-  const size_t o = (size_t)r * a.Is + b * kBlk + 2 * lane;
-  const float2 g = *reinterpret_cast<const float2*>(a.gsh + o);
-  const float2 u = *reinterpret_cast<const float2*>(a.ush + o);
-  const uint32_t h = (uint32_t)f32_to_bf16(silu_mul(g.x, u.x)) | ((uint32_t)f32_to_bf16(silu_mul(g.y, u.y)) << 16);
-  *reinterpret_cast<uint32_t*>(a.hsh + o) = h;
+  const int slot = (int)(item / nbI);
+  const int b = (int)(item % nbI);
+  if (slot >= a.sched[SCHED_SLOTS]) return;
+  quant_block<float>(a.hbuf + (size_t)slot * a.I + b * kBlk, a.hq + (size_t)slot * a.I + b * kBlk,
+                     a.hs + (size_t)slot * nbI + b, lane);
 }
 
 // ---------------------------------------------------------------- plan
@@ -170,11 +167,21 @@ __device__ __forceinline__ Tile routed_tile(const FfnArgs& a, int mtg) {
   return t;
 }
 
-// Routed gate+up for 16 columns of I and one tile of <= 16 slots; writes
-// h = silu(G) * U (fp32) for the tile's slots.
+// One wave per work item.  The grid covers the largest item count the call
+// can produce (the union is only known on the device); waves past the real
+// count exit at once, and the hardware dispatcher balances the rest.
+__device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + (threadIdx.x >> 6); }
+
+constexpr int kRing = 4;      // fp8 K-blocks in flight per wave
+constexpr int kRingBf = 8;    // bf16 K-steps (32 deep) in flight per wave
+
+// Routed gate+up for 8 columns of I and one tile of <= 16 slots.  The 16
+// rows of the MFMA A operand are gate rows n0..n0+7 (rows 0-7) and up rows
+// n0..n0+7 (rows 8-15), so lane l (l < 32) holds G and lane l + 32 holds U of
+// the same (slot, n).  Writes h = silu(G) * U (fp32) for the tile's slots.
 __device__ void routed_gateup(const FfnArgs& a, const Tile& t, int nt, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int n0 = nt * 16;
+  const int n0 = nt * 8;
   const int nkb = a.H / kBlk;
   int row = -1;
   if (c < t.mcnt) {
@@ -183,91 +190,112 @@ __device__ void routed_gateup(const FfnArgs& a, const Tile& t, int nt, int lane)
   }
   const uint8_t* bp = a.xq + (size_t)(row < 0 ? 0 : row) * a.H + kq * 32;
   const float* sxp = a.xs + (size_t)(row < 0 ? 0 : row) * nkb;
-  const size_t wrow = ((size_t)t.e * a.I + n0 + c) * a.H + kq * 32;
-  const uint8_t* gp = a.wg + wrow;
-  const uint8_t* up = a.wu + wrow;
-  const size_t srow = ((size_t)t.e * (a.I / kBlk) + n0 / kBlk) * nkb;
-  const float* sgp = a.sg + srow;
-  const float* sup = a.su + srow;
+  const uint8_t* wp = (c < 8 ? a.wg : a.wu) + ((size_t)t.e * a.I + n0 + (c & 7)) * a.H + kq * 32;
+  const float* swp = (kq < 2 ? a.sg : a.su) + ((size_t)t.e * (a.I / kBlk) + n0 / kBlk) * nkb;
   const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  v8i ag = load32(gp), au = load32(up);
-  v8i b = row >= 0 ? load32(bp) : zero8;
-  for (int kb = 0; kb < nkb; ++kb) {
-    v8i ag_n = ag, au_n = au, b_n = b;
-    if (kb + 1 < nkb) {
-      ag_n = load32(gp + (kb + 1) * kBlk);
-      au_n = load32(up + (kb + 1) * kBlk);
-      if (row >= 0) b_n = load32(bp + (kb + 1) * kBlk);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v8i wb[kRing], xb[kRing];
+  float sxb[kRing], swb[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    if (i < nkb) {
+      wb[i] = load32(wp + i * kBlk);
+      xb[i] = row >= 0 ? load32(bp + i * kBlk) : zero8;
+      sxb[i] = row >= 0 ? sxp[i] : 0.0f;
+      swb[i] = swp[i];
     }
-    const float sx = row >= 0 ? sxp[kb] : 0.0f;
-    const v4f pg = mfma_fp8_k128(ag, b);
-    const v4f pu = mfma_fp8_k128(au, b);
-    scale_acc(accg, pg, sx, sgp[kb]);
-    scale_acc(accu, pu, sx, sup[kb]);
-    ag = ag_n; au = au_n; b = b_n;
   }
-  if (row >= 0) {
+  for (int kb0 = 0; kb0 < nkb; kb0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int kb = kb0 + i;
+      if (kb >= nkb) break;
+      const v4f p = mfma_fp8_k128(wb[i], xb[i]);
+      scale_acc(acc, p, sxb[i], swb[i]);
+      const int nk = kb + kRing;
+      if (nk < nkb) {
+        wb[i] = load32(wp + nk * kBlk);
+        if (row >= 0) {
+          xb[i] = load32(bp + nk * kBlk);
+          sxb[i] = sxp[nk];
+        }
+        swb[i] = swp[nk];
+      }
+    }
+  }
+  float u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[i], 32, 64);
+  if (kq < 2 && row >= 0) {
     float4 h;
-    h.x = silu_mul(accg[0], accu[0]);
-    h.y = silu_mul(accg[1], accu[1]);
-    h.z = silu_mul(accg[2], accu[2]);
-    h.w = silu_mul(accg[3], accu[3]);
+    h.x = silu_mul(acc[0], u[0]);
+    h.y = silu_mul(acc[1], u[1]);
+    h.z = silu_mul(acc[2], u[2]);
+    h.w = silu_mul(acc[3], u[3]);
     *reinterpret_cast<float4*>(a.hbuf + (size_t)(t.s0 + c) * a.I + n0 + kq * 4) = h;
   }
 }
 
-// Shared gate (which == 0) or up (which == 1) for 16 rows and 16 columns.
-__device__ void shared_gateup(const FfnArgs& a, int mt, int nt, int which, int lane) {
+// Shared gate+up for 8 columns of I_s and 16 rows, arranged as above (gate
+// rows 0-7, up rows 8-15); writes h_s = bf16(silu(g) * u).
+__device__ void shared_gateup(const FfnArgs& a, int mt, int nt, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int n0 = nt * 16;
+  const int n0 = nt * 8;
   const int row = mt * kMTile + c;
   const bool valid = row < a.M && row_real(a.mask, row);
-  const uint16_t* wp = (which ? a.wsu : a.wsg) + (size_t)(n0 + c) * a.H + kq * 8;
+  const uint16_t* wp = (c < 8 ? a.wsg : a.wsu) + (size_t)(n0 + (c & 7)) * a.H + kq * 8;
   const uint16_t* bp = a.x + (size_t)(valid ? row : 0) * a.H + kq * 8;
   const v4i zero4 = {0, 0, 0, 0};
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   const int ns = a.H / 32;
-  v4i w = load16(wp);
-  v4i b = valid ? load16(bp) : zero4;
-  for (int s = 0; s < ns; ++s) {
-    v4i w_n = w, b_n = b;
-    if (s + 1 < ns) {
-      w_n = load16(wp + (s + 1) * 32);
-      if (valid) b_n = load16(bp + (s + 1) * 32);
+  v4i wb[kRingBf], xb[kRingBf];
+#pragma unroll
+  for (int i = 0; i < kRingBf; ++i) {
+    if (i < ns) {
+      wb[i] = load16(wp + i * 32);
+      xb[i] = valid ? load16(bp + i * 32) : zero4;
     }
-    acc = mfma_bf16_k32(w, b, acc);
-    w = w_n; b = b_n;
   }
-  if (valid) {
-    float* out = (which ? a.ush : a.gsh) + (size_t)row * a.Is + n0 + kq * 4;
-    *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  for (int s0 = 0; s0 < ns; s0 += kRingBf) {
+#pragma unroll
+    for (int i = 0; i < kRingBf; ++i) {
+      const int st = s0 + i;
+      if (st >= ns) break;
+      acc = mfma_bf16_k32(wb[i], xb[i], acc);
+      const int nx = st + kRingBf;
+      if (nx < ns) {
+        wb[i] = load16(wp + nx * 32);
+        if (valid) xb[i] = load16(bp + nx * 32);
+      }
+    }
+  }
+  float u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[i], 32, 64);
+  if (kq < 2 && valid) {
+    const v4f h = {silu_mul(acc[0], u[0]), silu_mul(acc[1], u[1]), silu_mul(acc[2], u[2]), silu_mul(acc[3], u[3])};
+    store_bf16x4(a.hsh + (size_t)row * a.Is + n0 + kq * 4, h);
   }
 }
 
-// Persistent: shared items first (gate and up of 16x16 tiles), then routed
-// items (column tile x 16 columns of I).  Each wave takes whole items.
-__global__ __launch_bounds__(256) void k_gateup(FfnArgs a) {
+// Shared items first (the longest), then routed items.
+__global__ __launch_bounds__(256, 2) void k_gateup(FfnArgs a) {
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwav = gridDim.x * 4;
-  const int ntI = a.I / 16;
-  const int ntS = a.Is / 16;
-  const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntS * 2 : 0;
+  const int ntI = a.I / 8;
+  const int ntS = a.Is / 8;
+  const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntS : 0;
   const int total = n_sh + a.sched[SCHED_MTILES] * ntI;
-  for (int t = gw; t < total; t += nwav) {
-    if (t < n_sh) {
-      const int which = t & 1;
-      const int tt = t >> 1;
-      shared_gateup(a, tt / ntS, tt % ntS, which, lane);
-    } else {
-      const int tt = t - n_sh;
-      routed_gateup(a, routed_tile(a, tt / ntI), tt % ntI, lane);
-    }
+  const int t = wave_item();
+  if (t >= total) return;
+  if (t < n_sh) {
+    shared_gateup(a, t / ntS, t % ntS, lane);
+  } else {
+    const int tt = t - n_sh;
+    routed_gateup(a, routed_tile(a, tt / ntI), tt % ntI, lane);
   }
 }
 
-// ---------------------------------------------------------------- down (generic)
+// ---------------------------------------------------------------- down
 // D[slot, n] for 16 columns of H and one tile of <= 16 slots.
 __device__ __forceinline__ v4f routed_down_chain(const FfnArgs& a, int e, int slot, int n0, int lane) {
   const int c = lane & 15, kq = lane >> 4;
@@ -278,18 +306,34 @@ __device__ __forceinline__ v4f routed_down_chain(const FfnArgs& a, int e, int sl
   const float* swp = a.sd + ((size_t)e * (a.H / kBlk) + n0 / kBlk) * nkb;
   const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  v8i w = load32(wp);
-  v8i b = slot >= 0 ? load32(bp) : zero8;
-  for (int kb = 0; kb < nkb; ++kb) {
-    v8i w_n = w, b_n = b;
-    if (kb + 1 < nkb) {
-      w_n = load32(wp + (kb + 1) * kBlk);
-      if (slot >= 0) b_n = load32(bp + (kb + 1) * kBlk);
+  v8i wb[kRing], hb[kRing];
+  float shb[kRing], swb[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    if (i < nkb) {
+      wb[i] = load32(wp + i * kBlk);
+      hb[i] = slot >= 0 ? load32(bp + i * kBlk) : zero8;
+      shb[i] = slot >= 0 ? shp[i] : 0.0f;
+      swb[i] = swp[i];
     }
-    const float sh = slot >= 0 ? shp[kb] : 0.0f;
-    const v4f p = mfma_fp8_k128(w, b);
-    scale_acc(acc, p, sh, swp[kb]);
-    w = w_n; b = b_n;
+  }
+  for (int kb0 = 0; kb0 < nkb; kb0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int kb = kb0 + i;
+      if (kb >= nkb) break;
+      const v4f p = mfma_fp8_k128(wb[i], hb[i]);
+      scale_acc(acc, p, shb[i], swb[i]);
+      const int nk = kb + kRing;
+      if (nk < nkb) {
+        wb[i] = load32(wp + nk * kBlk);
+        if (slot >= 0) {
+          hb[i] = load32(bp + nk * kBlk);
+          shb[i] = shp[nk];
+        }
+        swb[i] = swp[nk];
+      }
+    }
   }
   return acc;
 }
@@ -301,45 +345,54 @@ __device__ __forceinline__ v4f shared_down_chain(const FfnArgs& a, int row_or_ne
   const v4i zero4 = {0, 0, 0, 0};
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   const int ns = a.Is / 32;
-  v4i w = load16(wp);
-  v4i b = row_or_neg >= 0 ? load16(bp) : zero4;
-  for (int s = 0; s < ns; ++s) {
-    v4i w_n = w, b_n = b;
-    if (s + 1 < ns) {
-      w_n = load16(wp + (s + 1) * 32);
-      if (row_or_neg >= 0) b_n = load16(bp + (s + 1) * 32);
+  v4i wb[kRingBf], hb[kRingBf];
+#pragma unroll
+  for (int i = 0; i < kRingBf; ++i) {
+    if (i < ns) {
+      wb[i] = load16(wp + i * 32);
+      hb[i] = row_or_neg >= 0 ? load16(bp + i * 32) : zero4;
     }
-    acc = mfma_bf16_k32(w, b, acc);
-    w = w_n; b = b_n;
+  }
+  for (int st0 = 0; st0 < ns; st0 += kRingBf) {
+#pragma unroll
+    for (int i = 0; i < kRingBf; ++i) {
+      const int st = st0 + i;
+      if (st >= ns) break;
+      acc = mfma_bf16_k32(wb[i], hb[i], acc);
+      const int nx = st + kRingBf;
+      if (nx < ns) {
+        wb[i] = load16(wp + nx * 32);
+        if (row_or_neg >= 0) hb[i] = load16(bp + nx * 32);
+      }
+    }
   }
   return acc;
 }
 
-// Persistent: shared-down items first, then routed down items.
-__global__ __launch_bounds__(256) void k_down(FfnArgs a) {
+// Shared-down items first, then routed down items.
+__global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwav = gridDim.x * 4;
   const int ntH = a.H / 16;
   const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntH : 0;
   const int total = n_sh + a.sched[SCHED_MTILES] * ntH;
-  for (int t = gw; t < total; t += nwav) {
+  const int t = wave_item();
+  if (t < total) {
     if (t < n_sh) {
       const int mt = t / ntH, nt = t % ntH;
       const int row = mt * kMTile + c;
       const bool valid = row < a.M && row_real(a.mask, row);
-      const v4f s = shared_down_chain(a, valid ? row : -1, nt * 16, lane);
+      const v4f r = shared_down_chain(a, valid ? row : -1, nt * 16, lane);
       if (valid)
-        *reinterpret_cast<float4*>(a.S + (size_t)row * a.H + nt * 16 + kq * 4) = make_float4(s[0], s[1], s[2], s[3]);
+        *reinterpret_cast<float4*>(a.S + (size_t)row * a.H + nt * 16 + kq * 4) = make_float4(r[0], r[1], r[2], r[3]);
     } else {
       const int tt = t - n_sh;
       const Tile tl = routed_tile(a, tt / ntH);
       const int nt = tt % ntH;
       const int slot = c < tl.mcnt ? tl.s0 + c : -1;
-      const v4f d = routed_down_chain(a, tl.e, slot, nt * 16, lane);
+      const v4f r = routed_down_chain(a, tl.e, slot, nt * 16, lane);
       if (slot >= 0)
-        *reinterpret_cast<float4*>(a.D + (size_t)slot * a.H + nt * 16 + kq * 4) = make_float4(d[0], d[1], d[2], d[3]);
+        *reinterpret_cast<float4*>(a.D + (size_t)slot * a.H + nt * 16 + kq * 4) = make_float4(r[0], r[1], r[2], r[3]);
     }
   }
 }
@@ -378,94 +431,6 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
   store_bf16x4(yp, acc);
 }
 
-// ---------------------------------------------------------------- down + combine (decode)
-// For M <= 16 rows: one workgroup of 4 waves per 16 columns of H.  Jobs are
-// the union experts in ascending order followed by the shared expert; job j
-// runs on wave j % 4.  Each round the waves leave their 16x16 results in LDS
-// and wave 0 folds them into the per-row accumulators in job order, so every
-// row sees the same fma chain as in k_combine.
-constexpr int kDecMaxU = 256;
-
-__global__ __launch_bounds__(256) void k_down_combine_decode(FfnArgs a, int with_shared) {
-  __shared__ int slot_tbl[kDecMaxU][kDecodeMaxRows];
-  __shared__ float w_tbl[kDecMaxU][kDecodeMaxRows];
-  __shared__ v4f dres[4][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int nu = a.sched[SCHED_NUNION];
-  const int slots = a.sched[SCHED_SLOTS];
-  for (int i = threadIdx.x; i < nu * kDecodeMaxRows; i += blockDim.x) {
-    slot_tbl[i / kDecodeMaxRows][i % kDecodeMaxRows] = -1;
-    w_tbl[i / kDecodeMaxRows][i % kDecodeMaxRows] = 0.0f;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < a.M * a.K; i += blockDim.x) {
-    const int r = i / a.K;
-    if (!row_real(a.mask, r)) continue;
-    const int e = a.ids[i];
-    const int s = a.slot_of[i];
-    if (s < 0 || s >= slots) continue;
-    int lo = 0, hi = nu - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.union_ids[mid] < e) lo = mid + 1; else hi = mid;
-    }
-    if (nu > 0 && a.union_ids[lo] == e) {
-      slot_tbl[lo][r] = s;
-      w_tbl[lo][r] = a.w[i];
-    }
-  }
-  __syncthreads();
-  const int njobs = nu + (with_shared ? 1 : 0);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  v4f sres = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < njobs; j0 += 4) {
-    const int job = j0 + wave;
-    if (job < nu) {
-      const int slot = slot_tbl[job][c];
-      dres[wave][lane] = routed_down_chain(a, a.union_ids[job], slot, n0, lane);
-    } else if (job < njobs) {
-      const bool valid = c < a.M && row_real(a.mask, c);
-      dres[wave][lane] = shared_down_chain(a, valid ? c : -1, n0, lane);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      for (int q = 0; q < 4 && j0 + q < njobs; ++q) {
-        const int jb = j0 + q;
-        const v4f d = dres[q][lane];
-        if (jb < nu) {
-          if (slot_tbl[jb][c] >= 0) {
-            const float wj = w_tbl[jb][c];
-            acc[0] = __builtin_fmaf(wj, d[0], acc[0]);
-            acc[1] = __builtin_fmaf(wj, d[1], acc[1]);
-            acc[2] = __builtin_fmaf(wj, d[2], acc[2]);
-            acc[3] = __builtin_fmaf(wj, d[3], acc[3]);
-          }
-        } else {
-          sres = d;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (wave == 0 && c < a.M) {
-    uint16_t* yp = a.y + (size_t)c * a.H + n0 + kq * 4;
-    if (!row_real(a.mask, c)) {
-      *reinterpret_cast<uint2*>(yp) = make_uint2(0u, 0u);
-    } else {
-      if (with_shared) {
-        acc[0] = acc[0] + sres[0];
-        acc[1] = acc[1] + sres[1];
-        acc[2] = acc[2] + sres[2];
-        acc[3] = acc[3] + sres[3];
-      }
-      store_bf16x4(yp, acc);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s) {
@@ -473,10 +438,10 @@ hipError_t launch_plan(const FfnArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_quant_x(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_prep(const FfnArgs& a, hipStream_t s) {
   const long waves = (long)a.M * (a.H / kBlk);
-  MOE_LAUNCH(KID_QUANT_X, k_quant_rows<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a.x, a.mask,
-             a.M, a.H, a.xq, a.xs);
+  MOE_LAUNCH(KID_QUANT_X, k_prep, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a.x, a.mask, a.M, a.H, a.xq,
+             a.xs);
   return hipSuccess;
 }
 
@@ -496,14 +461,15 @@ hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const int with_shared = a.Is > 0 ? 1 : 0;
-  MOE_LAUNCH(KID_GATEUP, k_gateup, dim3(kPersistentBlocks), dim3(256), 0, s, a);
-  const long post_waves = (long)a.M * a.K * (a.I / kBlk) + (with_shared ? (long)a.M * (a.Is / kBlk) : 0);
+  // column tiles of <= 16 slots: at most ceil(M*K/16) + (union size) of them
+  const long mtiles_max = ((long)a.M * a.K + kMTile - 1) / kMTile + std::min<long>(a.E, (long)a.M * a.K);
+  const long sh_tiles = with_shared ? (a.M + kMTile - 1) / kMTile : 0;
+  const long gu_items = sh_tiles * (a.Is / 8) + mtiles_max * (a.I / 8);
+  MOE_LAUNCH(KID_GATEUP, k_gateup, dim3((unsigned)((gu_items + 3) / 4)), dim3(256), 0, s, a);
+  const long post_waves = (long)a.M * a.K * (a.I / kBlk);
   MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)((post_waves + 3) / 4)), dim3(256), 0, s, a);
-  if (a.M <= kDecodeMaxRows) {
-    MOE_LAUNCH(KID_DOWN_DECODE, k_down_combine_decode, dim3(a.H / 16), dim3(256), 0, s, a, with_shared);
-    return hipSuccess;
-  }
-  MOE_LAUNCH(KID_DOWN, k_down, dim3(kPersistentBlocks), dim3(256), 0, s, a);
+  const long dn_items = (sh_tiles + mtiles_max) * (a.H / 16);
+  MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)((dn_items + 3) / 4)), dim3(256), 0, s, a);
   const long threads = (long)a.M * (a.H / 4);
   MOE_LAUNCH(KID_COMBINE, k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, with_shared);
   return hipSuccess;

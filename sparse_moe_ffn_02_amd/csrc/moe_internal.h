@@ -8,7 +8,7 @@
 namespace moe {
 
 constexpr int kMTile = 16;          // slots (or rows) per MFMA column tile
-constexpr int kDecodeMaxRows = 16;  // rows served by the fused decode down/combine kernel
+constexpr int kDecodeMaxRows = 16;  // rows served by the fused small-step router kernel
 
 // sched[] words written by the union / plan kernels and read by the FFN kernels
 enum { SCHED_NUNION = 0, SCHED_MTILES = 1, SCHED_SLOTS = 2, SCHED_BAD = 3, SCHED_WORDS = 8 };
@@ -56,7 +56,6 @@ struct FfnArgs {
   uint8_t* xq; float* xs;  // [M, H], [M, H/128]
   float* hbuf;             // [M*K, I]
   uint8_t* hq; float* hs;  // [M*K, I], [M*K, I/128]
-  float* gsh; float* ush;  // shared gate/up outputs [M, Is] (fp32)
   uint16_t* hsh;           // [M, Is] bf16 shared h
   float* S;                // [M, H]
   float* D;                // [M*K, H]
@@ -66,7 +65,7 @@ struct FfnArgs {
 // Kernel ids reported by the timing hook (moe_trace_set).
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
-  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_COUNT
+  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_COUNT
 };
 
 void trace_before(hipStream_t s);
@@ -85,7 +84,7 @@ void trace_after(int kid, hipStream_t s);
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s);
-hipError_t launch_quant_x(const FfnArgs& a, hipStream_t s);
+hipError_t launch_prep(const FfnArgs& a, hipStream_t s);   // quantize x
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);

@@ -74,29 +74,32 @@ __global__ __launch_bounds__(256) void k_router_logits(RouteArgs a) {
 // One wave per row.  c = sigmoid(l) + bias; the k largest c win, exact ties
 // to the lower expert id.  Output ids ascending; w = scale * sig / sum(sig)
 // with the sum taken in ascending id order (float64, stored as float32).
+// Pad rows get ids -1, weights 0, slot_of -1 and an empty expert bitmask.
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 256;
 
-__global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.M) return;
+__device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_bits) {
   const int nwords = (a.E + 31) / 32;
   const bool real = (a.mask == nullptr || a.mask[row] != 0);
   if (!real) {
     if (lane < a.K) {
       a.ids[(size_t)row * a.K + lane] = -1;
       a.w[(size_t)row * a.K + lane] = 0.0f;
+      a.slot_of[(size_t)row * a.K + lane] = -1;
     }
-    if (lane < nwords) a.rowbits[(size_t)row * nwords + lane] = 0u;
+    if (lane < nwords) {
+      a.rowbits[(size_t)row * nwords + lane] = 0u;
+      if (lds_bits) lds_bits[lane] = 0u;
+    }
     return;
   }
   double c[4], sg[4];
-  bool ok[4];
+  bool ok[4], picked[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     ok[q] = e < a.E;
+    picked[q] = false;
     c[q] = -INFINITY;
     sg[q] = 0.0;
     if (ok[q]) {
@@ -106,59 +109,70 @@ __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
       c[q] = (cc == cc) ? cc : -INFINITY;
     }
   }
-  int sel[kMaxTopK];
-  double ssel[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    sel[j] = 0x7fffffff;
-    ssel[j] = 0.0;
-    if (j >= a.K) continue;
-    double bc = -INFINITY, bs = 0.0;
+  // k rounds of a wave-wide argmax of (c, -id)
+  for (int j = 0; j < a.K; ++j) {
+    double bc = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
-      if (ok[q] && (c[q] > bc || (c[q] == bc && e < be))) { bc = c[q]; be = e; bs = sg[q]; }
+      if (ok[q] && (c[q] > bc || (c[q] == bc && e < be))) { bc = c[q]; be = e; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const double oc = __shfl_xor(bc, o, 64);
       const int oe = __shfl_xor(be, o, 64);
-      const double os = __shfl_xor(bs, o, 64);
-      if (oc > bc || (oc == bc && oe < be)) { bc = oc; be = oe; bs = os; }
+      if (oc > bc || (oc == bc && oe < be)) { bc = oc; be = oe; }
     }
-    sel[j] = be;
-    ssel[j] = bs;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (lane + 64 * q == be) ok[q] = false;
+      if (lane + 64 * q == be) { ok[q] = false; picked[q] = true; }
   }
-  // ascending id order (k <= 16, wave-uniform insertion sort)
+  // Ascending id order: id = lane + 64 q, so positions follow q, then lane.
+  // Each pick is pushed to lane `position` (ds_permute); lane 63 is never a
+  // position (k <= 16) and takes the pushes of lanes without a pick.
+  int my_e = -1;
+  double my_s = 0.0;
+  int base = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int i = 1; i < kMaxTopK; ++i) {
-#pragma unroll
-    for (int j = i; j > 0; --j) {
-      if (sel[j] < sel[j - 1]) {
-        const int te = sel[j]; sel[j] = sel[j - 1]; sel[j - 1] = te;
-        const double ts = ssel[j]; ssel[j] = ssel[j - 1]; ssel[j - 1] = ts;
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t m = __ballot(picked[q]);
+    const int pos = base + __popcll(m & below);
+    const int dst = picked[q] ? pos : 63;
+    const int tag = picked[q] ? (lane + 64 * q + 1) : 0;
+    const uint64_t sb = (uint64_t)__double_as_longlong(sg[q]);
+    const int rt = __builtin_amdgcn_ds_permute(dst * 4, tag);
+    const int rlo = __builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)sb);
+    const int rhi = __builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)(sb >> 32));
+    if (rt != 0 && lane < a.K) {
+      my_e = rt - 1;
+      my_s = __longlong_as_double((long long)(((uint64_t)(uint32_t)rhi << 32) | (uint32_t)rlo));
+    }
+    if (lane < 8) {
+      const uint32_t word = (uint32_t)(lane == 2 * q ? m : (lane == 2 * q + 1 ? (m >> 32) : 0ull));
+      if (lane == 2 * q || lane == 2 * q + 1) {
+        if (lane < nwords) {
+          a.rowbits[(size_t)row * nwords + lane] = word;
+          if (lds_bits) lds_bits[lane] = word;
+        }
       }
     }
+    base += __popcll(m);
   }
   double tot = 0.0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < a.K) tot += ssel[j];
-  uint32_t word = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= a.K) continue;
-    if (lane == j) {
-      a.ids[(size_t)row * a.K + j] = sel[j];
-      a.w[(size_t)row * a.K + j] = (float)((double)a.scale * (ssel[j] / tot));
-    }
-    if ((sel[j] >> 5) == lane) word |= 1u << (sel[j] & 31);
+  for (int j = 0; j < a.K; ++j) tot += __shfl(my_s, j, 64);     // ascending id order
+  if (lane < a.K) {
+    a.ids[(size_t)row * a.K + lane] = my_e;
+    a.w[(size_t)row * a.K + lane] = (float)((double)a.scale * (my_s / tot));
   }
-  if (lane < nwords) a.rowbits[(size_t)row * nwords + lane] = word;
+}
+
+__global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
+  select_row(a, row, lane, nullptr);
 }
 
 // ---------------------------------------------------------------- union
@@ -236,13 +250,131 @@ __global__ __launch_bounds__(1024) void k_union(RouteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- small steps
+// For M <= 16 rows: one workgroup per expert with one wave per row computing
+// that row's logit by the procedure above (chunks streamed through a ring);
+// then one workgroup selects every row's top-k and builds the union and the
+// row lists in LDS.  The kernel boundary orders the two phases.
+constexpr int kSmallRing = 4;
+
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(x, o, 64);
+    if (lane >= o) x += n;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = tmp[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__device__ __forceinline__ double dot_chunk(const uint4& xv, const uint4& wv, double acc) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const double xd = (double)bf16_to_f32((uint16_t)(xw[t >> 1] >> ((t & 1) * 16)));
+    const double wd = (double)bf16_to_f32((uint16_t)(ww[t >> 1] >> ((t & 1) * 16)));
+    acc = __builtin_fma(xd, wd, acc);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x;
+  const int r = threadIdx.x >> 6;          // one wave per row
+  if (r >= a.M || (a.mask != nullptr && a.mask[r] == 0)) return;
+  const uint16_t* wrow = a.wr + (size_t)e * a.H + 8 * lane;
+  const uint16_t* xrow = a.x + (size_t)r * a.H + 8 * lane;
+  const int nch = (a.H + 511) / 512;
+  uint4 wv[kSmallRing], xv[kSmallRing];
+#pragma unroll
+  for (int i = 0; i < kSmallRing; ++i) {
+    const bool in = i < nch && 512 * i + 8 * lane < a.H;
+    wv[i] = in ? *reinterpret_cast<const uint4*>(wrow + 512 * i) : make_uint4(0, 0, 0, 0);
+    xv[i] = in ? *reinterpret_cast<const uint4*>(xrow + 512 * i) : make_uint4(0, 0, 0, 0);
+  }
+  double acc = 0.0;
+  for (int i0 = 0; i0 < nch; i0 += kSmallRing) {
+#pragma unroll
+    for (int ii = 0; ii < kSmallRing; ++ii) {
+      const int i = i0 + ii;
+      if (i >= nch) break;
+      if (512 * i + 8 * lane < a.H) acc = dot_chunk(xv[ii], wv[ii], acc);
+      const int ni = i + kSmallRing;
+      if (ni < nch && 512 * ni + 8 * lane < a.H) {
+        wv[ii] = *reinterpret_cast<const uint4*>(wrow + 512 * ni);
+        xv[ii] = *reinterpret_cast<const uint4*>(xrow + 512 * ni);
+      }
+    }
+  }
+  const double sum = wave_sum_f64(acc);
+  if (lane == 0) a.logits[(size_t)r * a.E + e] = sum;
+}
+
+// One workgroup: top-k of every row (wave per row), then the union and the
+// row lists built in LDS, one thread per expert.
+__global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a) {
+  __shared__ uint32_t sbits[kDecodeMaxRows][8];
+  __shared__ int tmp[16];
+  const int lane = threadIdx.x & 63;
+  const int r = threadIdx.x >> 6;
+  if (r < a.M) select_row(a, r, lane, &sbits[r][0]);
+  __syncthreads();
+  const int t = threadIdx.x;
+  int cnt = 0;
+  if (t < a.E)
+    for (int q = 0; q < a.M; ++q) cnt += (sbits[q][t >> 5] >> (t & 31)) & 1u;
+  int nu, total, total_mt;
+  const int off = block_excl_scan(cnt, tmp, &total);
+  const int uidx = block_excl_scan(cnt > 0 ? 1 : 0, tmp, &nu);
+  const int mto = block_excl_scan((cnt + kMTile - 1) / kMTile, tmp, &total_mt);
+  if (cnt > 0) {
+    a.union_ids[uidx] = t;
+    a.offs[uidx] = off;
+    a.mtile_offs[uidx] = mto;
+    int i = 0;
+    const uint32_t below = (1u << (t & 31)) - 1u;
+    for (int q = 0; q < a.M; ++q) {
+      if (!((sbits[q][t >> 5] >> (t & 31)) & 1u)) continue;
+      int j = __popc(sbits[q][t >> 5] & below);
+      for (int w2 = 0; w2 < (t >> 5); ++w2) j += __popc(sbits[q][w2]);
+      a.rows[off + i] = q;
+      a.slot_of[(size_t)q * a.K + j] = off + i;
+      ++i;
+    }
+  }
+  if (t == 0) {
+    a.offs[nu] = total;
+    a.mtile_offs[nu] = total_mt;
+    *a.n_union = nu;
+    a.sched[SCHED_NUNION] = nu;
+    a.sched[SCHED_MTILES] = total_mt;
+    a.sched[SCHED_SLOTS] = total;
+    a.sched[SCHED_BAD] = 0;
+  }
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const dim3 blk(256);
   if (a.M <= kDecodeMaxRows) {
-    MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<1>, dim3((a.M + 7) / 8, (a.E + 3) / 4), blk, 0, s, a);
-  } else {
-    MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((a.M + 7) / 8, (a.E + 15) / 16), blk, 0, s, a);
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * a.M), 0, s, a);
+    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(1024), 0, s, a);
+    return hipSuccess;
   }
+  MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((a.M + 7) / 8, (a.E + 15) / 16), blk, 0, s, a);
   MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union, dim3(1), dim3(1024), 0, s, a);
   return hipSuccess;
