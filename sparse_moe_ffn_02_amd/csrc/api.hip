@@ -2,6 +2,7 @@
 // launch sequence of each entry point.  Nothing here allocates, frees or
 // synchronizes; every check happens before the first launch.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include "moe_ffn.h"
@@ -16,7 +17,8 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t sched, mtile, logits, rowbits, xq, xs, hbuf, hq, hs, hsh, S, D, total;
+  size_t sched, mtile, logits, sig, rowbits, xq, xs, hbuf, hq, hs, hsh, S, D, part_gu, part_sh, part_d, part_s, total;
+  bool split;
 };
 
 Layout make_layout(const moe_dims& d, int M) {
@@ -31,6 +33,7 @@ Layout make_layout(const moe_dims& d, int M) {
   L.sched = take(SCHED_WORDS * sizeof(int32_t));
   L.mtile = take((E + 1) * sizeof(int32_t));
   L.logits = take(m * E * sizeof(double));
+  L.sig = take(m * E * sizeof(double));
   L.rowbits = take(m * ((E + 31) / 32) * sizeof(uint32_t));
   L.xq = take(m * H);
   L.xs = take(m * (H / 128) * sizeof(float));
@@ -40,6 +43,12 @@ Layout make_layout(const moe_dims& d, int M) {
   L.hsh = take(m * Is * sizeof(uint16_t));
   L.S = take(m * H * sizeof(float));
   L.D = take(m * K * H * sizeof(float));
+  L.split = use_split(M, d.hidden);
+  const size_t sp = L.split ? 1 : 0;
+  L.part_gu = take(sp * kSegGU * m * K * 2 * I * sizeof(float));
+  L.part_sh = take(sp * kSegSG * m * 2 * Is * sizeof(float));
+  L.part_d = take(sp * kSegDN * m * K * H * sizeof(float));
+  L.part_s = take(sp * kSegDN * m * H * sizeof(float));
   L.total = off;
   return L;
 }
@@ -104,6 +113,7 @@ RouteArgs route_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t*
   a.K = d.top_k;
   a.scale = d.routed_scale;
   a.logits = reinterpret_cast<double*>(ws + L.logits);
+  a.sig = reinterpret_cast<double*>(ws + L.sig);
   a.rowbits = reinterpret_cast<uint32_t*>(ws + L.rowbits);
   a.ids = out.topk_ids;
   a.w = out.topk_w;
@@ -158,6 +168,11 @@ FfnArgs ffn_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t* mas
   a.hsh = reinterpret_cast<uint16_t*>(ws + L.hsh);
   a.S = reinterpret_cast<float*>(ws + L.S);
   a.D = reinterpret_cast<float*>(ws + L.D);
+  a.split = L.split ? 1 : 0;
+  a.part_gu = reinterpret_cast<float*>(ws + L.part_gu);
+  a.part_sh = reinterpret_cast<float*>(ws + L.part_sh);
+  a.part_d = reinterpret_cast<float*>(ws + L.part_d);
+  a.part_s = reinterpret_cast<float*>(ws + L.part_s);
   a.y = y;
   return a;
 }
@@ -172,7 +187,7 @@ Tracer g_trace;
 
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
-    "down_combine_decode", "down", "combine", "quant", "route_small",
+    "down_combine_decode", "down", "combine", "quant", "select_union", "front",
 };
 
 }  // namespace
@@ -216,7 +231,12 @@ const char* moe_kernel_name(int32_t kernel_id) {
 
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_rows) {
   if (check_dims(dims) != MOE_OK || check_rows(max_rows) != MOE_OK) return 0;
-  return make_layout(*dims, max_rows).total;
+  // small steps keep per-segment partials, so the largest layout for M <=
+  // max_rows is either at max_rows or at the largest split row count
+  size_t need = make_layout(*dims, max_rows).total;
+  const int split_m = max_rows < kSmallRows ? max_rows : kSmallRows;
+  need = std::max(need, make_layout(*dims, split_m).total);
+  return need;
 }
 
 int moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
@@ -233,15 +253,6 @@ int moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
   char* w = static_cast<char*>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const RouteArgs a = route_args(*dims, M, x, row_mask, *router, *out, w, L);
-  FfnArgs p;
-  memset(&p, 0, sizeof(p));
-  p.M = M;
-  p.H = dims->hidden;
-  p.x = x;
-  p.mask = row_mask;
-  p.xq = reinterpret_cast<uint8_t*>(w + L.xq);
-  p.xs = reinterpret_cast<float*>(w + L.xs);
-  if ((st = to_status(launch_prep(p, s))) != MOE_OK) return st;
   return to_status(launch_route(a, s));
 }
 
@@ -289,8 +300,14 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const RouteArgs ra = route_args(*dims, M, x, row_mask, *router, *out, w, L);
   const FfnArgs a = ffn_args(*dims, M, x, row_mask, *out, *experts, shared, y, taps, w, L);
-  if ((st = to_status(launch_prep(a, s))) != MOE_OK) return st;
-  if ((st = to_status(launch_route(ra, s))) != MOE_OK) return st;
+  if (a.split) {
+    // one front launch computes the logits, quantizes x and streams the
+    // shared expert's gate/up while the router runs
+    if ((st = to_status(launch_front_split(ra, a, s))) != MOE_OK) return st;
+  } else {
+    if ((st = to_status(launch_prep(a, s))) != MOE_OK) return st;
+    if ((st = to_status(launch_route(ra, s))) != MOE_OK) return st;
+  }
   return to_status(launch_ffn(a, s));
 }
 

@@ -11,66 +11,29 @@
 // (openinfer PR #610, description and "Gates").
 //
 // One procedure per output element, shared by every kernel here:
-//   routed GEMM  out[s, n] = chain over K-blocks kb ascending of
-//                acc = fma(s_act[s, kb] * s_w[n/128, kb], P_kb, acc), acc0 = 0,
-//                P_kb = one 16x16x128 fp8 MFMA with a zero accumulator;
-//   shared GEMM  one bf16 16x16x32 MFMA chain over K ascending from zero;
+//   routed GEMM  K-blocks split into fixed contiguous segments (kSegGU for
+//                gate/up, kSegDN for down); per segment acc = 0 and, for
+//                K-blocks kb ascending, acc = fma(s_act[kb] * s_w[kb], P_kb,
+//                acc) with P_kb one 16x16x128 fp8 MFMA from a zero
+//                accumulator; the element is ((seg0 + seg1) + seg2) + ...;
+//   shared GEMM  fixed K segments (kSegSG for gate/up, kSegDN for down),
+//                each a bf16 16x16x32 MFMA chain from zero, summed in order;
 //   combine      acc = fma(w_j, D[slot(r, j)], acc) for j ascending, then
 //                + S[r] when the shared expert is present, then bf16 RNE.
-// Which tile, wave or kernel computes an element never changes its bits.
+// Which tile, wave or kernel computes an element never changes its bits
+// (the MFMA result does not depend on the row or column an element occupies).
 #include <algorithm>
 
-#include "moe_device.h"
-#include "moe_internal.h"
+#include "moe_chains.h"
 
 namespace moe {
 
-
-__device__ __forceinline__ v8i load32(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  return r;
-}
-
-__device__ __forceinline__ v4i load16(const uint16_t* p) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  v4i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-  return r;
-}
-
-__device__ __forceinline__ bool row_real(const uint8_t* mask, int r) { return mask == nullptr || mask[r] != 0; }
-
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, const v4f& v) {
-  const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
-}
-
-// ---------------------------------------------------------------- quantization
-// One wave per (row, 128-column block): amax, s = fl32(amax/448) (1 for a
-// zero block), code = e4m3_rne_sat(fl32(v/s)); zero blocks give zero codes.
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p);
 template <>
 __device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
-
-template <typename T>
-__device__ __forceinline__ void quant_block(const T* in, uint8_t* codes, float* scale, int lane) {
-  const float v0 = load_as_f32<T>(in + 2 * lane);
-  const float v1 = load_as_f32<T>(in + 2 * lane + 1);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float s = quant_scale(amax);
-  uint32_t c0 = 0, c1 = 0;
-  if (amax != 0.0f) {
-    c0 = quant_code(v0, s);
-    c1 = quant_code(v1, s);
-  }
-  *reinterpret_cast<uint16_t*>(codes + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) *scale = s;
-}
 
 // rows [0, R) of a [R, C] matrix; rows with mask 0 are skipped (never read).
 template <typename T>
@@ -82,31 +45,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* in, const uint8_t* 
   const int r = (int)(item / nb);
   const int b = (int)(item % nb);
   if (r >= R || !row_real(mask, r)) return;
-  quant_block<T>(in + (size_t)r * C + b * kBlk, codes + (size_t)r * C + b * kBlk, scales + (size_t)r * nb + b, lane);
-}
-
-// First kernel of every call: quantize x (real rows).
-__global__ __launch_bounds__(256) void k_prep(const uint16_t* x, const uint8_t* mask, int M, int H, uint8_t* xq,
-                                              float* xs) {
-  const int lane = threadIdx.x & 63;
-  const int nb = H / kBlk;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int r = (int)(item / nb);
-  const int b = (int)(item % nb);
-  if (r >= M || !row_real(mask, r)) return;
-  quant_block<uint16_t>(x + (size_t)r * H + b * kBlk, xq + (size_t)r * H + b * kBlk, xs + (size_t)r * nb + b, lane);
-}
-
-// After gate/up: requantize routed h per (slot, block) for the slots in use.
-__global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nbI = a.I / kBlk;
-  const int slot = (int)(item / nbI);
-  const int b = (int)(item % nbI);
-  if (slot >= a.sched[SCHED_SLOTS]) return;
-  quant_block<float>(a.hbuf + (size_t)slot * a.I + b * kBlk, a.hq + (size_t)slot * a.I + b * kBlk,
-                     a.hs + (size_t)slot * nbI + b, lane);
+  const T* p = in + (size_t)r * C + b * kBlk + 2 * lane;
+  quant_pair(load_as_f32<T>(p), load_as_f32<T>(p + 1), codes + (size_t)r * C + b * kBlk, scales + (size_t)r * nb + b,
+             lane);
 }
 
 // ---------------------------------------------------------------- plan
@@ -172,13 +113,19 @@ __device__ __forceinline__ Tile routed_tile(const FfnArgs& a, int mtg) {
 // count exit at once, and the hardware dispatcher balances the rest.
 __device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + (threadIdx.x >> 6); }
 
-constexpr int kRing = 4;      // fp8 K-blocks in flight per wave
-constexpr int kRingBf = 8;    // bf16 K-steps (32 deep) in flight per wave
+// Gate/up tiles: the 16 MFMA A rows are gate rows n0..n0+7 (rows 0-7) and
+// up rows n0..n0+7 (rows 8-15), so lane l (l < 32) holds gate values and
+// lane l + 32 the up values of the same (column, n); n = n0 + 4 (kq & 1) + i.
+__device__ __forceinline__ const uint8_t* gu_row(const FfnArgs& a, int e, int n0, int c, int kq) {
+  return (c < 8 ? a.wg : a.wu) + ((size_t)e * a.I + n0 + (c & 7)) * a.H + kq * 32;
+}
+__device__ __forceinline__ const float* gu_scale(const FfnArgs& a, int e, int n0, int kq) {
+  return (kq < 2 ? a.sg : a.su) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * (a.H / kBlk);
+}
 
-// Routed gate+up for 8 columns of I and one tile of <= 16 slots.  The 16
-// rows of the MFMA A operand are gate rows n0..n0+7 (rows 0-7) and up rows
-// n0..n0+7 (rows 8-15), so lane l (l < 32) holds G and lane l + 32 holds U of
-// the same (slot, n).  Writes h = silu(G) * U (fp32) for the tile's slots.
+// ---------------------------------------------------------------- gate/up (any M)
+// Routed: 8 columns of I for one tile of <= 16 slots, all segments in-wave;
+// writes h = silu(G) * U (fp32) for the tile's slots.
 __device__ void routed_gateup(const FfnArgs& a, const Tile& t, int nt, int lane) {
   const int c = lane & 15, kq = lane >> 4;
   const int n0 = nt * 8;
@@ -190,54 +137,17 @@ __device__ void routed_gateup(const FfnArgs& a, const Tile& t, int nt, int lane)
   }
   const uint8_t* bp = a.xq + (size_t)(row < 0 ? 0 : row) * a.H + kq * 32;
   const float* sxp = a.xs + (size_t)(row < 0 ? 0 : row) * nkb;
-  const uint8_t* wp = (c < 8 ? a.wg : a.wu) + ((size_t)t.e * a.I + n0 + (c & 7)) * a.H + kq * 32;
-  const float* swp = (kq < 2 ? a.sg : a.su) + ((size_t)t.e * (a.I / kBlk) + n0 / kBlk) * nkb;
-  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  v8i wb[kRing], xb[kRing];
-  float sxb[kRing], swb[kRing];
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) {
-    if (i < nkb) {
-      wb[i] = load32(wp + i * kBlk);
-      xb[i] = row >= 0 ? load32(bp + i * kBlk) : zero8;
-      sxb[i] = row >= 0 ? sxp[i] : 0.0f;
-      swb[i] = swp[i];
-    }
-  }
-  for (int kb0 = 0; kb0 < nkb; kb0 += kRing) {
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int kb = kb0 + i;
-      if (kb >= nkb) break;
-      const v4f p = mfma_fp8_k128(wb[i], xb[i]);
-      scale_acc(acc, p, sxb[i], swb[i]);
-      const int nk = kb + kRing;
-      if (nk < nkb) {
-        wb[i] = load32(wp + nk * kBlk);
-        if (row >= 0) {
-          xb[i] = load32(bp + nk * kBlk);
-          sxb[i] = sxp[nk];
-        }
-        swb[i] = swp[nk];
-      }
-    }
-  }
+  const v4f acc = fp8_full<false>(gu_row(a, t.e, n0, c, kq), gu_scale(a, t.e, n0, kq), bp, sxp, row >= 0, nkb, kSegGU);
   float u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[i], 32, 64);
   if (kq < 2 && row >= 0) {
-    float4 h;
-    h.x = silu_mul(acc[0], u[0]);
-    h.y = silu_mul(acc[1], u[1]);
-    h.z = silu_mul(acc[2], u[2]);
-    h.w = silu_mul(acc[3], u[3]);
-    *reinterpret_cast<float4*>(a.hbuf + (size_t)(t.s0 + c) * a.I + n0 + kq * 4) = h;
+    const v4f h = {silu_mul(acc[0], u[0]), silu_mul(acc[1], u[1]), silu_mul(acc[2], u[2]), silu_mul(acc[3], u[3])};
+    store_f4(a.hbuf + (size_t)(t.s0 + c) * a.I + n0 + kq * 4, h);
   }
 }
 
-// Shared gate+up for 8 columns of I_s and 16 rows, arranged as above (gate
-// rows 0-7, up rows 8-15); writes h_s = bf16(silu(g) * u).
+// Shared: 8 columns of I_s for 16 rows, all segments in-wave; h_s = bf16(silu(g) u).
 __device__ void shared_gateup(const FfnArgs& a, int mt, int nt, int lane) {
   const int c = lane & 15, kq = lane >> 4;
   const int n0 = nt * 8;
@@ -245,30 +155,7 @@ __device__ void shared_gateup(const FfnArgs& a, int mt, int nt, int lane) {
   const bool valid = row < a.M && row_real(a.mask, row);
   const uint16_t* wp = (c < 8 ? a.wsg : a.wsu) + (size_t)(n0 + (c & 7)) * a.H + kq * 8;
   const uint16_t* bp = a.x + (size_t)(valid ? row : 0) * a.H + kq * 8;
-  const v4i zero4 = {0, 0, 0, 0};
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  const int ns = a.H / 32;
-  v4i wb[kRingBf], xb[kRingBf];
-#pragma unroll
-  for (int i = 0; i < kRingBf; ++i) {
-    if (i < ns) {
-      wb[i] = load16(wp + i * 32);
-      xb[i] = valid ? load16(bp + i * 32) : zero4;
-    }
-  }
-  for (int s0 = 0; s0 < ns; s0 += kRingBf) {
-#pragma unroll
-    for (int i = 0; i < kRingBf; ++i) {
-      const int st = s0 + i;
-      if (st >= ns) break;
-      acc = mfma_bf16_k32(wb[i], xb[i], acc);
-      const int nx = st + kRingBf;
-      if (nx < ns) {
-        wb[i] = load16(wp + nx * 32);
-        if (valid) xb[i] = load16(bp + nx * 32);
-      }
-    }
-  }
+  const v4f acc = bf16_full(wp, bp, valid, a.H / 32, kSegSG);
   float u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[i], 32, 64);
@@ -278,7 +165,6 @@ __device__ void shared_gateup(const FfnArgs& a, int mt, int nt, int lane) {
   }
 }
 
-// Shared items first (the longest), then routed items.
 __global__ __launch_bounds__(256, 2) void k_gateup(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const int ntI = a.I / 8;
@@ -295,109 +181,153 @@ __global__ __launch_bounds__(256, 2) void k_gateup(FfnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- gate/up (split small steps)
+// M <= kSmallRows: the workgroup keeps every row's x codes and scales in LDS
+// (rows padded by 16 bytes against bank conflicts) and the MFMA columns are
+// the step's rows (column c is row c; rows not routed to the item's expert
+// are computed and dropped).  Each item is one K segment of one 8-column
+// tile; it writes fp32 partials, reduced in segment order by k_post_gateup.
+constexpr int kLdsPad = 16;
+
+__global__ __launch_bounds__(512) void k_gateup_split(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int nkb = a.H / kBlk;
+  const int ldx = a.H + kLdsPad;
+  uint8_t* lx = smem;
+  float* lsx = reinterpret_cast<float*>(smem + (size_t)a.M * ldx);
+  const int ntI = a.I / 8;
+  const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU;
+  const int t0 = blockIdx.x * 8;
+  if (t0 >= n_items) return;                    // workgroup beyond the union: nothing to stage
+  {
+    const int per_row = a.H / 16;
+    for (int i = threadIdx.x; i < a.M * per_row; i += blockDim.x) {
+      const int r = i / per_row, j = i % per_row;
+      const uint4 v = row_real(a.mask, r) ? *reinterpret_cast<const uint4*>(a.xq + (size_t)r * a.H + j * 16)
+                                          : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(lx + (size_t)r * ldx + j * 16) = v;
+    }
+    for (int i = threadIdx.x; i < a.M * nkb; i += blockDim.x)
+      lsx[i] = row_real(a.mask, i / nkb) ? a.xs[i] : 0.0f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, kq = lane >> 4;
+  const int t = t0 + (threadIdx.x >> 6);
+  if (t >= n_items) return;
+  const int seg = t % kSegGU;
+  const int item = t / kSegGU;
+  const int u = item / ntI, nt = item % ntI;
+  const int n0 = nt * 8;
+  const int e = a.union_ids[u];
+  const bool col = c < a.M;
+  const v4f p = fp8_chain<true>(gu_row(a, e, n0, c, kq), gu_scale(a, e, n0, kq), lx + (size_t)(col ? c : 0) * ldx + kq * 32,
+                                lsx + (col ? c : 0) * nkb, col, seg_begin(nkb, seg, kSegGU),
+                                seg_begin(nkb, seg + 1, kSegGU));
+  if (!col) return;
+  // slot of (row c, expert e): the expert's rows are listed ascending
+  const int lo = a.offs[u], hi = a.offs[u + 1];
+  int slot = -1;
+  for (int s = lo; s < hi; ++s)
+    if (a.rows[s] == c) slot = s;
+  if (slot >= 0)
+    store_f4(a.part_gu + (((size_t)seg * a.M * a.K + slot) * 2 + (kq >> 1)) * a.I + n0 + (kq & 1) * 4, p);
+}
+
+// ---------------------------------------------------------------- requantization
+// Routed h per (slot, 128-column block) for the slots in use.  Split steps
+// first sum the gate/up segment partials in order and form h = silu(G) U;
+// larger steps read h from hbuf.
+__global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nbI = a.I / kBlk;
+  const int slot = (int)(item / nbI);
+  const int b = (int)(item % nbI);
+  if (slot >= a.sched[SCHED_SLOTS]) return;
+  const int n = b * kBlk + 2 * lane;
+  float h0, h1;
+  if (a.split) {
+    const size_t st = (size_t)a.M * a.K * 2 * a.I;          // segment stride
+    const float* pg = a.part_gu + ((size_t)slot * 2 + 0) * a.I + n;
+    const float* pu = a.part_gu + ((size_t)slot * 2 + 1) * a.I + n;
+    float2 g = *reinterpret_cast<const float2*>(pg);
+    float2 u = *reinterpret_cast<const float2*>(pu);
+    for (int s = 1; s < kSegGU; ++s) {
+      const float2 gs = *reinterpret_cast<const float2*>(pg + s * st);
+      const float2 us = *reinterpret_cast<const float2*>(pu + s * st);
+      g.x = g.x + gs.x; g.y = g.y + gs.y;
+      u.x = u.x + us.x; u.y = u.y + us.y;
+    }
+    h0 = silu_mul(g.x, u.x);
+    h1 = silu_mul(g.y, u.y);
+  } else {
+    const float2 h = *reinterpret_cast<const float2*>(a.hbuf + (size_t)slot * a.I + n);
+    h0 = h.x;
+    h1 = h.y;
+  }
+  quant_pair(h0, h1, a.hq + (size_t)slot * a.I + b * kBlk, a.hs + (size_t)slot * nbI + b, lane);
+}
+
 // ---------------------------------------------------------------- down
-// D[slot, n] for 16 columns of H and one tile of <= 16 slots.
-__device__ __forceinline__ v4f routed_down_chain(const FfnArgs& a, int e, int slot, int n0, int lane) {
-  const int c = lane & 15, kq = lane >> 4;
-  const int nkb = a.I / kBlk;
-  const uint8_t* wp = a.wd + ((size_t)e * a.H + n0 + c) * a.I + kq * 32;
-  const uint8_t* bp = a.hq + (size_t)(slot < 0 ? 0 : slot) * a.I + kq * 32;
-  const float* shp = a.hs + (size_t)(slot < 0 ? 0 : slot) * nkb;
-  const float* swp = a.sd + ((size_t)e * (a.H / kBlk) + n0 / kBlk) * nkb;
-  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  v8i wb[kRing], hb[kRing];
-  float shb[kRing], swb[kRing];
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) {
-    if (i < nkb) {
-      wb[i] = load32(wp + i * kBlk);
-      hb[i] = slot >= 0 ? load32(bp + i * kBlk) : zero8;
-      shb[i] = slot >= 0 ? shp[i] : 0.0f;
-      swb[i] = swp[i];
-    }
-  }
-  for (int kb0 = 0; kb0 < nkb; kb0 += kRing) {
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int kb = kb0 + i;
-      if (kb >= nkb) break;
-      const v4f p = mfma_fp8_k128(wb[i], hb[i]);
-      scale_acc(acc, p, shb[i], swb[i]);
-      const int nk = kb + kRing;
-      if (nk < nkb) {
-        wb[i] = load32(wp + nk * kBlk);
-        if (slot >= 0) {
-          hb[i] = load32(bp + nk * kBlk);
-          shb[i] = shp[nk];
-        }
-        swb[i] = swp[nk];
-      }
-    }
-  }
-  return acc;
-}
-
-__device__ __forceinline__ v4f shared_down_chain(const FfnArgs& a, int row_or_neg, int n0, int lane) {
-  const int c = lane & 15, kq = lane >> 4;
-  const uint16_t* wp = a.wsd + (size_t)(n0 + c) * a.Is + kq * 8;
-  const uint16_t* bp = a.hsh + (size_t)(row_or_neg < 0 ? 0 : row_or_neg) * a.Is + kq * 8;
-  const v4i zero4 = {0, 0, 0, 0};
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  const int ns = a.Is / 32;
-  v4i wb[kRingBf], hb[kRingBf];
-#pragma unroll
-  for (int i = 0; i < kRingBf; ++i) {
-    if (i < ns) {
-      wb[i] = load16(wp + i * 32);
-      hb[i] = row_or_neg >= 0 ? load16(bp + i * 32) : zero4;
-    }
-  }
-  for (int st0 = 0; st0 < ns; st0 += kRingBf) {
-#pragma unroll
-    for (int i = 0; i < kRingBf; ++i) {
-      const int st = st0 + i;
-      if (st >= ns) break;
-      acc = mfma_bf16_k32(wb[i], hb[i], acc);
-      const int nx = st + kRingBf;
-      if (nx < ns) {
-        wb[i] = load16(wp + nx * 32);
-        if (row_or_neg >= 0) hb[i] = load16(bp + nx * 32);
-      }
-    }
-  }
-  return acc;
-}
-
-// Shared-down items first, then routed down items.
+// D[slot, n] (routed) and S[r, n] (shared) for 16 columns of H and one tile
+// of <= 16 slots / rows.  Split steps run one K segment per item and write
+// partials; larger steps run all segments in-wave.
 __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
   const int ntH = a.H / 16;
-  const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntH : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntH;
+  const int nseg = a.split ? kSegDN : 1;
+  const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntH * nseg : 0;
+  const int total = n_sh + a.sched[SCHED_MTILES] * ntH * nseg;
   const int t = wave_item();
-  if (t < total) {
-    if (t < n_sh) {
-      const int mt = t / ntH, nt = t % ntH;
-      const int row = mt * kMTile + c;
-      const bool valid = row < a.M && row_real(a.mask, row);
-      const v4f r = shared_down_chain(a, valid ? row : -1, nt * 16, lane);
-      if (valid)
-        *reinterpret_cast<float4*>(a.S + (size_t)row * a.H + nt * 16 + kq * 4) = make_float4(r[0], r[1], r[2], r[3]);
+  if (t >= total) return;
+  if (t < n_sh) {
+    const int seg = t % nseg, tt = t / nseg;
+    const int mt = tt / ntH, nt = tt % ntH;
+    const int row = mt * kMTile + c;
+    const bool valid = row < a.M && row_real(a.mask, row);
+    const uint16_t* wp = a.wsd + (size_t)(nt * 16 + c) * a.Is + kq * 8;
+    const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
+    const int nst = a.Is / 32;
+    if (a.split) {
+      const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
+      if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * 16 + kq * 4, p);
     } else {
-      const int tt = t - n_sh;
-      const Tile tl = routed_tile(a, tt / ntH);
-      const int nt = tt % ntH;
-      const int slot = c < tl.mcnt ? tl.s0 + c : -1;
-      const v4f r = routed_down_chain(a, tl.e, slot, nt * 16, lane);
-      if (slot >= 0)
-        *reinterpret_cast<float4*>(a.D + (size_t)slot * a.H + nt * 16 + kq * 4) = make_float4(r[0], r[1], r[2], r[3]);
+      const v4f s = bf16_full(wp, bp, valid, nst, kSegDN);
+      if (valid) store_f4(a.S + (size_t)row * a.H + nt * 16 + kq * 4, s);
     }
+    return;
+  }
+  const int tt = t - n_sh;
+  const int seg = tt % nseg, it = tt / nseg;
+  const Tile tl = routed_tile(a, it / ntH);
+  const int nt = it % ntH;
+  const int slot = c < tl.mcnt ? tl.s0 + c : -1;
+  const int nkb = a.I / kBlk;
+  const uint8_t* wp = a.wd + ((size_t)tl.e * a.H + nt * 16 + c) * a.I + kq * 32;
+  const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * 16) / kBlk) * nkb;
+  const uint8_t* bp = a.hq + (size_t)(slot < 0 ? 0 : slot) * a.I + kq * 32;
+  const float* shp = a.hs + (size_t)(slot < 0 ? 0 : slot) * nkb;
+  if (a.split) {
+    const v4f p = fp8_chain<false>(wp, swp, bp, shp, slot >= 0, seg_begin(nkb, seg, kSegDN),
+                                   seg_begin(nkb, seg + 1, kSegDN));
+    if (slot >= 0) store_f4(a.part_d + ((size_t)seg * a.M * a.K + slot) * a.H + nt * 16 + kq * 4, p);
+  } else {
+    const v4f d = fp8_full<false>(wp, swp, bp, shp, slot >= 0, nkb, kSegDN);
+    if (slot >= 0) store_f4(a.D + (size_t)slot * a.H + nt * 16 + kq * 4, d);
   }
 }
 
+// ---------------------------------------------------------------- combine
 // y[r, n] = bf16( chain_j fma(w_j, D[slot_of[r, j], n]) (+ S[r, n]) ); pads 0.
+// Split steps first sum the down partials of each slot (and of S) in order.
+__device__ __forceinline__ v4f load_f4(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  v4f r = {v.x, v.y, v.z, v.w};
+  return r;
+}
+
 __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int q = a.H / 4;
@@ -415,18 +345,29 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
     const int s = a.slot_of[(size_t)r * a.K + j];
     if (s < 0 || s >= slots) continue;
     const float wj = a.w[(size_t)r * a.K + j];
-    const float4 d = *reinterpret_cast<const float4*>(a.D + (size_t)s * a.H + n);
-    acc[0] = __builtin_fmaf(wj, d.x, acc[0]);
-    acc[1] = __builtin_fmaf(wj, d.y, acc[1]);
-    acc[2] = __builtin_fmaf(wj, d.z, acc[2]);
-    acc[3] = __builtin_fmaf(wj, d.w, acc[3]);
+    v4f d;
+    if (a.split) {
+      const size_t st = (size_t)a.M * a.K * a.H;
+      d = load_f4(a.part_d + (size_t)s * a.H + n);
+      for (int g = 1; g < kSegDN; ++g) d = add4(d, load_f4(a.part_d + g * st + (size_t)s * a.H + n));
+    } else {
+      d = load_f4(a.D + (size_t)s * a.H + n);
+    }
+    acc[0] = __builtin_fmaf(wj, d[0], acc[0]);
+    acc[1] = __builtin_fmaf(wj, d[1], acc[1]);
+    acc[2] = __builtin_fmaf(wj, d[2], acc[2]);
+    acc[3] = __builtin_fmaf(wj, d[3], acc[3]);
   }
   if (with_shared) {
-    const float4 sv = *reinterpret_cast<const float4*>(a.S + (size_t)r * a.H + n);
-    acc[0] = acc[0] + sv.x;
-    acc[1] = acc[1] + sv.y;
-    acc[2] = acc[2] + sv.z;
-    acc[3] = acc[3] + sv.w;
+    v4f sv;
+    if (a.split) {
+      const size_t st = (size_t)a.M * a.H;
+      sv = load_f4(a.part_s + (size_t)r * a.H + n);
+      for (int g = 1; g < kSegDN; ++g) sv = add4(sv, load_f4(a.part_s + g * st + (size_t)r * a.H + n));
+    } else {
+      sv = load_f4(a.S + (size_t)r * a.H + n);
+    }
+    acc = add4(acc, sv);
   }
   store_bf16x4(yp, acc);
 }
@@ -440,8 +381,8 @@ hipError_t launch_plan(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_prep(const FfnArgs& a, hipStream_t s) {
   const long waves = (long)a.M * (a.H / kBlk);
-  MOE_LAUNCH(KID_QUANT_X, k_prep, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a.x, a.mask, a.M, a.H, a.xq,
-             a.xs);
+  MOE_LAUNCH(KID_QUANT_X, k_quant_rows<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a.x, a.mask,
+             a.M, a.H, a.xq, a.xs);
   return hipSuccess;
 }
 
@@ -459,16 +400,31 @@ hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8
   return hipSuccess;
 }
 
+size_t split_lds_bytes(int M, int H) {
+  return (size_t)M * (H + kLdsPad) + (size_t)M * (H / kBlk) * sizeof(float);
+}
+
+bool use_split(int M, int H) { return M <= kSmallRows && split_lds_bytes(M, H) <= 65536; }
+
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const int with_shared = a.Is > 0 ? 1 : 0;
-  // column tiles of <= 16 slots: at most ceil(M*K/16) + (union size) of them
-  const long mtiles_max = ((long)a.M * a.K + kMTile - 1) / kMTile + std::min<long>(a.E, (long)a.M * a.K);
+  // column tiles of <= 16 slots: one per expert for M <= 16, else at most
+  // ceil(M*K/16) + (union size)
+  const long max_union = std::min<long>(a.E, (long)a.M * a.K);
+  const long mtiles_max = a.M <= kMTile ? max_union : ((long)a.M * a.K + kMTile - 1) / kMTile + max_union;
   const long sh_tiles = with_shared ? (a.M + kMTile - 1) / kMTile : 0;
-  const long gu_items = sh_tiles * (a.Is / 8) + mtiles_max * (a.I / 8);
-  MOE_LAUNCH(KID_GATEUP, k_gateup, dim3((unsigned)((gu_items + 3) / 4)), dim3(256), 0, s, a);
+  if (a.split) {
+    // the shared expert's gate/up ran in the front launch
+    const long items = max_union * (a.I / 8) * kSegGU;
+    MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)((items + 7) / 8)), dim3(512), split_lds_bytes(a.M, a.H), s,
+               a);
+  } else {
+    const long gu_items = sh_tiles * (a.Is / 8) + mtiles_max * (a.I / 8);
+    MOE_LAUNCH(KID_GATEUP, k_gateup, dim3((unsigned)((gu_items + 3) / 4)), dim3(256), 0, s, a);
+  }
   const long post_waves = (long)a.M * a.K * (a.I / kBlk);
   MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)((post_waves + 3) / 4)), dim3(256), 0, s, a);
-  const long dn_items = (sh_tiles + mtiles_max) * (a.H / 16);
+  const long dn_items = (sh_tiles + mtiles_max) * (a.H / 16) * (a.split ? kSegDN : 1);
   MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)((dn_items + 3) / 4)), dim3(256), 0, s, a);
   const long threads = (long)a.M * (a.H / 4);
   MOE_LAUNCH(KID_COMBINE, k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, with_shared);

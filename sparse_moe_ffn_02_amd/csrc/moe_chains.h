@@ -1,0 +1,162 @@
+// Device building blocks shared by the routing and expert kernels: vector
+// loads, stores, the 1x128 quantization of a 128-value block held by one
+// wave, and the fp8 / bf16 MFMA chains that define every GEMM element.
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ v8i load32(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  return r;
+}
+
+__device__ __forceinline__ v4i load16(const uint16_t* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  v4i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  return r;
+}
+
+__device__ __forceinline__ bool row_real(const uint8_t* mask, int r) { return mask == nullptr || mask[r] != 0; }
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, const v4f& v) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ void store_f4(float* p, const v4f& v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ v4f add4(const v4f& a, const v4f& b) {
+  v4f r = {a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+  return r;
+}
+
+// first K-block (or K-step) of segment s when n blocks are split into S
+__device__ __forceinline__ int seg_begin(int n, int s, int S) { return (n * s) / S; }
+
+// ---------------------------------------------------------------- quantization
+// One wave per (row, 128-column block): amax, s = fl32(amax/448) (1 for a
+// zero block), code = e4m3_rne_sat(fl32(v/s)); zero blocks give zero codes.
+__device__ __forceinline__ void quant_pair(float v0, float v1, uint8_t* codes, float* scale, int lane) {
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float s = quant_scale(amax);
+  uint32_t c0 = 0, c1 = 0;
+  if (amax != 0.0f) {
+    c0 = quant_code(v0, s);
+    c1 = quant_code(v1, s);
+  }
+  *reinterpret_cast<uint16_t*>(codes + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  if (lane == 0) *scale = s;
+}
+
+// ---------------------------------------------------------------- GEMM chains
+constexpr int kRing = 4;      // fp8 K-blocks in flight per wave
+constexpr int kRingBf = 8;    // bf16 K-steps (32 deep) in flight per wave
+
+// fp8 chain over K-blocks [kb0, kb1) for one 16x16 tile.  A (weights) rows
+// stream from global memory through a ring; B is read from global memory
+// (ring) or from LDS (kLdsB: a workgroup-resident copy).  Lanes with
+// bvalid == false contribute a zero B column and a zero activation scale.
+template <bool kLdsB>
+__device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, const uint8_t* bp, const float* sxp,
+                                         bool bvalid, int kb0, int kb1) {
+  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v8i wb[kRing], xb[kRing];
+  float swb[kRing], sxb[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    const int kb = kb0 + i;
+    if (kb < kb1) {
+      wb[i] = load32(wp + kb * kBlk);
+      swb[i] = swp[kb];
+      if (!kLdsB) {
+        xb[i] = bvalid ? load32(bp + kb * kBlk) : zero8;
+        sxb[i] = bvalid ? sxp[kb] : 0.0f;
+      }
+    }
+  }
+  for (int k0 = kb0; k0 < kb1; k0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int kb = k0 + i;
+      if (kb >= kb1) break;
+      v8i x;
+      float sx;
+      if (kLdsB) {
+        x = bvalid ? *reinterpret_cast<const v8i*>(bp + kb * kBlk) : zero8;
+        sx = bvalid ? sxp[kb] : 0.0f;
+      } else {
+        x = xb[i];
+        sx = sxb[i];
+      }
+      const v4f p = mfma_fp8_k128(wb[i], x);
+      scale_acc(acc, p, sx, swb[i]);
+      const int nk = kb + kRing;
+      if (nk < kb1) {
+        wb[i] = load32(wp + nk * kBlk);
+        swb[i] = swp[nk];
+        if (!kLdsB && bvalid) {
+          xb[i] = load32(bp + nk * kBlk);
+          sxb[i] = sxp[nk];
+        }
+      }
+    }
+  }
+  return acc;
+}
+
+// bf16 chain over K-steps [s0, s1) (32 deep each) for one 16x16 tile.
+__device__ __forceinline__ v4f bf16_chain(const uint16_t* wp, const uint16_t* bp, bool bvalid, int s0, int s1) {
+  const v4i zero4 = {0, 0, 0, 0};
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4i wb[kRingBf], xb[kRingBf];
+#pragma unroll
+  for (int i = 0; i < kRingBf; ++i) {
+    const int st = s0 + i;
+    if (st < s1) {
+      wb[i] = load16(wp + st * 32);
+      xb[i] = bvalid ? load16(bp + st * 32) : zero4;
+    }
+  }
+  for (int k0 = s0; k0 < s1; k0 += kRingBf) {
+#pragma unroll
+    for (int i = 0; i < kRingBf; ++i) {
+      const int st = k0 + i;
+      if (st >= s1) break;
+      acc = mfma_bf16_k32(wb[i], xb[i], acc);
+      const int nx = st + kRingBf;
+      if (nx < s1) {
+        wb[i] = load16(wp + nx * 32);
+        if (bvalid) xb[i] = load16(bp + nx * 32);
+      }
+    }
+  }
+  return settle_bf16(acc);
+}
+
+// All segments of an fp8 element, in order.
+template <bool kLdsB>
+__device__ __forceinline__ v4f fp8_full(const uint8_t* wp, const float* swp, const uint8_t* bp, const float* sxp,
+                                        bool bvalid, int nkb, int nseg) {
+  v4f tot = fp8_chain<kLdsB>(wp, swp, bp, sxp, bvalid, 0, seg_begin(nkb, 1, nseg));
+  for (int s = 1; s < nseg; ++s)
+    tot = add4(tot, fp8_chain<kLdsB>(wp, swp, bp, sxp, bvalid, seg_begin(nkb, s, nseg), seg_begin(nkb, s + 1, nseg)));
+  return tot;
+}
+
+__device__ __forceinline__ v4f bf16_full(const uint16_t* wp, const uint16_t* bp, bool bvalid, int nst, int nseg) {
+  v4f tot = bf16_chain(wp, bp, bvalid, 0, seg_begin(nst, 1, nseg));
+  for (int s = 1; s < nseg; ++s)
+    tot = add4(tot, bf16_chain(wp, bp, bvalid, seg_begin(nst, s, nseg), seg_begin(nst, s + 1, nseg)));
+  return tot;
+}
+
+}  // namespace moe

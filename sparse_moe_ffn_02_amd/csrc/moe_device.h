@@ -20,18 +20,37 @@ constexpr int kBlk = 128;       // quantization block (1x128 activations, 128x12
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- MFMA
+// The matrix core does not interlock a vector-ALU, LDS or memory read of an
+// MFMA result: such a reader has to issue a fixed number of wait states after
+// the MFMA (12 for the fp8 16x16x128 form, 8 for bf16 16x16x32 on gfx950).
+// The compiler pads this inside a basic block, but it was seen to leave a
+// reader on a branch path 8 instructions behind the MFMA, which then read
+// stale accumulator values.  So every result passes through an explicit wait
+// tied to it (the asm both reads and "writes" the registers, so no reader can
+// move above it), with margin over the required count.
+__device__ __forceinline__ v4f settle_fp8(v4f p) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p));       // 16 wait states
+  return p;
+}
+__device__ __forceinline__ v4f settle_bf16(v4f p) {
+  asm volatile("s_nop 7\n\ts_nop 3" : "+v"(p));       // 12 wait states
+  return p;
+}
+
 // fp8 e4m3 x e4m3 -> fp32, 16x16 output, K = 128, zero initial accumulator.
 // Operand layout (both operands): lane l holds 32 consecutive K values of
 // row/column (l % 16), starting at K = 32 * (l / 16).
 // Output layout: lane l holds C[4 * (l / 16) + i][l % 16], i = 0..3.
+// The result is settled and may be read at once.
 __device__ __forceinline__ v4f mfma_fp8_k128(const v8i& a, const v8i& b) {
   v4f z = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+  return settle_fp8(__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0));
 }
 
 // bf16 x bf16 -> fp32, 16x16 output, K = 32, accumulating into c.
 // Operand layout: lane l holds 8 consecutive K values of row/column (l % 16)
-// starting at K = 8 * (l / 16).  Output layout as above.
+// starting at K = 8 * (l / 16).  Output layout as above.  The result may feed
+// the next call's c directly; pass it through settle_bf16 before any other read.
 __device__ __forceinline__ v4f mfma_bf16_k32(const v4i& a, const v4i& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
                                                  c, 0, 0, 0);
@@ -82,6 +101,15 @@ __device__ __forceinline__ float quant_scale(float amax) {
 // Code of one value under scale s (zero blocks give code 0 via v = 0).
 __device__ __forceinline__ uint32_t quant_code(float v, float s) {
   return f32_to_e4m3(__fdiv_rn(v, s));
+}
+
+// Router score of a float64 logit: sigmoid s = 1 / (1 + exp(-l)) and the
+// selection score c = s + bias (a NaN score becomes -inf, so the selection
+// stays defined).
+__device__ __forceinline__ void route_score(double l, float bias, double& sig, double& c) {
+  sig = 1.0 / (1.0 + exp(-l));
+  const double cc = sig + (double)bias;
+  c = (cc == cc) ? cc : -INFINITY;
 }
 
 // h = silu(g) * u in fp32, silu(g) = g / (1 + exp(-g)).

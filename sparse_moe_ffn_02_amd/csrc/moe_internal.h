@@ -8,7 +8,15 @@
 namespace moe {
 
 constexpr int kMTile = 16;          // slots (or rows) per MFMA column tile
-constexpr int kDecodeMaxRows = 16;  // rows served by the fused small-step router kernel
+constexpr int kDecodeMaxRows = 16;  // rows served by the small-step router kernels
+constexpr int kSmallRows = 8;       // rows served by the split small-step expert kernels
+// Every GEMM element is the fixed-order sum of its K-segment chains:
+// routed gate/up over kSegGU segments of K = H, shared gate/up over kSegSG,
+// routed and shared down over kSegDN segments of K = I.  Small steps run each segment as its own work
+// item and reduce the fp32 partials later; larger steps run them in-wave.
+constexpr int kSegGU = 4;
+constexpr int kSegDN = 2;
+constexpr int kSegSG = 8;           // shared expert gate/up (bf16 steps stream half the bytes per load)
 
 // sched[] words written by the union / plan kernels and read by the FFN kernels
 enum { SCHED_NUNION = 0, SCHED_MTILES = 1, SCHED_SLOTS = 2, SCHED_BAD = 3, SCHED_WORDS = 8 };
@@ -20,7 +28,8 @@ struct RouteArgs {
   const float* bias;       // [E]
   int M, H, E, K;
   float scale;
-  double* logits;          // ws [M, E]
+  double* logits;          // ws [M, E] logits (large steps) or biased scores c (small steps)
+  double* sig;             // ws [M, E] sigmoid of the logits (small steps)
   uint32_t* rowbits;       // ws [M, ceil(E/32)]
   int32_t* ids;            // [M, K]
   float* w;                // [M, K]
@@ -59,13 +68,19 @@ struct FfnArgs {
   uint16_t* hsh;           // [M, Is] bf16 shared h
   float* S;                // [M, H]
   float* D;                // [M*K, H]
+  // split small-step path (M <= kSmallRows): per-segment fp32 partials
+  int split;
+  float* part_gu;          // [kSegGU][M*K][2][I]  routed gate / up
+  float* part_sh;          // [kSegSG][M][2][Is]   shared gate / up
+  float* part_d;           // [kSegDN][M*K][H]     routed down
+  float* part_s;           // [kSegDN][M][H]       shared down
   uint16_t* y;             // bf16 [M, H]
 };
 
 // Kernel ids reported by the timing hook (moe_trace_set).
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
-  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_COUNT
+  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_COUNT
 };
 
 void trace_before(hipStream_t s);
@@ -83,9 +98,12 @@ void trace_after(int kid, hipStream_t s);
   } while (0)
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// split small steps: logits + x quantization + shared gate/up, then select/union + shared h_s
+hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s);
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prep(const FfnArgs& a, hipStream_t s);   // quantize x
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+bool use_split(int M, int H);   // M <= kSmallRows and the x codes fit the LDS budget
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);
 

@@ -10,8 +10,9 @@
 //
 // Logits are float64: bf16 x bf16 products are exact in float64, so the
 // selection agrees with a float64 evaluation except on near-exact ties.
-#include "moe_device.h"
-#include "moe_internal.h"
+#include <string.h>
+
+#include "moe_chains.h"
 
 namespace moe {
 
@@ -104,9 +105,7 @@ __device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_
     sg[q] = 0.0;
     if (ok[q]) {
       const double l = a.logits[(size_t)row * a.E + e];
-      sg[q] = 1.0 / (1.0 + exp(-l));
-      const double cc = sg[q] + (double)a.bias[e];
-      c[q] = (cc == cc) ? cc : -INFINITY;
+      route_score(l, a.bias[e], sg[q], c[q]);
     }
   }
   // k rounds of a wave-wide argmax of (c, -id)
@@ -251,9 +250,10 @@ __global__ __launch_bounds__(1024) void k_union(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- small steps
-// For M <= 16 rows: one workgroup per expert with one wave per row computing
-// that row's logit by the procedure above (chunks streamed through a ring);
-// then one workgroup selects every row's top-k and builds the union and the
+// For M <= 16 rows.  Logits: one workgroup per expert with one wave per row,
+// the row's chunks streamed through a ring (same per-lane procedure as
+// above); the kernel also stores sigmoid(l) and the biased score c.  Then one
+// workgroup selects every row's top-k by rank and builds the union and the
 // row lists in LDS.  The kernel boundary orders the two phases.
 constexpr int kSmallRing = 4;
 
@@ -291,11 +291,8 @@ __device__ __forceinline__ double dot_chunk(const uint4& xv, const uint4& wv, do
   return acc;
 }
 
-__global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x;
-  const int r = threadIdx.x >> 6;          // one wave per row
-  if (r >= a.M || (a.mask != nullptr && a.mask[r] == 0)) return;
+// logit of (row r, expert e) for the calling wave; stores sigmoid and score
+__device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int lane) {
   const uint16_t* wrow = a.wr + (size_t)e * a.H + 8 * lane;
   const uint16_t* xrow = a.x + (size_t)r * a.H + 8 * lane;
   const int nch = (a.H + 511) / 512;
@@ -320,19 +317,155 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
       }
     }
   }
-  const double sum = wave_sum_f64(acc);
-  if (lane == 0) a.logits[(size_t)r * a.E + e] = sum;
+  const double l = wave_sum_f64(acc);
+  if (lane == 0) {
+    double sig, c;
+    route_score(l, a.bias[e], sig, c);
+    a.logits[(size_t)r * a.E + e] = c;
+    a.sig[(size_t)r * a.E + e] = sig;
+  }
 }
 
-// One workgroup: top-k of every row (wave per row), then the union and the
-// row lists built in LDS, one thread per expert.
-__global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a) {
+__global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = threadIdx.x >> 6;          // one wave per row
+  if (r >= a.M || (a.mask != nullptr && a.mask[r] == 0)) return;
+  logit_row(a, r, blockIdx.x, lane);
+}
+
+// The front of a split small step (M <= kSmallRows), one launch:
+//   blocks [0, E)             logits of expert b, wave = row
+//   blocks [E, E + nq)        x quantization, one (row, 128-block) per wave
+//   blocks [E + nq, ...)      shared expert gate/up, one K segment of one
+//                             8-column tile per wave (fp32 partials)
+// The shared expert needs no routing, so its weights stream while the router
+// runs.
+__global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  if (b < r.E) {
+    if (wave < r.M && (r.mask == nullptr || r.mask[wave] != 0)) logit_row(r, wave, b, lane);
+    return;
+  }
+  if (b < r.E + nq) {
+    const int item = (b - r.E) * 8 + wave;
+    const int nb = f.H / kBlk;
+    const int row = item / nb, blk = item % nb;
+    if (row >= f.M || !row_real(f.mask, row)) return;
+    const uint16_t* p = f.x + (size_t)row * f.H + blk * kBlk + 2 * lane;
+    quant_pair(bf16_to_f32(p[0]), bf16_to_f32(p[1]), f.xq + (size_t)row * f.H + blk * kBlk, f.xs + (size_t)row * nb + blk,
+               lane);
+    return;
+  }
+  const int t = (b - r.E - nq) * 8 + wave;
+  if (f.Is == 0 || t >= (f.Is / 8) * kSegSG) return;
+  const int c = lane & 15, kq = lane >> 4;
+  const int seg = t % kSegSG, nt = t / kSegSG;
+  const int n0 = nt * 8;
+  const bool valid = c < f.M && row_real(f.mask, c);
+  const uint16_t* wp = (c < 8 ? f.wsg : f.wsu) + (size_t)(n0 + (c & 7)) * f.H + kq * 8;
+  const uint16_t* bp = f.x + (size_t)(valid ? c : 0) * f.H + kq * 8;
+  const int nst = f.H / 32;
+  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));
+  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + (kq >> 1)) * f.Is + n0 + (kq & 1) * 4, p);
+}
+
+// One workgroup (blockIdx 0): top-k of every row by rank (c[e] beats c[e']
+// when larger, or equal with the lower id), then the union and the row lists
+// in LDS, one thread per expert.  With do_hs, blocks >= 1 also form the
+// shared expert's h_s = bf16(silu(g) u) from its segment partials.
+__global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArgs f, int do_hs) {
+  __shared__ double sc[kDecodeMaxRows][kMaxExperts];
+  __shared__ double ssig[kDecodeMaxRows][kMaxTopK];
   __shared__ uint32_t sbits[kDecodeMaxRows][8];
   __shared__ int tmp[16];
+  if (blockIdx.x > 0) {
+    if (!do_hs) return;
+    const long idx = ((long)(blockIdx.x - 1) * blockDim.x + threadIdx.x) * 2;
+    const int r = (int)(idx / f.Is), n = (int)(idx % f.Is);
+    if (r >= f.M || !row_real(f.mask, r)) return;
+    const size_t st = (size_t)f.M * 2 * f.Is;
+    const float* pg = f.part_sh + ((size_t)r * 2 + 0) * f.Is + n;
+    const float* pu = f.part_sh + ((size_t)r * 2 + 1) * f.Is + n;
+    float2 g = *reinterpret_cast<const float2*>(pg);
+    float2 u = *reinterpret_cast<const float2*>(pu);
+    for (int s = 1; s < kSegSG; ++s) {
+      const float2 gs = *reinterpret_cast<const float2*>(pg + s * st);
+      const float2 us = *reinterpret_cast<const float2*>(pu + s * st);
+      g.x = g.x + gs.x; g.y = g.y + gs.y;
+      u.x = u.x + us.x; u.y = u.y + us.y;
+    }
+    const uint32_t h = (uint32_t)f32_to_bf16(silu_mul(g.x, u.x)) | ((uint32_t)f32_to_bf16(silu_mul(g.y, u.y)) << 16);
+    *reinterpret_cast<uint32_t*>(f.hsh + (size_t)r * f.Is + n) = h;
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int r = threadIdx.x >> 6;
-  if (r < a.M) select_row(a, r, lane, &sbits[r][0]);
+  const int nwords = (a.E + 31) / 32;
+  const bool real = r < a.M && (a.mask == nullptr || a.mask[r] != 0);
+  double c[4], sg[4];
+  if (real) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      c[q] = -INFINITY;
+      sg[q] = 0.0;
+      if (e < a.E) {
+        c[q] = a.logits[(size_t)r * a.E + e];
+        sg[q] = a.sig[(size_t)r * a.E + e];
+        sc[r][e] = c[q];
+      }
+    }
+  }
   __syncthreads();
+  if (real) {
+    bool picked[4];
+    int rank[4] = {0, 0, 0, 0};
+#pragma unroll 8
+    for (int e2 = 0; e2 < a.E; ++e2) {
+      const double v = sc[r][e2];           // same address in every lane: an LDS broadcast
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rank[q] += (v > c[q] || (v == c[q] && e2 < lane + 64 * q)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) picked[q] = lane + 64 * q < a.E && rank[q] < a.K;
+    // ascending id order: id = lane + 64 q, so positions follow q, then lane
+    int base = 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t m = __ballot(picked[q]);
+      if (picked[q]) {
+        const int pos = base + __popcll(m & below);
+        ssig[r][pos] = sg[q];
+        a.ids[(size_t)r * a.K + pos] = lane + 64 * q;
+      }
+      if (lane == 2 * q || lane == 2 * q + 1) {
+        const uint32_t word = (uint32_t)(lane == 2 * q ? m : (m >> 32));
+        if (lane < nwords) {
+          sbits[r][lane] = word;
+          a.rowbits[(size_t)r * nwords + lane] = word;
+        }
+      }
+      base += __popcll(m);
+    }
+  } else if (r < a.M) {
+    if (lane < a.K) {
+      a.ids[(size_t)r * a.K + lane] = -1;
+      a.w[(size_t)r * a.K + lane] = 0.0f;
+      a.slot_of[(size_t)r * a.K + lane] = -1;
+    }
+    if (lane < nwords) {
+      sbits[r][lane] = 0u;
+      a.rowbits[(size_t)r * nwords + lane] = 0u;
+    }
+  }
+  __syncthreads();
+  if (real && lane < a.K) {
+    double tot = 0.0;
+    for (int j = 0; j < a.K; ++j) tot += ssig[r][j];     // ascending id order
+    a.w[(size_t)r * a.K + lane] = (float)((double)a.scale * (ssig[r][lane] / tot));
+  }
   const int t = threadIdx.x;
   int cnt = 0;
   if (t < a.E)
@@ -367,16 +500,29 @@ __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- launchers
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const dim3 blk(256);
   if (a.M <= kDecodeMaxRows) {
+    FfnArgs none;
+    memset(&none, 0, sizeof(none));
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * a.M), 0, s, a);
-    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(1024), 0, s, a);
+    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(1024), 0, s, a, none, 0);
     return hipSuccess;
   }
   MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((a.M + 7) / 8, (a.E + 15) / 16), blk, 0, s, a);
   MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union, dim3(1), dim3(1024), 0, s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s) {
+  const int nq = (f.M * (f.H / kBlk) + 7) / 8;
+  const int ns = f.Is > 0 ? ((f.Is / 8) * kSegSG + 7) / 8 : 0;
+  MOE_LAUNCH(KID_FRONT, k_front, dim3(r.E + nq + ns), dim3(512), 0, s, r, f, nq);
+  const int nh = f.Is > 0 ? (f.M * f.Is / 2 + 1023) / 1024 : 0;
+  MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1 + nh), dim3(1024), 0, s, r, f, f.Is > 0 ? 1 : 0);
   return hipSuccess;
 }
 

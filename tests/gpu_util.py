@@ -163,37 +163,76 @@ def assert_y_close(y_bits, out: oracle.LayerOut, rows=None, tol=REL_TOL) -> floa
     return float(err.max())
 
 
-def _adjacent(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    zero = {0x00, 0x80, 0x01, 0x81}
-    same_sign = (a & 0x80) == (b & 0x80)
-    near_zero = np.isin(a, list(zero)) & np.isin(b, list(zero))
-    return (same_sign & (np.abs(a.astype(int) - b.astype(int)) <= 1)) | near_zero
+# Measured on gfx950: one 16x16x128 fp8 MFMA returns its 128-term dot product
+# within 2^-15 * sum|a*b| of the exact value.  The check below allows twice that.
+MFMA_REL = 2.0 ** -14
 
 
-def compare_h_codes(g_codes: np.ndarray, g_scales: np.ndarray, out: oracle.LayerOut, max_frac=1e-2,
-                    scale_tol=2.0 ** -10):
+def _e4m3_step(v_over_s: np.ndarray) -> np.ndarray:
+    """Grid spacing of e4m3 at |v/s| (3 mantissa bits; fixed 2^-9 below 2^-6)."""
+    a = np.maximum(np.abs(v_over_s), 2.0 ** -6)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 3)
+
+
+def h_value_bounds(out: oracle.LayerOut, gl: "GpuLayer"):
+    """Per evaluated slot: the oracle's float64 h and a bound on |h_gpu - h|.
+
+    G and U err by at most MFMA_REL * (sum over K-blocks of |s_x s_w| *
+    sum|a||w|) plus fp32 accumulation; the bound propagates that through
+    h = silu(G) * U to first order.  Absolute values of the codes are the
+    codes with the sign bit cleared."""
+    rt = out.routing
+    ew = gl.expert_fn()
+    res = {}
+    for u, e in enumerate(rt.union_ids):
+        slots = [s for s in range(int(rt.offs[u]), int(rt.offs[u + 1])) if s in out.h_codes]
+        if not slots:
+            continue
+        rows = rt.rows[slots]
+        xq, xs = out.x_codes[rows], out.x_scales[rows]
+        w = ew(int(e))
+        g = oracle.block_gemm(xq, xs, w["gate"], w["s_gate"])
+        uu = oracle.block_gemm(xq, xs, w["up"], w["s_up"])
+        ag = oracle.block_gemm(xq & 0x7F, xs, w["gate"] & 0x7F, w["s_gate"])
+        au = oracle.block_gemm(xq & 0x7F, xs, w["up"] & 0x7F, w["s_up"])
+        nkb = xq.shape[1] // 128
+        dg = (MFMA_REL + nkb * 2.0 ** -23) * ag
+        du = (MFMA_REL + nkb * 2.0 ** -23) * au
+        sg = 1.0 / (1.0 + np.exp(-g))
+        h = g * sg * uu
+        dh = np.abs(uu * sg * (1.0 + g * (1.0 - sg))) * dg + np.abs(g * sg) * du + 2.0 ** -21 * np.abs(h)
+        for i, s in enumerate(slots):
+            res[s] = (h[i], dh[i])
+    return res
+
+
+def compare_h_codes(g_codes: np.ndarray, g_scales: np.ndarray, out: oracle.LayerOut, gl: "GpuLayer",
+                    max_frac=1e-2, scale_tol=2.0 ** -10):
     """Layer-level h codes.
 
     The requantization itself is bit-exact (checked on its own against the
-    oracle's fl32(h)).  Upstream, the gfx950 fp8 MFMA returns each 128-term
-    partial within 2^-15 of sum|a*b| (measured; not a correctly rounded fp32
-    sum), so G and U move by ~1e-5 relative and an h value lying that close to
-    an e4m3 rounding midpoint lands on the neighbouring code.  Allowed: every
-    difference is an adjacent code, at most 1% of codes differ, and block
-    scales (amax / 448) agree within 2^-10 relative."""
+    oracle's fl32(h)).  Upstream, G and U carry the MFMA error above, so an h
+    lying that close to a rounding midpoint lands on another code.  Allowed:
+    every decoded GPU value within (propagated error bound + one e4m3 step at
+    that magnitude) of the oracle's h, at most 1% of codes different, and
+    block scales (amax/448) within 2^-10 relative."""
+    bounds = h_value_bounds(out, gl)
     n = 0
     bad = 0
     worst = 0.0
     for s, oc in out.h_codes.items():
         gc = g_codes[s]
-        diff = gc != oc
-        bad += int(diff.sum())
+        bad += int((gc != oc).sum())
         n += oc.size
-        assert _adjacent(gc[diff], oc[diff]).all(), f"non-adjacent h code flip at slot {s}"
         gs = g_scales[s].astype(np.float64)
         os_ = out.h_scales[s].astype(np.float64)
+        hg = (oracle.decode_e4m3(gc).reshape(gs.size, -1) * gs[:, None]).reshape(-1)
+        h, dh = bounds[s]
+        step = _e4m3_step(h / np.repeat(os_, 128)) * np.repeat(os_, 128)
+        ok = np.abs(hg - h) <= dh + 1.01 * step
+        assert ok.all(), f"h values differ at slot {s}: worst excess {np.max(np.abs(hg - h) - dh - step):.3e}"
         worst = max(worst, float(np.max(np.abs(gs - os_) / os_)))
-    say(f"h codes: {bad} of {n} differ (adjacent); worst scale rel diff {worst:.2e}")
+    say(f"h codes: {bad} of {n} differ; worst scale rel diff {worst:.2e}")
     assert worst <= scale_tol, f"h scales differ by {worst:.2e}"
     assert bad <= max(2, max_frac * n), f"{bad} of {n} h codes differ"
     return bad, n

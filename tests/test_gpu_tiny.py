@@ -71,7 +71,7 @@ def test_layer_parity(tiny):
     assert_routing_equal(g, o.routing, mask)
     assert np.array_equal(g["x_codes"], o.x_codes)
     assert np.array_equal(g["x_scales"], o.x_scales)
-    bad, n = compare_h_codes(g["h_codes"], g["h_scales"], o)
+    bad, n = compare_h_codes(g["h_codes"], g["h_scales"], o, gl)
     err = assert_y_close(g["y"], o)
     say(f"tiny layer: max row rel err {err:.3e}, h code flips {bad}/{n}")
 
@@ -105,7 +105,7 @@ def test_ffn_fp8_with_oracle_routing(tiny):
     cfg, gl, x, mask = tiny
     o = run_oracle(gl, x, mask, shared=False)
     g = run_ffn(gl, x, mask, o.routing)
-    compare_h_codes(g["h_codes"], g["h_scales"], o)
+    compare_h_codes(g["h_codes"], g["h_scales"], o, gl)
     err = assert_y_close(g["y"], o)
     say(f"ffn_fp8 (routed only): max row rel err {err:.3e}")
 
@@ -170,7 +170,7 @@ def test_ragged_row_counts(tiny, m):
     o = run_oracle(gl, x, mask)
     assert_routing_equal(g, o.routing, mask)
     assert np.array_equal(g["x_codes"][mask != 0], o.x_codes[mask != 0])
-    compare_h_codes(g["h_codes"], g["h_scales"], o)
+    compare_h_codes(g["h_codes"], g["h_scales"], o, gl)
     assert_y_close(g["y"], o)
     assert not g["y"][mask == 0].any()
 
