@@ -120,15 +120,33 @@ def decode_bytes(nu, d, m):
 
 
 def gateup_bytes(nu, d, m):
-    """Algorithmic bytes of the gate/up kernel: gate and up codes + scales of
-    the union experts, the shared gate/up bf16 weights, x codes and bf16 x."""
-    H, I, Is = d.hidden, d.inter, d.shared_inter
-    return nu * (2 * I * H + 4 * 2 * (I // 128) * (H // 128)) + 2 * Is * H * 2 + m * H * 3 + m * (H // 128) * 4
+    """Algorithmic bytes of the routed gate/up kernel (small steps): gate and up
+    codes + scales of the union experts, x codes and scales."""
+    H, I = d.hidden, d.inter
+    return nu * (2 * I * H + 4 * 2 * (I // 128) * (H // 128)) + m * H + m * (H // 128) * 4
 
 
 def down_decode_bytes(nu, d, m):
-    H, I, Is = d.hidden, d.inter, d.shared_inter
-    return nu * (I * H + 4 * (H // 128) * (I // 128)) + H * Is * 2 + m * H * 2
+    """Algorithmic bytes of the down kernel: down codes + scales of the union
+    experts, the shared down bf16 weights, h codes + scales, shared h (bf16)."""
+    H, I, Is, K = d.hidden, d.inter, d.shared_inter, d.top_k
+    return (nu * (I * H + 4 * (H // 128) * (I // 128)) + H * Is * 2 + m * K * (I + 4 * (I // 128))
+            + m * Is * 2)
+
+
+def front_bytes(d, m):
+    """Algorithmic bytes of the fused front kernel (small steps): the router
+    weights, the shared gate/up bf16 weights, x (bf16) once, x codes and
+    scales out."""
+    H, Is, E = d.hidden, d.shared_inter, d.n_experts
+    return E * H * 2 + 2 * Is * H * 2 + m * H * 2 + m * H + m * (H // 128) * 4
+
+
+def kernel_bytes(name, nu, d, m):
+    """Algorithmic bytes per launch of the kernels that stream weights."""
+    return {"gateup": gateup_bytes(nu, d, m),
+            "down": down_decode_bytes(nu, d, m),
+            "front": front_bytes(d, m)}.get(name)
 
 
 def layer_flops(d, m_real, slots):
@@ -165,6 +183,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs the layer on one GPU only; --gpus {args.gpus} is not supported "
@@ -178,8 +198,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    lib = moe.load()
     torch.cuda.set_device(0)
+    if args.calib_copy:
+        n = args.calib_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x5")
+        return
+    lib = moe.load()
 
     # ---------------- decode: span-8 step
     cfg = synth.CONFIGS["span8"]
@@ -265,12 +294,13 @@ def main():
         per.setdefault(name, []).append(tev.elapsed_ms(tev.ev[2 * i], tev.ev[2 * i + 1]))
     kern_us = {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
     tev.close()
-    dom = max(kern_us, key=lambda k: kern_us[k])
-    dom_bytes = {"gateup": gateup_bytes(nu, d, M), "down_combine_decode": down_decode_bytes(nu, d, M)}.get(dom)
-    if dom_bytes is None:
-        dom_bytes = total_b
+    streaming = {k: v for k, v in kern_us.items() if kernel_bytes(k, nu, d, M) is not None}
+    dom = max(streaming, key=lambda k: streaming[k])
+    dom_bytes = kernel_bytes(dom, nu, d, M)
     dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
     log(f"[bench] kernels (us): " + ", ".join(f"{k}={v:.1f}" for k, v in kern_us.items()))
+    log(f"[bench] kernel GB/s: " + ", ".join(
+        f"{k}={kernel_bytes(k, nu, d, M) / (v * 1e-6) / 1e9:.0f}" for k, v in streaming.items()))
 
     result = {
         "metric": METRIC,
@@ -298,7 +328,8 @@ def main():
         "routed_weight_bytes": routed_b,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": dom_bytes, "kernel_us": round(kern_us[dom], 2)},
     }
 
     # ---------------- CPU oracle baseline on the same decode step

@@ -128,10 +128,78 @@ __device__ __forceinline__ void scale_acc(v4f& acc, const v4f& p, float sa, floa
   acc[3] = __builtin_fmaf(ss, p[3], acc[3]);
 }
 
+// ---------------------------------------------------------------- cross-lane, VALU only
+// DPP lane patterns (within rows of 16 lanes) and the gfx950 row swaps move
+// data between lanes without the LDS round trip of ds_bpermute.
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15 - i within 16
+constexpr int kDppRowShr1 = 0x111;      // row_shr:n = 0x110 + n
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, true);
+}
+
+// max of a value over the wave.  The mirrors pair whole quads / halves after
+// the quad steps, so every lane ends with the row maximum; each row swap puts
+// the partner row's value in one of its two outputs (the lane's own value in
+// the other), so taking the max over both covers either ordering.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(v, fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1])));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(v, fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])));
   return v;
+}
+
+__device__ __forceinline__ double u2_to_f64(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return u2_to_f64(dpp_u32<kCtrl>((uint32_t)b), dpp_u32<kCtrl>((uint32_t)(b >> 32)));
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<kDppXor1>(v));
+  v = fmax(v, dpp_f64<kDppXor2>(v));
+  v = fmax(v, dpp_f64<kDppHalfMirror>(v));
+  v = fmax(v, dpp_f64<kDppMirror>(v));
+  {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = fmax(v, fmax(u2_to_f64(lo[0], hi[0]), u2_to_f64(lo[1], hi[1])));
+  }
+  {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = fmax(v, fmax(u2_to_f64(lo[0], hi[0]), u2_to_f64(lo[1], hi[1])));
+  }
+  return v;
+}
+
+// Inclusive prefix sum over the wave (unsigned, wrapping): Hillis-Steele
+// shifts within each row of 16, then the totals of the rows below.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+  v += dpp_u32<kDppRowShr1>(v);           // row_shr with zero fill at the row start
+  v += dpp_u32<kDppRowShr1 + 1>(v);
+  v += dpp_u32<kDppRowShr1 + 3>(v);
+  v += dpp_u32<kDppRowShr1 + 7>(v);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {

@@ -79,6 +79,29 @@ __global__ __launch_bounds__(256) void k_router_logits(RouteArgs a) {
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 256;
 
+// k rounds of a wave-wide argmax of (score, -id) over candidates held four per
+// lane (id = lane + 64 q): the k largest scores, ties to the lower id.  The
+// winners are marked in picked[] and cleared from ok[].  Scores are never NaN
+// (route_score maps NaN to -inf); -inf candidates still rank by id.
+__device__ __forceinline__ void topk_rounds(const double (&c)[4], bool (&ok)[4], bool (&picked)[4], int k, int lane) {
+  for (int j = 0; j < k; ++j) {
+    double m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (ok[q]) m = fmax(m, c[q]);
+    m = wave_max_f64(m);
+    int best = -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t b = __ballot(ok[q] && c[q] == m);
+      if (best < 0 && b != 0ull) best = 64 * q + __ffsll((long long)b) - 1;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane + 64 * q == best) { ok[q] = false; picked[q] = true; }
+  }
+}
+
 __device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_bits) {
   const int nwords = (a.E + 31) / 32;
   const bool real = (a.mask == nullptr || a.mask[row] != 0);
@@ -108,25 +131,7 @@ __device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_
       route_score(l, a.bias[e], sg[q], c[q]);
     }
   }
-  // k rounds of a wave-wide argmax of (c, -id)
-  for (int j = 0; j < a.K; ++j) {
-    double bc = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (ok[q] && (c[q] > bc || (c[q] == bc && e < be))) { bc = c[q]; be = e; }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double oc = __shfl_xor(bc, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (oc > bc || (oc == bc && oe < be)) { bc = oc; be = oe; }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + 64 * q == be) { ok[q] = false; picked[q] = true; }
-  }
+  topk_rounds(c, ok, picked, a.K, lane);
   // Ascending id order: id = lane + 64 q, so positions follow q, then lane.
   // Each pick is pushed to lane `position` (ds_permute); lane 63 is never a
   // position (k <= 16) and takes the pushes of lanes without a pick.
@@ -257,28 +262,6 @@ __global__ __launch_bounds__(1024) void k_union(RouteArgs a) {
 // row lists in LDS.  The kernel boundary orders the two phases.
 constexpr int kSmallRing = 4;
 
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(x, o, 64);
-    if (lane >= o) x += n;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int t = tmp[w];
-    if (w < wave) before += t;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
-}
-
 __device__ __forceinline__ double dot_chunk(const uint4& xv, const uint4& wv, double acc) {
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
   const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -375,10 +358,10 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
 // in LDS, one thread per expert.  With do_hs, blocks >= 1 also form the
 // shared expert's h_s = bf16(silu(g) u) from its segment partials.
 __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArgs f, int do_hs) {
-  __shared__ double sc[kDecodeMaxRows][kMaxExperts];
   __shared__ double ssig[kDecodeMaxRows][kMaxTopK];
+  __shared__ int sid[kDecodeMaxRows][kMaxTopK];
   __shared__ uint32_t sbits[kDecodeMaxRows][8];
-  __shared__ int tmp[16];
+  __shared__ int soff[kMaxExperts];
   if (blockIdx.x > 0) {
     if (!do_hs) return;
     const long idx = ((long)(blockIdx.x - 1) * blockDim.x + threadIdx.x) * 2;
@@ -399,36 +382,27 @@ __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArg
     *reinterpret_cast<uint32_t*>(f.hsh + (size_t)r * f.Is + n) = h;
     return;
   }
+  // Phase A (wave r = row r): top-k, ids in ascending order, row bitmaps.
   const int lane = threadIdx.x & 63;
   const int r = threadIdx.x >> 6;
   const int nwords = (a.E + 31) / 32;
   const bool real = r < a.M && (a.mask == nullptr || a.mask[r] != 0);
-  double c[4], sg[4];
   if (real) {
+    double c[4], sg[4];
+    bool ok[4], picked[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
+      ok[q] = e < a.E;
+      picked[q] = false;
       c[q] = -INFINITY;
       sg[q] = 0.0;
-      if (e < a.E) {
+      if (ok[q]) {
         c[q] = a.logits[(size_t)r * a.E + e];
         sg[q] = a.sig[(size_t)r * a.E + e];
-        sc[r][e] = c[q];
       }
     }
-  }
-  __syncthreads();
-  if (real) {
-    bool picked[4];
-    int rank[4] = {0, 0, 0, 0};
-#pragma unroll 8
-    for (int e2 = 0; e2 < a.E; ++e2) {
-      const double v = sc[r][e2];           // same address in every lane: an LDS broadcast
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rank[q] += (v > c[q] || (v == c[q] && e2 < lane + 64 * q)) ? 1 : 0;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) picked[q] = lane + 64 * q < a.E && rank[q] < a.K;
+    topk_rounds(c, ok, picked, a.K, lane);
     // ascending id order: id = lane + 64 q, so positions follow q, then lane
     int base = 0;
     const uint64_t below = (1ull << lane) - 1ull;
@@ -438,6 +412,7 @@ __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArg
       if (picked[q]) {
         const int pos = base + __popcll(m & below);
         ssig[r][pos] = sg[q];
+        sid[r][pos] = lane + 64 * q;
         a.ids[(size_t)r * a.K + pos] = lane + 64 * q;
       }
       if (lane == 2 * q || lane == 2 * q + 1) {
@@ -461,42 +436,63 @@ __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArg
     }
   }
   __syncthreads();
+  // Phase B (last wave; lane l owns experts 4 l .. 4 l + 3): per-expert row
+  // counts, then one exclusive scan of a packed word gives each expert's
+  // first slot (bits 0-12), union index (bits 13-21) and first M-tile (22-31).
+  if (r == (int)(blockDim.x >> 6) - 1) {
+    uint32_t cnt[4], pk[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      cnt[i] = 0;
+      if (e < a.E) {
+#pragma unroll
+        for (int q = 0; q < kDecodeMaxRows; ++q)
+          if (q < a.M) cnt[i] += (sbits[q][e >> 5] >> (e & 31)) & 1u;
+      }
+      pk[i] = run;
+      run += cnt[i] | ((cnt[i] > 0 ? 1u : 0u) << 13) | (((cnt[i] + kMTile - 1) / kMTile) << 22);
+    }
+    const uint32_t incl = wave_incl_scan(run, lane);
+    const uint32_t base = incl - run;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cnt[i] == 0) continue;
+      const int e = 4 * lane + i;
+      const uint32_t v = base + pk[i];
+      const int off = (int)(v & 0x1FFFu), uidx = (int)((v >> 13) & 0x1FFu);
+      a.union_ids[uidx] = e;
+      a.offs[uidx] = off;
+      a.mtile_offs[uidx] = (int)(v >> 22);
+      soff[e] = off;
+    }
+    if (lane == 63) {
+      const int nu = (int)((incl >> 13) & 0x1FFu), total = (int)(incl & 0x1FFFu), total_mt = (int)(incl >> 22);
+      a.offs[nu] = total;
+      a.mtile_offs[nu] = total_mt;
+      *a.n_union = nu;
+      a.sched[SCHED_NUNION] = nu;
+      a.sched[SCHED_MTILES] = total_mt;
+      a.sched[SCHED_SLOTS] = total;
+      a.sched[SCHED_BAD] = 0;
+    }
+  }
+  __syncthreads();
+  // Phase C (wave r, lane j = pick j): combine weight and slot.  An expert's
+  // slots list its rows ascending, so row r's slot is the expert's first slot
+  // plus the number of earlier rows that picked it.
   if (real && lane < a.K) {
     double tot = 0.0;
     for (int j = 0; j < a.K; ++j) tot += ssig[r][j];     // ascending id order
     a.w[(size_t)r * a.K + lane] = (float)((double)a.scale * (ssig[r][lane] / tot));
-  }
-  const int t = threadIdx.x;
-  int cnt = 0;
-  if (t < a.E)
-    for (int q = 0; q < a.M; ++q) cnt += (sbits[q][t >> 5] >> (t & 31)) & 1u;
-  int nu, total, total_mt;
-  const int off = block_excl_scan(cnt, tmp, &total);
-  const int uidx = block_excl_scan(cnt > 0 ? 1 : 0, tmp, &nu);
-  const int mto = block_excl_scan((cnt + kMTile - 1) / kMTile, tmp, &total_mt);
-  if (cnt > 0) {
-    a.union_ids[uidx] = t;
-    a.offs[uidx] = off;
-    a.mtile_offs[uidx] = mto;
-    int i = 0;
-    const uint32_t below = (1u << (t & 31)) - 1u;
-    for (int q = 0; q < a.M; ++q) {
-      if (!((sbits[q][t >> 5] >> (t & 31)) & 1u)) continue;
-      int j = __popc(sbits[q][t >> 5] & below);
-      for (int w2 = 0; w2 < (t >> 5); ++w2) j += __popc(sbits[q][w2]);
-      a.rows[off + i] = q;
-      a.slot_of[(size_t)q * a.K + j] = off + i;
-      ++i;
-    }
-  }
-  if (t == 0) {
-    a.offs[nu] = total;
-    a.mtile_offs[nu] = total_mt;
-    *a.n_union = nu;
-    a.sched[SCHED_NUNION] = nu;
-    a.sched[SCHED_MTILES] = total_mt;
-    a.sched[SCHED_SLOTS] = total;
-    a.sched[SCHED_BAD] = 0;
+    const int e = sid[r][lane];
+    int before = 0;
+#pragma unroll
+    for (int q = 0; q < kDecodeMaxRows; ++q)
+      if (q < r) before += (sbits[q][e >> 5] >> (e & 31)) & 1u;
+    const int slot = soff[e] + before;
+    a.slot_of[(size_t)r * a.K + lane] = slot;
+    a.rows[slot] = r;
   }
 }
 
