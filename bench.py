@@ -157,6 +157,20 @@ def layer_flops(d, m_real, slots):
     return fp8, bf16, router
 
 
+COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_span8_hbm_counters.md")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    from sparse_moe_ffn_02_amd.profile_summary import load_traffic
+    tr = load_traffic(COUNTERS)
+    if not tr:
+        return None
+    k = tr["kernels"].get(kernel + "_split") or tr["kernels"].get(kernel)
+    return None if k is None else k["read_bytes"] + k["write_bytes"]
+
+
 def cpu_info():
     try:
         threads = len(os.sched_getaffinity(0))
@@ -328,7 +342,9 @@ def main():
         "routed_weight_bytes": routed_b,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": dom_bytes, "kernel_us": round(kern_us[dom], 2)},
     }
 
