@@ -187,6 +187,62 @@ def cpu_info():
     return threads, model
 
 
+def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
+    """4096-token prefill chunk over `args.prefill_layers` stacked layers."""
+    pcfg = synth.CONFIGS["prefill4096x4"]
+    n_layers = args.prefill_layers
+    layers = []
+    for l in range(n_layers):
+        t0 = time.time()
+        layers.append(device_layer(pcfg, l, torch, moe, replicas=1)[0])
+        log(f"[bench] prefill layer {l} ready in {time.time() - t0:.1f}s")
+    Mp = pcfg.rows
+    xs = [torch.from_numpy(synth.activations(pcfg, layer=l)[0].view(np.int16)).cuda() for l in range(n_layers)]
+    wsp = moe.workspace(md, Mp)
+    yp = torch.empty((Mp, d.hidden), dtype=torch.int16, device="cuda")
+    rts = [moe.Routing.empty(md, Mp) for _ in layers]
+
+    def pstep():
+        for l, L in enumerate(layers):
+            moe.layer(md, xs[l], None, L["router_w"], L["bias"], L["experts"], L["shared"], yp, rts[l], wsp)
+
+    pstep()
+    torch.cuda.synchronize()
+    rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+    for _ in range(args.prefill_steps):
+        pstep()
+    rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+    torch.cuda.synchronize()
+    ms_p = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.prefill_steps
+    f8 = f16 = fr = 0.0
+    pbytes = 0
+    loads = []
+    for l in range(n_layers):
+        nu_l = int(rts[l].n_union.item())
+        sl = int(rts[l].offs[nu_l].item())
+        a, b_, c_ = layer_flops(d, Mp, sl)
+        f8 += a; f16 += b_; fr += c_
+        rb, fb = decode_bytes(nu_l, d, Mp)
+        pbytes += rb + fb
+        loads.append(np.diff(rts[l].offs[:nu_l + 1].cpu().numpy()))
+    t_s = ms_p * 1e-3
+    out = {
+        "workload": f"4096-token prefill chunk over {n_layers} stacked MoE layers (independent seeded weights, "
+                    "per-layer seeded inputs), Zipf(1.1) router bias, same layer shape",
+        "layers": n_layers,
+        "ms_per_step": round(ms_p, 4), "ms_per_layer": round(ms_p / n_layers, 4),
+        "tflops_total": round((f8 + f16 + fr) / t_s / 1e12, 2),
+        "tflops_fp8": round(f8 / t_s / 1e12, 2),
+        "fp8_mfma_frac": round(f8 / t_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "mfma_composite_frac": round((f8 / 1e12 / FP8_PEAK_TFLOPS + f16 / 1e12 / BF16_PEAK_TFLOPS) / t_s, 4),
+        "hbm_frac": round(pbytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
+        "expert_rows_max": int(max(l.max() for l in loads)),
+        "expert_rows_mean": round(float(np.mean([l.mean() for l in loads])), 1),
+    }
+    log(f"[bench] prefill4096 x{n_layers} layers: {ms_p:.2f} ms/step, {out['tflops_total']} TFLOPS")
+    return out
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -196,6 +252,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4, help="device copies of the decode layer's weights")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="only the prefill part (profiling)")
+    ap.add_argument("--prefill-layers", type=int, default=4, help="stacked layers of the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
@@ -223,6 +281,15 @@ def main():
         log(f"[bench] copied {n} bytes x5")
         return
     lib = moe.load()
+    if args.prefill_only:
+        pd = synth.CONFIGS["prefill4096x4"].dims
+        pmd = moe.Dims(pd.hidden, pd.n_experts, pd.top_k, pd.inter, pd.shared_inter, pd.routed_scale)
+        pev = HipEvents(2)
+        pev.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        out = prefill_bench(args, torch, moe, synth, pmd, pd, pev, pev.rt, torch.cuda.current_stream().cuda_stream)
+        pev.close()
+        print(json.dumps({"prefill": out}), flush=True)
+        return
 
     # ---------------- decode: span-8 step
     cfg = synth.CONFIGS["span8"]
@@ -379,57 +446,8 @@ def main():
     del reps
     torch.cuda.empty_cache()
 
-    # ---------------- prefill: 4096 tokens over 4 stacked layers
     if not args.no_prefill:
-        pcfg = synth.CONFIGS["prefill4096x4"]
-        layers = []
-        for l in range(pcfg.n_layers):
-            t0 = time.time()
-            layers.append(device_layer(pcfg, l, torch, moe, replicas=1)[0])
-            log(f"[bench] prefill layer {l} ready in {time.time() - t0:.1f}s")
-        Mp = pcfg.rows
-        xs = [torch.from_numpy(synth.activations(pcfg, layer=l)[0].view(np.int16)).cuda() for l in range(pcfg.n_layers)]
-        wsp = moe.workspace(md, Mp)
-        yp = torch.empty((Mp, d.hidden), dtype=torch.int16, device="cuda")
-        rts = [moe.Routing.empty(md, Mp) for _ in layers]
-
-        def pstep():
-            for l, L in enumerate(layers):
-                moe.layer(md, xs[l], None, L["router_w"], L["bias"], L["experts"], L["shared"], yp, rts[l], wsp)
-
-        pstep()
-        torch.cuda.synchronize()
-        rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
-        for _ in range(args.prefill_steps):
-            pstep()
-        rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
-        torch.cuda.synchronize()
-        ms_p = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.prefill_steps
-        f8 = f16 = fr = 0.0
-        pbytes = 0
-        loads = []
-        for l in range(pcfg.n_layers):
-            nu_l = int(rts[l].n_union.item())
-            sl = int(rts[l].offs[nu_l].item())
-            a, b_, c_ = layer_flops(d, Mp, sl)
-            f8 += a; f16 += b_; fr += c_
-            rb, fb = decode_bytes(nu_l, d, Mp)
-            pbytes += rb + fb
-            loads.append(np.diff(rts[l].offs[:nu_l + 1].cpu().numpy()))
-        t_s = ms_p * 1e-3
-        result["prefill"] = {
-            "workload": "4096-token prefill chunk over 4 stacked MoE layers (independent seeded weights, per-layer "
-                        "seeded inputs), Zipf(1.1) router bias, same layer shape",
-            "ms_per_step": round(ms_p, 4), "ms_per_layer": round(ms_p / pcfg.n_layers, 4),
-            "tflops_total": round((f8 + f16 + fr) / t_s / 1e12, 2),
-            "tflops_fp8": round(f8 / t_s / 1e12, 2),
-            "fp8_mfma_frac": round(f8 / t_s / 1e12 / FP8_PEAK_TFLOPS, 4),
-            "mfma_composite_frac": round((f8 / 1e12 / FP8_PEAK_TFLOPS + f16 / 1e12 / BF16_PEAK_TFLOPS) / t_s, 4),
-            "hbm_frac": round(pbytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
-            "expert_rows_max": int(max(l.max() for l in loads)),
-            "expert_rows_mean": round(float(np.mean([l.mean() for l in loads])), 1),
-        }
-        log(f"[bench] prefill4096x4: {ms_p:.2f} ms/step, {result['prefill']['tflops_total']} TFLOPS")
+        result["prefill"] = prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream)
     ev.close()
     print(json.dumps(result), flush=True)
 

@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t sched, mtile, logits, sig, rowbits, xq, xs, hbuf, hq, hs, hsh, S, D, part_gu, part_sh, part_d, part_s, total;
+  size_t sched, mtile, logits, sig, rowbits, xq, xs, hq, hs, hsh, S, D, part_gu, part_sh, part_d, part_s, total;
   bool split;
 };
 
@@ -37,7 +37,6 @@ Layout make_layout(const moe_dims& d, int M) {
   L.rowbits = take(m * ((E + 31) / 32) * sizeof(uint32_t));
   L.xq = take(m * H);
   L.xs = take(m * (H / 128) * sizeof(float));
-  L.hbuf = take(m * K * I * sizeof(float));
   L.hq = take(m * K * I);
   L.hs = take(m * K * (I / 128) * sizeof(float));
   L.hsh = take(m * Is * sizeof(uint16_t));
@@ -162,7 +161,6 @@ FfnArgs ffn_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t* mas
   a.mtile_offs = reinterpret_cast<int32_t*>(ws + L.mtile);
   a.xq = (taps && taps->x_codes) ? taps->x_codes : reinterpret_cast<uint8_t*>(ws + L.xq);
   a.xs = (taps && taps->x_scales) ? taps->x_scales : reinterpret_cast<float*>(ws + L.xs);
-  a.hbuf = reinterpret_cast<float*>(ws + L.hbuf);
   a.hq = (taps && taps->h_codes) ? taps->h_codes : reinterpret_cast<uint8_t*>(ws + L.hq);
   a.hs = (taps && taps->h_scales) ? taps->h_scales : reinterpret_cast<float*>(ws + L.hs);
   a.hsh = reinterpret_cast<uint16_t*>(ws + L.hsh);

@@ -88,26 +88,6 @@ __global__ __launch_bounds__(64) void k_plan(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- work items
-struct Tile {
-  int e;       // expert id
-  int s0;      // first slot of the column tile
-  int mcnt;    // slots in the tile (<= 16)
-};
-
-__device__ __forceinline__ Tile routed_tile(const FfnArgs& a, int mtg) {
-  const int nu = a.sched[SCHED_NUNION];
-  int lo = 0, hi = nu - 1;          // largest u with mtile_offs[u] <= mtg
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.mtile_offs[mid] <= mtg) lo = mid; else hi = mid - 1;
-  }
-  Tile t;
-  t.e = a.union_ids[lo];
-  t.s0 = a.offs[lo] + (mtg - a.mtile_offs[lo]) * kMTile;
-  t.mcnt = min(kMTile, a.offs[lo + 1] - t.s0);
-  return t;
-}
-
 // One wave per work item.  The grid covers the largest item count the call
 // can produce (the union is only known on the device); waves past the real
 // count exit at once, and the hardware dispatcher balances the rest.
@@ -121,64 +101,6 @@ __device__ __forceinline__ const uint8_t* gu_row(const FfnArgs& a, int e, int n0
 }
 __device__ __forceinline__ const float* gu_scale(const FfnArgs& a, int e, int n0, int kq) {
   return (kq < 2 ? a.sg : a.su) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * (a.H / kBlk);
-}
-
-// ---------------------------------------------------------------- gate/up (any M)
-// Routed: 8 columns of I for one tile of <= 16 slots, all segments in-wave;
-// writes h = silu(G) * U (fp32) for the tile's slots.
-__device__ void routed_gateup(const FfnArgs& a, const Tile& t, int nt, int lane) {
-  const int c = lane & 15, kq = lane >> 4;
-  const int n0 = nt * 8;
-  const int nkb = a.H / kBlk;
-  int row = -1;
-  if (c < t.mcnt) {
-    row = a.rows[t.s0 + c];
-    if (row < 0 || row >= a.M) row = -1;
-  }
-  const uint8_t* bp = a.xq + (size_t)(row < 0 ? 0 : row) * a.H + kq * 32;
-  const float* sxp = a.xs + (size_t)(row < 0 ? 0 : row) * nkb;
-  const v4f acc = fp8_full<false>(gu_row(a, t.e, n0, c, kq), gu_scale(a, t.e, n0, kq), bp, sxp, row >= 0, nkb, kSegGU);
-  float u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[i], 32, 64);
-  if (kq < 2 && row >= 0) {
-    const v4f h = {silu_mul(acc[0], u[0]), silu_mul(acc[1], u[1]), silu_mul(acc[2], u[2]), silu_mul(acc[3], u[3])};
-    store_f4(a.hbuf + (size_t)(t.s0 + c) * a.I + n0 + kq * 4, h);
-  }
-}
-
-// Shared: 8 columns of I_s for 16 rows, all segments in-wave; h_s = bf16(silu(g) u).
-__device__ void shared_gateup(const FfnArgs& a, int mt, int nt, int lane) {
-  const int c = lane & 15, kq = lane >> 4;
-  const int n0 = nt * 8;
-  const int row = mt * kMTile + c;
-  const bool valid = row < a.M && row_real(a.mask, row);
-  const uint16_t* wp = (c < 8 ? a.wsg : a.wsu) + (size_t)(n0 + (c & 7)) * a.H + kq * 8;
-  const uint16_t* bp = a.x + (size_t)(valid ? row : 0) * a.H + kq * 8;
-  const v4f acc = bf16_full(wp, bp, valid, a.H / 32, kSegSG);
-  float u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[i], 32, 64);
-  if (kq < 2 && valid) {
-    const v4f h = {silu_mul(acc[0], u[0]), silu_mul(acc[1], u[1]), silu_mul(acc[2], u[2]), silu_mul(acc[3], u[3])};
-    store_bf16x4(a.hsh + (size_t)row * a.Is + n0 + kq * 4, h);
-  }
-}
-
-__global__ __launch_bounds__(256, 2) void k_gateup(FfnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int ntI = a.I / 8;
-  const int ntS = a.Is / 8;
-  const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntS : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntI;
-  const int t = wave_item();
-  if (t >= total) return;
-  if (t < n_sh) {
-    shared_gateup(a, t / ntS, t % ntS, lane);
-  } else {
-    const int tt = t - n_sh;
-    routed_gateup(a, routed_tile(a, tt / ntI), tt % ntI, lane);
-  }
 }
 
 // ---------------------------------------------------------------- gate/up (split small steps)
@@ -235,9 +157,8 @@ __global__ __launch_bounds__(512) void k_gateup_split(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- requantization
-// Routed h per (slot, 128-column block) for the slots in use.  Split steps
-// first sum the gate/up segment partials in order and form h = silu(G) U;
-// larger steps read h from hbuf.
+// Split steps: routed h per (slot, 128-column block) for the slots in use,
+// from the gate/up segment partials summed in order, h = silu(G) U.
 __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -246,77 +167,60 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
   const int b = (int)(item % nbI);
   if (slot >= a.sched[SCHED_SLOTS]) return;
   const int n = b * kBlk + 2 * lane;
-  float h0, h1;
-  if (a.split) {
-    const size_t st = (size_t)a.M * a.K * 2 * a.I;          // segment stride
-    const float* pg = a.part_gu + ((size_t)slot * 2 + 0) * a.I + n;
-    const float* pu = a.part_gu + ((size_t)slot * 2 + 1) * a.I + n;
-    float2 g = *reinterpret_cast<const float2*>(pg);
-    float2 u = *reinterpret_cast<const float2*>(pu);
-    for (int s = 1; s < kSegGU; ++s) {
-      const float2 gs = *reinterpret_cast<const float2*>(pg + s * st);
-      const float2 us = *reinterpret_cast<const float2*>(pu + s * st);
-      g.x = g.x + gs.x; g.y = g.y + gs.y;
-      u.x = u.x + us.x; u.y = u.y + us.y;
-    }
-    h0 = silu_mul(g.x, u.x);
-    h1 = silu_mul(g.y, u.y);
-  } else {
-    const float2 h = *reinterpret_cast<const float2*>(a.hbuf + (size_t)slot * a.I + n);
-    h0 = h.x;
-    h1 = h.y;
+  const size_t st = (size_t)a.M * a.K * 2 * a.I;            // segment stride
+  const float* pg = a.part_gu + ((size_t)slot * 2 + 0) * a.I + n;
+  const float* pu = a.part_gu + ((size_t)slot * 2 + 1) * a.I + n;
+  float2 g = *reinterpret_cast<const float2*>(pg);
+  float2 u = *reinterpret_cast<const float2*>(pu);
+  for (int s = 1; s < kSegGU; ++s) {
+    const float2 gs = *reinterpret_cast<const float2*>(pg + s * st);
+    const float2 us = *reinterpret_cast<const float2*>(pu + s * st);
+    g.x = g.x + gs.x; g.y = g.y + gs.y;
+    u.x = u.x + us.x; u.y = u.y + us.y;
   }
+  const float h0 = silu_mul(g.x, u.x);
+  const float h1 = silu_mul(g.y, u.y);
   quant_pair(h0, h1, a.hq + (size_t)slot * a.I + b * kBlk, a.hs + (size_t)slot * nbI + b, lane);
 }
 
-// ---------------------------------------------------------------- down
-// D[slot, n] (routed) and S[r, n] (shared) for 16 columns of H and one tile
-// of <= 16 slots / rows.  Split steps run one K segment per item and write
-// partials; larger steps run all segments in-wave.
+// ---------------------------------------------------------------- down (split small steps)
+// Per-segment items: D[slot, n] (routed) and S[r, n] (shared) partials for
+// 16 columns of H and one union expert's slots (at most kSmallRows), or the
+// step's rows for the shared expert.
+constexpr int kCols = 16;
+
 __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
-  const int ntH = a.H / 16;
-  const int nseg = a.split ? kSegDN : 1;
-  const int n_sh = (a.Is > 0) ? ((a.M + kMTile - 1) / kMTile) * ntH * nseg : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntH * nseg;
+  const int ntH = a.H / kCols;
+  const int n_sh = (a.Is > 0) ? ntH * kSegDN : 0;
+  const int total = n_sh + a.sched[SCHED_MTILES] * ntH * kSegDN;
   const int t = wave_item();
   if (t >= total) return;
   if (t < n_sh) {
-    const int seg = t % nseg, tt = t / nseg;
-    const int mt = tt / ntH, nt = tt % ntH;
-    const int row = mt * kMTile + c;
+    const int seg = t % kSegDN, nt = t / kSegDN;
+    const int row = c;
     const bool valid = row < a.M && row_real(a.mask, row);
-    const uint16_t* wp = a.wsd + (size_t)(nt * 16 + c) * a.Is + kq * 8;
+    const uint16_t* wp = a.wsd + (size_t)(nt * kCols + c) * a.Is + kq * 8;
     const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
     const int nst = a.Is / 32;
-    if (a.split) {
-      const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
-      if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * 16 + kq * 4, p);
-    } else {
-      const v4f s = bf16_full(wp, bp, valid, nst, kSegDN);
-      if (valid) store_f4(a.S + (size_t)row * a.H + nt * 16 + kq * 4, s);
-    }
+    const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
+    if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * kCols + kq * 4, p);
     return;
   }
   const int tt = t - n_sh;
-  const int seg = tt % nseg, it = tt / nseg;
+  const int seg = tt % kSegDN, it = tt / kSegDN;
   const Tile tl = routed_tile(a, it / ntH);
   const int nt = it % ntH;
   const int slot = c < tl.mcnt ? tl.s0 + c : -1;
   const int nkb = a.I / kBlk;
-  const uint8_t* wp = a.wd + ((size_t)tl.e * a.H + nt * 16 + c) * a.I + kq * 32;
-  const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * 16) / kBlk) * nkb;
+  const uint8_t* wp = a.wd + ((size_t)tl.e * a.H + nt * kCols + c) * a.I + kq * 32;
+  const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * kCols) / kBlk) * nkb;
   const uint8_t* bp = a.hq + (size_t)(slot < 0 ? 0 : slot) * a.I + kq * 32;
   const float* shp = a.hs + (size_t)(slot < 0 ? 0 : slot) * nkb;
-  if (a.split) {
-    const v4f p = fp8_chain<false>(wp, swp, bp, shp, slot >= 0, seg_begin(nkb, seg, kSegDN),
-                                   seg_begin(nkb, seg + 1, kSegDN));
-    if (slot >= 0) store_f4(a.part_d + ((size_t)seg * a.M * a.K + slot) * a.H + nt * 16 + kq * 4, p);
-  } else {
-    const v4f d = fp8_full<false>(wp, swp, bp, shp, slot >= 0, nkb, kSegDN);
-    if (slot >= 0) store_f4(a.D + (size_t)slot * a.H + nt * 16 + kq * 4, d);
-  }
+  const v4f p = fp8_chain<false>(wp, swp, bp, shp, slot >= 0, seg_begin(nkb, seg, kSegDN),
+                                 seg_begin(nkb, seg + 1, kSegDN));
+  if (slot >= 0) store_f4(a.part_d + ((size_t)seg * a.M * a.K + slot) * a.H + nt * kCols + kq * 4, p);
 }
 
 // ---------------------------------------------------------------- combine
@@ -408,24 +312,22 @@ bool use_split(int M, int H) { return M <= kSmallRows && split_lds_bytes(M, H) <
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const int with_shared = a.Is > 0 ? 1 : 0;
-  // column tiles of <= 16 slots: one per expert for M <= 16, else at most
-  // ceil(M*K/16) + (union size)
   const long max_union = std::min<long>(a.E, (long)a.M * a.K);
-  const long mtiles_max = a.M <= kMTile ? max_union : ((long)a.M * a.K + kMTile - 1) / kMTile + max_union;
-  const long sh_tiles = with_shared ? (a.M + kMTile - 1) / kMTile : 0;
   if (a.split) {
-    // the shared expert's gate/up ran in the front launch
+    // one slot tile per union expert; the shared expert's gate/up ran in the front launch
     const long items = max_union * (a.I / 8) * kSegGU;
     MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)((items + 7) / 8)), dim3(512), split_lds_bytes(a.M, a.H), s,
                a);
+    const long post_waves = (long)a.M * a.K * (a.I / kBlk);
+    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)((post_waves + 3) / 4)), dim3(256), 0, s, a);
+    const long dn_items = ((with_shared ? 1 : 0) + max_union) * (a.H / kCols) * kSegDN;
+    MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)((dn_items + 3) / 4)), dim3(256), 0, s, a);
   } else {
-    const long gu_items = sh_tiles * (a.Is / 8) + mtiles_max * (a.I / 8);
-    MOE_LAUNCH(KID_GATEUP, k_gateup, dim3((unsigned)((gu_items + 3) / 4)), dim3(256), 0, s, a);
+    // slot tiles: at most ceil(M*K / kMTile) + (union size), one partial tile per expert
+    const long mtiles_max = ((long)a.M * a.K + kMTile - 1) / kMTile + max_union;
+    const hipError_t e = launch_tiled(a, mtiles_max, s);
+    if (e != hipSuccess) return e;
   }
-  const long post_waves = (long)a.M * a.K * (a.I / kBlk);
-  MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)((post_waves + 3) / 4)), dim3(256), 0, s, a);
-  const long dn_items = (sh_tiles + mtiles_max) * (a.H / 16) * (a.split ? kSegDN : 1);
-  MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)((dn_items + 3) / 4)), dim3(256), 0, s, a);
   const long threads = (long)a.M * (a.H / 4);
   MOE_LAUNCH(KID_COMBINE, k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, with_shared);
   return hipSuccess;

@@ -159,4 +159,27 @@ __device__ __forceinline__ v4f bf16_full(const uint16_t* wp, const uint16_t* bp,
   return tot;
 }
 
+// ---------------------------------------------------------------- slot tiles
+// A tile of <= kMTile consecutive slots of one union expert.  Tiles are
+// numbered expert by expert (mtile_offs[u] = first tile of union expert u).
+struct Tile {
+  int e;       // expert id
+  int s0;      // first slot of the tile
+  int mcnt;    // slots in the tile (<= kMTile)
+};
+
+__device__ __forceinline__ Tile routed_tile(const FfnArgs& a, int mtg) {
+  const int nu = a.sched[SCHED_NUNION];
+  int lo = 0, hi = nu - 1;          // largest u with mtile_offs[u] <= mtg
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.mtile_offs[mid] <= mtg) lo = mid; else hi = mid - 1;
+  }
+  Tile t;
+  t.e = a.union_ids[lo];
+  t.s0 = a.offs[lo] + (mtg - a.mtile_offs[lo]) * kMTile;
+  t.mcnt = min(kMTile, a.offs[lo + 1] - t.s0);
+  return t;
+}
+
 }  // namespace moe

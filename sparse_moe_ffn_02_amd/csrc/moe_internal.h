@@ -7,7 +7,7 @@
 
 namespace moe {
 
-constexpr int kMTile = 16;          // slots (or rows) per MFMA column tile
+constexpr int kMTile = 128;          // slots (or rows) per tile of the tiled grouped GEMMs
 constexpr int kDecodeMaxRows = 16;  // rows served by the small-step router kernels
 constexpr int kSmallRows = 8;       // rows served by the split small-step expert kernels
 // Every GEMM element is the fixed-order sum of its K-segment chains:
@@ -63,7 +63,6 @@ struct FfnArgs {
   int32_t* sched;
   int32_t* mtile_offs;
   uint8_t* xq; float* xs;  // [M, H], [M, H/128]
-  float* hbuf;             // [M*K, I]
   uint8_t* hq; float* hs;  // [M*K, I], [M*K, I/128]
   uint16_t* hsh;           // [M, Is] bf16 shared h
   float* S;                // [M, H]
@@ -103,6 +102,8 @@ hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t 
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prep(const FfnArgs& a, hipStream_t s);   // quantize x
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// steps that do not take the split path: tiled gate/up (+ SiLU, requant) and down
+hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s);
 bool use_split(int M, int H);   // M <= kSmallRows and the x codes fit the LDS budget
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);

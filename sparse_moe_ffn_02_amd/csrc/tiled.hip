@@ -1,0 +1,421 @@
+// Tiled grouped GEMMs for steps that do not take the split small-step path.
+//
+// A workgroup of eight waves computes one tile of kTM = 128 slots (routed
+// experts) or rows (shared expert) by the tile's output columns:
+//   gate/up: 128 h columns, i.e. 128 gate rows and 128 up rows of the weights;
+//   down:    256 columns of H.
+// Each wave owns 32 weight rows (two 16-row MFMA tiles; for gate/up the gate
+// and the up rows of the same 16 h columns), streams them from global memory
+// straight into MFMA operand registers two K stages ahead, and applies them to
+// all 128 slots (eight 16-column MFMA tiles).  The tile's activation rows,
+// which all eight waves read, are staged through a double-buffered LDS ring.
+// The weight rows of one (expert, column tile) are shared by the expert's
+// slot tiles; their blocks are numbered so that they land on the same XCD
+// (blocks are dealt to the 8 XCDs round-robin and the column-tile count is a
+// multiple of 8), where the L2 serves the re-reads.
+//
+// Every output element follows the same procedure as in the small-step
+// kernels: one fp8 16x16x128 MFMA per 128-deep K-block scaled into a fp32
+// chain (or bf16 16x16x32 MFMAs accumulating in the chain), one chain per K
+// segment, segments added in order.  So a row's bits do not depend on the
+// tile, the tile shape or the other rows of the step.  The gate/up epilogue
+// forms h = silu(G) U and requantizes each 1x128 block of h (the block is the
+// tile's column range); the shared-expert epilogue rounds h to bf16.
+#include "moe_chains.h"
+
+namespace moe {
+
+constexpr int kTM = kMTile;                // slots (rows) per tile
+constexpr int kStageBytes = 128;           // bytes of one row per K stage
+constexpr int kLdsRow = kStageBytes + 16;  // padded LDS row: the 16 lanes of a fragment read hit distinct banks
+constexpr int kWaves = 8;
+constexpr int kTileThreads = 64 * kWaves;
+constexpr int kNA = 2;                     // 16-row weight tiles per wave
+constexpr int kNB = kTM / 16;              // 16-column slot tiles per wave
+constexpr int kBPart = kStageBytes * kTM / kTileThreads;   // activation bytes per thread per stage
+constexpr int kBVec = kBPart / 16;         // 16-byte loads per thread per stage
+constexpr int kBParts = kStageBytes / kBPart;              // threads per activation row
+constexpr int kRingA = 2;                  // weight stages in flight per wave
+
+struct TileIn {
+  const uint8_t* a[kNA]; // per lane: weight row of each of the wave's A tiles, at K byte 0
+  const float* sw[kNA];  // fp8: weight scales of each A tile, indexed by K-block
+  const uint8_t* b;      // per thread: its kBPart-byte part of activation row tid / kBParts; null = zeros
+  const float* bs;       // fp8, threads < kTM: activation scales of row tid, indexed by K-block; null = zeros
+  int nstage;            // K stages of 128 bytes
+  int nseg;              // K segments (fp8: over K-blocks; bf16: over 32-deep K steps)
+  bool on;               // wave has rows in range
+};
+
+struct TileLds {
+  uint8_t b[2][kTM * kLdsRow];
+  float s[2][kTM];
+};
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <bool kFp8>
+__device__ __forceinline__ void load_a(v8i (&dst)[kNA], const TileIn& in, int st, int q) {
+#pragma unroll
+  for (int t = 0; t < kNA; ++t) {
+    const uint8_t* p = in.a[t] + (size_t)st * kStageBytes;
+    uint4 lo, hi;
+    if (kFp8) {
+      lo = ld16(p + q * 32);
+      hi = ld16(p + q * 32 + 16);
+    } else {                         // two 32-deep bf16 steps: 16 bytes each
+      lo = ld16(p + q * 16);
+      hi = ld16(p + 64 + q * 16);
+    }
+    v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    dst[t] = r;
+  }
+}
+
+struct BStage {
+  uint4 v[kBVec];
+  float s;
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void load_b(BStage& r, const TileIn& in, int st) {
+#pragma unroll
+  for (int i = 0; i < kBVec; ++i)
+    r.v[i] = in.b ? ld16(in.b + (size_t)st * kStageBytes + 16 * i) : make_uint4(0, 0, 0, 0);
+  if (kFp8) r.s = in.bs ? in.bs[st] : 0.0f;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void store_b(TileLds& L, int buf, const BStage& r) {
+  const int tid = threadIdx.x;
+  uint8_t* d = &L.b[buf][(tid / kBParts) * kLdsRow + (tid % kBParts) * kBPart];
+#pragma unroll
+  for (int i = 0; i < kBVec; ++i) *reinterpret_cast<uint4*>(d + 16 * i) = r.v[i];
+  if (kFp8 && tid < kTM) L.s[buf][tid] = r.s;
+}
+
+// All four results of a group of MFMAs wait out the MFMA latency together
+// before any vector-ALU read (see settle_fp8).
+__device__ __forceinline__ void settle4(v4f& p0, v4f& p1, v4f& p2, v4f& p3) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p0), "+v"(p1), "+v"(p2), "+v"(p3));
+}
+
+__device__ __forceinline__ v4f mfma_fp8_raw(const v8i& a, const v8i& b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+struct SegState {
+  int seg, end, nunits, nseg;
+};
+
+using Acc = v4f[kNA][kNB];
+
+// Close every K segment that ends at or before `done` units: tot = acc for
+// the first segment, tot = tot + acc after it.  Further segments ending at the
+// same point are empty and add zeros (tot + 0, once: repeats change nothing).
+// The loops over the arrays stay free of data-dependent trip counts so that
+// acc and tot stay in registers.
+template <bool kFp8>
+__device__ __forceinline__ void close_segments(SegState& g, int done, Acc& acc, Acc& tot) {
+  if (g.seg >= g.nseg || g.end > done) return;
+  const bool first = g.seg == 0;
+#pragma unroll
+  for (int t = 0; t < kNA; ++t)
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const v4f v = kFp8 ? acc[t][b] : settle_bf16(acc[t][b]);
+      tot[t][b] = first ? v : add4(tot[t][b], v);
+      acc[t][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  ++g.seg;
+  g.end = seg_begin(g.nunits, g.seg + 1, g.nseg);
+  bool empty = false;
+  while (g.seg < g.nseg && g.end <= done) {
+    ++g.seg;
+    g.end = seg_begin(g.nunits, g.seg + 1, g.nseg);
+    empty = true;
+  }
+  if (empty) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kNA; ++t)
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) tot[t][b] = add4(tot[t][b], z);
+  }
+}
+
+// One K stage on LDS buffer `buf` with A fragments `a`.
+template <bool kFp8>
+__device__ __forceinline__ void tile_stage(const TileIn& in, const TileLds& L, int buf, const v8i (&a)[kNA], int st,
+                                           Acc& acc, Acc& tot, SegState& g) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  if (kFp8) {
+    const float sw0 = in.sw[0][st], sw1 = in.sw[1][st];
+#pragma unroll
+    for (int b = 0; b < kNB; b += 2) {
+      v8i xb[2];
+      float sx[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint8_t* src = &L.b[buf][(16 * (b + j) + c) * kLdsRow + q * 32];
+        const uint4 lo = ld16(src), hi = ld16(src + 16);
+        xb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sx[j] = L.s[buf][16 * (b + j) + c];
+      }
+      v4f p0 = mfma_fp8_raw(a[0], xb[0]), p1 = mfma_fp8_raw(a[1], xb[0]);
+      v4f p2 = mfma_fp8_raw(a[0], xb[1]), p3 = mfma_fp8_raw(a[1], xb[1]);
+      settle4(p0, p1, p2, p3);
+      scale_acc(acc[0][b], p0, sx[0], sw0);
+      scale_acc(acc[1][b], p1, sx[0], sw1);
+      scale_acc(acc[0][b + 1], p2, sx[1], sw0);
+      scale_acc(acc[1][b + 1], p3, sx[1], sw1);
+      __builtin_amdgcn_sched_barrier(0);     // keep one pair of slot tiles' operands live at a time
+    }
+    close_segments<true>(g, st + 1, acc, tot);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const uint4 xv = ld16(&L.b[buf][(16 * b + c) * kLdsRow + j * 64 + q * 16]);
+        const v4i xb = {(int)xv.x, (int)xv.y, (int)xv.z, (int)xv.w};
+#pragma unroll
+        for (int t = 0; t < kNA; ++t) {
+          const v4i ah = {a[t][4 * j], a[t][4 * j + 1], a[t][4 * j + 2], a[t][4 * j + 3]};
+          acc[t][b] = mfma_bf16_k32(ah, xb, acc[t][b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      close_segments<false>(g, 2 * st + j + 1, acc, tot);
+    }
+  }
+}
+
+// The K loop of one tile: tot[t][b] = the element values of A tile t by slot
+// tile b (lane layout of the 16x16 MFMA output).  Weight fragments are loaded
+// kRingA stages ahead into registers; activation rows two stages ahead into
+// registers, then into the LDS double buffer one stage ahead.  The stage loop
+// is unrolled by kRingA so every ring index is a compile-time constant.
+template <bool kFp8>
+__device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
+  const int q = (threadIdx.x & 63) >> 4;
+  Acc acc;
+#pragma unroll
+  for (int t = 0; t < kNA; ++t)
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      acc[t][b] = v4f{0.f, 0.f, 0.f, 0.f};
+      tot[t][b] = acc[t][b];
+    }
+  SegState g;
+  g.seg = 0;
+  g.nseg = in.nseg;
+  g.nunits = kFp8 ? in.nstage : 2 * in.nstage;
+  g.end = seg_begin(g.nunits, 1, g.nseg);
+  close_segments<kFp8>(g, 0, acc, tot);
+  const int n = in.nstage;
+  v8i ar[kRingA][kNA];
+  BStage br[2];
+#pragma unroll
+  for (int u = 0; u < kRingA; ++u)
+    if (in.on && u < n) load_a<kFp8>(ar[u], in, u, q);
+  load_b<kFp8>(br[0], in, 0);
+  store_b<kFp8>(L, 0, br[0]);
+  if (1 < n) load_b<kFp8>(br[1], in, 1);
+  if (2 < n) load_b<kFp8>(br[0], in, 2);
+  __syncthreads();
+  for (int st0 = 0; st0 < n; st0 += kRingA) {
+#pragma unroll
+    for (int u = 0; u < kRingA; ++u) {
+      const int st = st0 + u;
+      if (st >= n) break;
+      if (in.on) tile_stage<kFp8>(in, L, u & 1, ar[u], st, acc, tot, g);
+      if (in.on && st + kRingA < n) load_a<kFp8>(ar[u], in, st + kRingA, q);
+      if (st + 1 < n) store_b<kFp8>(L, (u + 1) & 1, br[(u + 1) & 1]);      // stage st + 1
+      if (st + 3 < n) load_b<kFp8>(br[(u + 1) & 1], in, st + 3);          // stored two stages later
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- gate/up
+// Blocks [0, n_sh): shared-expert tiles (row tile, 128-column tile); then
+// routed tiles (slot tile of one expert, 128-column tile).  Wave w holds the
+// gate (A tile 0) and up (A tile 1) rows of h columns n0 + 16 w .. + 15.
+__global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
+  __shared__ TileLds L;
+  __shared__ float samax[kWaves][kTM];
+  const int ntI = a.I / kBlk, ntS = a.Is / kBlk;
+  const int n_sh = a.Is > 0 ? ((a.M + kTM - 1) / kTM) * ntS : 0;
+  const int total = n_sh + a.sched[SCHED_MTILES] * ntI;
+  const int bid = blockIdx.x;
+  if (bid >= total) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  Acc tot;
+  if (bid < n_sh) {
+    const int mt = bid / ntS, nt = bid % ntS;
+    const int n0 = nt * kBlk + 16 * w;                 // wave's first h column
+    TileIn in;
+    in.a[0] = reinterpret_cast<const uint8_t*>(a.wsg + (size_t)(n0 + c) * a.H);
+    in.a[1] = reinterpret_cast<const uint8_t*>(a.wsu + (size_t)(n0 + c) * a.H);
+    in.sw[0] = in.sw[1] = nullptr;
+    const int brow = mt * kTM + tid / kBParts;
+    const bool bvalid = brow < a.M && row_real(a.mask, brow);
+    in.b = bvalid ? reinterpret_cast<const uint8_t*>(a.x + (size_t)brow * a.H) + (tid % kBParts) * kBPart : nullptr;
+    in.bs = nullptr;
+    in.nstage = a.H * 2 / kStageBytes;
+    in.nseg = kSegSG;
+    in.on = true;
+    tile_gemm<false>(in, L, tot);
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int row = mt * kTM + 16 * b + c;
+      if (row >= a.M || !row_real(a.mask, row)) continue;
+      const v4f h = {silu_mul(tot[0][b][0], tot[1][b][0]), silu_mul(tot[0][b][1], tot[1][b][1]),
+                     silu_mul(tot[0][b][2], tot[1][b][2]), silu_mul(tot[0][b][3], tot[1][b][3])};
+      store_bf16x4(a.hsh + (size_t)row * a.Is + n0 + 4 * q, h);
+    }
+    return;
+  }
+  const int rb = bid - n_sh;
+  const int nt = rb % ntI;
+  const Tile tl = routed_tile(a, rb / ntI);
+  const int n0 = nt * kBlk + 16 * w;
+  const int nkb = a.H / kBlk;
+  TileIn in;
+  in.a[0] = a.wg + ((size_t)tl.e * a.I + n0 + c) * a.H;
+  in.a[1] = a.wu + ((size_t)tl.e * a.I + n0 + c) * a.H;
+  in.sw[0] = a.sg + ((size_t)tl.e * ntI + nt) * nkb;
+  in.sw[1] = a.su + ((size_t)tl.e * ntI + nt) * nkb;
+  {
+    const int i = tid / kBParts;
+    const int row = i < tl.mcnt ? a.rows[tl.s0 + i] : -1;
+    in.b = (row >= 0 && row < a.M) ? a.xq + (size_t)row * a.H + (tid % kBParts) * kBPart : nullptr;
+    const int rs = (tid < kTM && tid < tl.mcnt) ? a.rows[tl.s0 + tid] : -1;
+    in.bs = (rs >= 0 && rs < a.M) ? a.xs + (size_t)rs * nkb : nullptr;
+  }
+  in.nstage = nkb;
+  in.nseg = kSegGU;
+  in.on = true;
+  tile_gemm<true>(in, L, tot);
+  // h = silu(G) U in place of G; 1x128 requantization over the tile's 128 columns
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tot[0][b][i] = silu_mul(tot[0][b][i], tot[1][b][i]);
+      m = fmaxf(m, fabsf(tot[0][b][i]));
+    }
+    // max over the four lanes of the same column (xor 16, xor 32)
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(m, fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1])));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(m, fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])));
+    if (q == 0) samax[w][16 * b + c] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    const int i = 16 * b + c;
+    if (i >= tl.mcnt) continue;
+    const int slot = tl.s0 + i;
+    float amax = samax[0][i];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) amax = fmaxf(amax, samax[v][i]);
+    const float s = quant_scale(amax);
+    uint32_t word = 0;
+    if (amax != 0.0f)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) word |= quant_code(tot[0][b][k], s) << (8 * k);
+    *reinterpret_cast<uint32_t*>(a.hq + (size_t)slot * a.I + n0 + 4 * q) = word;
+    if (w == 0 && q == 0) a.hs[(size_t)slot * ntI + nt] = s;
+  }
+}
+
+// ---------------------------------------------------------------- down
+// Blocks [0, n_sh): shared-expert tiles (row tile, 256-column tile of H);
+// then routed tiles (slot tile of one expert, 256-column tile).  Wave w holds
+// output columns n0 + 32 w .. + 31 (A tiles 0 and 1).
+constexpr int kDnCols = 32 * kWaves;
+
+__global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
+  __shared__ TileLds L;
+  const int ntH = (a.H + kDnCols - 1) / kDnCols;
+  const int n_sh = a.Is > 0 ? ((a.M + kTM - 1) / kTM) * ntH : 0;
+  const int total = n_sh + a.sched[SCHED_MTILES] * ntH;
+  const int bid = blockIdx.x;
+  if (bid >= total) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  Acc tot;
+  if (bid < n_sh) {
+    const int mt = bid / ntH, nt = bid % ntH;
+    const int n0 = nt * kDnCols + 32 * w;
+    TileIn in;
+    in.on = true;                                   // waves past H compute on in-range rows, store nothing
+    const int nr = n0 < a.H ? n0 : a.H - 32;
+#pragma unroll
+    for (int t = 0; t < kNA; ++t) {
+      in.a[t] = reinterpret_cast<const uint8_t*>(a.wsd + (size_t)(nr + 16 * t + c) * a.Is);
+      in.sw[t] = nullptr;
+    }
+    const int brow = mt * kTM + tid / kBParts;
+    const bool bvalid = brow < a.M && row_real(a.mask, brow);
+    in.b = bvalid ? reinterpret_cast<const uint8_t*>(a.hsh + (size_t)brow * a.Is) + (tid % kBParts) * kBPart : nullptr;
+    in.bs = nullptr;
+    in.nstage = a.Is * 2 / kStageBytes;
+    in.nseg = kSegDN;
+    tile_gemm<false>(in, L, tot);
+    if (n0 >= a.H) return;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int row = mt * kTM + 16 * b + c;
+      if (row >= a.M || !row_real(a.mask, row)) continue;
+#pragma unroll
+      for (int t = 0; t < kNA; ++t) store_f4(a.S + (size_t)row * a.H + n0 + 16 * t + 4 * q, tot[t][b]);
+    }
+    return;
+  }
+  const int rb = bid - n_sh;
+  const int nt = rb % ntH;
+  const Tile tl = routed_tile(a, rb / ntH);
+  const int n0 = nt * kDnCols + 32 * w;
+  const int nkb = a.I / kBlk;
+  TileIn in;
+  in.on = true;
+  const int nr = n0 < a.H ? n0 : a.H - 32;
+#pragma unroll
+  for (int t = 0; t < kNA; ++t) {
+    in.a[t] = a.wd + ((size_t)tl.e * a.H + nr + 16 * t + c) * a.I;
+    in.sw[t] = a.sd + ((size_t)tl.e * (a.H / kBlk) + nr / kBlk) * nkb;
+  }
+  {
+    const int i = tid / kBParts;
+    in.b = i < tl.mcnt ? a.hq + (size_t)(tl.s0 + i) * a.I + (tid % kBParts) * kBPart : nullptr;
+    in.bs = (tid < kTM && tid < tl.mcnt) ? a.hs + (size_t)(tl.s0 + tid) * nkb : nullptr;
+  }
+  in.nstage = nkb;
+  in.nseg = kSegDN;
+  tile_gemm<true>(in, L, tot);
+  if (n0 >= a.H) return;
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    const int i = 16 * b + c;
+    if (i >= tl.mcnt) continue;
+#pragma unroll
+    for (int t = 0; t < kNA; ++t) store_f4(a.D + (size_t)(tl.s0 + i) * a.H + n0 + 16 * t + 4 * q, tot[t][b]);
+  }
+}
+
+hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s) {
+  const long sh_tiles = a.Is > 0 ? (a.M + kTM - 1) / kTM : 0;
+  const long gu = sh_tiles * (a.Is / kBlk) + mtiles_max * (a.I / kBlk);
+  MOE_LAUNCH(KID_GATEUP, k_gateup_tiled, dim3((unsigned)gu), dim3(kTileThreads), 0, s, a);
+  const long ntH = (a.H + kDnCols - 1) / kDnCols;
+  const long dn = (sh_tiles + mtiles_max) * ntH;
+  MOE_LAUNCH(KID_DOWN, k_down_tiled, dim3((unsigned)dn), dim3(kTileThreads), 0, s, a);
+  return hipSuccess;
+}
+
+}  // namespace moe
