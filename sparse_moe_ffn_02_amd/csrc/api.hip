@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t sched, mtile, logits, sig, rowbits, xq, xs, hq, hs, hsh, S, D, part_gu, part_sh, part_d, part_s, total;
+  size_t sched, mtile, ucount, logits, sig, rowbits, xq, xs, hq, hs, hsh, S, D, part_gu, part_sh, part_d, part_s, total;
   bool split;
 };
 
@@ -32,6 +32,7 @@ Layout make_layout(const moe_dims& d, int M) {
   const size_t m = (size_t)M, H = d.hidden, E = d.n_experts, K = d.top_k, I = d.inter, Is = d.shared_inter;
   L.sched = take(SCHED_WORDS * sizeof(int32_t));
   L.mtile = take((E + 1) * sizeof(int32_t));
+  L.ucount = take(kUChunks * E * sizeof(int32_t));
   L.logits = take(m * E * sizeof(double));
   L.sig = take(m * E * sizeof(double));
   L.rowbits = take(m * ((E + 31) / 32) * sizeof(uint32_t));
@@ -123,6 +124,7 @@ RouteArgs route_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t*
   a.slot_of = out.slot_of;
   a.sched = reinterpret_cast<int32_t*>(ws + L.sched);
   a.mtile_offs = reinterpret_cast<int32_t*>(ws + L.mtile);
+  a.ucount = reinterpret_cast<int32_t*>(ws + L.ucount);
   return a;
 }
 

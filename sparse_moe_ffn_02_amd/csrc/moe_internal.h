@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kMTile = 128;          // slots (or rows) per tile of the tiled grouped GEMMs
 constexpr int kDecodeMaxRows = 16;  // rows served by the small-step router kernels
 constexpr int kSmallRows = 8;       // rows served by the split small-step expert kernels
+constexpr int kUChunks = 64;        // row chunks of the larger-step union
 // Every GEMM element is the fixed-order sum of its K-segment chains:
 // routed gate/up over kSegGU segments of K = H, shared gate/up over kSegSG,
 // routed and shared down over kSegDN segments of K = I.  Small steps run each segment as its own work
@@ -40,6 +41,7 @@ struct RouteArgs {
   int32_t* slot_of;        // [M, K]
   int32_t* sched;          // ws [SCHED_WORDS]
   int32_t* mtile_offs;     // ws [E + 1]
+  int32_t* ucount;         // ws [kUChunks, E] per row-chunk counts, then first slots (larger steps)
 };
 
 struct FfnArgs {

@@ -180,77 +180,104 @@ __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- union
-// One workgroup.  Counts per expert, the ascending union with its slot
-// offsets and column-tile offsets, then each expert's rows in ascending row
-// order (ballot + prefix popcount), and slot_of[r, j] for every (row, pick).
-__global__ __launch_bounds__(1024) void k_union(RouteArgs a) {
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int base[kMaxExperts];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
+// Larger steps: the rows are cut into kUChunks chunks.  (1) per chunk and
+// expert, the number of rows that picked the expert; (2) one workgroup turns
+// the counts into each chunk's first slot per expert, the ascending union
+// with its slot and tile offsets; (3) per chunk and expert, the chunk's rows
+// that picked the expert are written in ascending row order from that first
+// slot, with slot_of[r, j] (j = the pick's position among the row's ascending
+// ids).  The result is the same as one ordered pass over all rows.
+__device__ __forceinline__ int chunk_rows(int M) { return (M + kUChunks - 1) / kUChunks; }
+
+__global__ __launch_bounds__(kMaxExperts) void k_union_count(RouteArgs a) {
+  const int c = blockIdx.x, e = threadIdx.x;
+  if (e >= a.E) return;
   const int nwords = (a.E + 31) / 32;
-  for (int e = tid; e < a.E; e += blockDim.x) cnt[e] = 0;
+  const int cr = chunk_rows(a.M);
+  const int r0 = c * cr, r1 = min(a.M, r0 + cr);
+  const uint32_t bit = 1u << (e & 31);
+  int n = 0;
+  for (int r = r0; r < r1; ++r) n += (a.rowbits[(size_t)r * nwords + (e >> 5)] & bit) ? 1 : 0;
+  a.ucount[(size_t)c * a.E + e] = n;
+}
+
+// Inclusive scan over a workgroup of kMaxExperts threads (4 waves).
+__device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v, lane);
+  if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  for (int r = tid; r < a.M; r += blockDim.x) {
-    const bool real = (a.mask == nullptr || a.mask[r] != 0);
-    for (int j = 0; j < a.K; ++j) {
-      if (real) {
-        const int e = a.ids[(size_t)r * a.K + j];
-        if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);
-      } else {
-        a.slot_of[(size_t)r * a.K + j] = -1;
-      }
-    }
+  uint32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += tmp[w];
+  __syncthreads();
+  return x + before;
+}
+
+__global__ __launch_bounds__(kMaxExperts) void k_union_scan(RouteArgs a) {
+  __shared__ uint32_t tmp[4];
+  __shared__ uint32_t tot[2];
+  const int e = threadIdx.x;
+  const bool ok = e < a.E;
+  // per-expert exclusive prefix over the chunks (kept in registers)
+  int pre[kUChunks];
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < kUChunks; ++c) {
+    pre[c] = n;
+    n += ok ? a.ucount[(size_t)c * a.E + e] : 0;
+  }
+  // across experts: first slot (32-bit scan) and union index | first tile (packed scan)
+  const uint32_t nt = (uint32_t)((n + kMTile - 1) / kMTile);
+  const uint32_t v1 = (uint32_t)n;
+  const uint32_t v2 = (n > 0 ? 1u : 0u) | (nt << 16);
+  const uint32_t i1 = block_incl_scan256(v1, tmp);
+  const uint32_t i2 = block_incl_scan256(v2, tmp);
+  const int off = (int)(i1 - v1);
+  const int uidx = (int)((i2 - v2) & 0xFFFFu), mto = (int)((i2 - v2) >> 16);
+  if (ok && n > 0) {
+    a.union_ids[uidx] = e;
+    a.offs[uidx] = off;
+    a.mtile_offs[uidx] = mto;
+  }
+  if (ok) {
+#pragma unroll
+    for (int c = 0; c < kUChunks; ++c) a.ucount[(size_t)c * a.E + e] = off + pre[c];
+  }
+  if (e == kMaxExperts - 1) {
+    tot[0] = i1;
+    tot[1] = i2;
   }
   __syncthreads();
-  if (tid == 0) {
-    int nu = 0, acc = 0, mt = 0;
-    for (int e = 0; e < a.E; ++e) {
-      const int n = cnt[e];
-      base[e] = acc;
-      if (n) {
-        a.union_ids[nu] = e;
-        a.offs[nu] = acc;
-        a.mtile_offs[nu] = mt;
-        ++nu;
-        acc += n;
-        mt += (n + kMTile - 1) / kMTile;
-      }
-    }
-    a.offs[nu] = acc;
-    a.mtile_offs[nu] = mt;
+  if (e == 0) {
+    const int nu = (int)(tot[1] & 0xFFFFu), total_mt = (int)(tot[1] >> 16), total = (int)tot[0];
+    a.offs[nu] = total;
+    a.mtile_offs[nu] = total_mt;
     *a.n_union = nu;
     a.sched[SCHED_NUNION] = nu;
-    a.sched[SCHED_MTILES] = mt;
-    a.sched[SCHED_SLOTS] = acc;
+    a.sched[SCHED_MTILES] = total_mt;
+    a.sched[SCHED_SLOTS] = total;
     a.sched[SCHED_BAD] = 0;
   }
-  __syncthreads();
-  for (int e = wave; e < a.E; e += nwaves) {
-    if (cnt[e] == 0) continue;
-    int b = base[e];
-    const int wi = e >> 5;
-    const uint32_t bit = 1u << (e & 31);
-    for (int r0 = 0; r0 < a.M; r0 += 64) {
-      const int r = r0 + lane;
-      bool hit = false;
-      uint32_t word = 0;
-      if (r < a.M) {
-        word = a.rowbits[(size_t)r * nwords + wi];
-        hit = (word & bit) != 0;
-      }
-      const uint64_t m = __ballot(hit);
-      if (hit) {
-        const int p = b + __popcll(m & ((1ull << lane) - 1ull));
-        a.rows[p] = r;
-        int j = __popc(word & (bit - 1u));
-        for (int w2 = 0; w2 < wi; ++w2) j += __popc(a.rowbits[(size_t)r * nwords + w2]);
-        a.slot_of[(size_t)r * a.K + j] = p;
-      }
-      b += __popcll(m);
-    }
+}
+
+__global__ __launch_bounds__(kMaxExperts) void k_union_scatter(RouteArgs a) {
+  const int c = blockIdx.x, e = threadIdx.x;
+  if (e >= a.E) return;
+  const int nwords = (a.E + 31) / 32;
+  const int cr = chunk_rows(a.M);
+  const int r0 = c * cr, r1 = min(a.M, r0 + cr);
+  const int wi = e >> 5;
+  const uint32_t bit = 1u << (e & 31);
+  int slot = a.ucount[(size_t)c * a.E + e];
+  for (int r = r0; r < r1; ++r) {
+    const uint32_t* rb = a.rowbits + (size_t)r * nwords;
+    const uint32_t word = rb[wi];
+    if (!(word & bit)) continue;
+    int j = __popc(word & (bit - 1u));
+    for (int w2 = 0; w2 < wi; ++w2) j += __popc(rb[w2]);
+    a.rows[slot] = r;
+    a.slot_of[(size_t)r * a.K + j] = slot;
+    ++slot;
   }
 }
 
@@ -509,7 +536,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   }
   MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((a.M + 7) / 8, (a.E + 15) / 16), blk, 0, s, a);
   MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
-  MOE_LAUNCH(KID_UNION, k_union, dim3(1), dim3(1024), 0, s, a);
+  MOE_LAUNCH(KID_UNION, k_union_count, dim3(kUChunks), dim3(kMaxExperts), 0, s, a);
+  MOE_LAUNCH(KID_UNION, k_union_scan, dim3(1), dim3(kMaxExperts), 0, s, a);
+  MOE_LAUNCH(KID_UNION, k_union_scatter, dim3(kUChunks), dim3(kMaxExperts), 0, s, a);
   return hipSuccess;
 }
 
