@@ -35,16 +35,17 @@ constexpr int kNB = kTM / 16;              // 16-column slot tiles per wave
 constexpr int kBPart = kStageBytes * kTM / kTileThreads;   // activation bytes per thread per stage
 constexpr int kBVec = kBPart / 16;         // 16-byte loads per thread per stage
 constexpr int kBParts = kStageBytes / kBPart;              // threads per activation row
-constexpr int kRingA = 2;                  // weight stages in flight per wave
+constexpr int kRingA = 2;                  // weight stages in flight per wave (the loop below assumes 2)
 
 struct TileIn {
   const uint8_t* a[kNA]; // per lane: weight row of each of the wave's A tiles, at K byte 0
   const float* sw[kNA];  // fp8: weight scales of each A tile, indexed by K-block
-  const uint8_t* b;      // per thread: its kBPart-byte part of activation row tid / kBParts; null = zeros
-  const float* bs;       // fp8, threads < kTM: activation scales of row tid, indexed by K-block; null = zeros
+  const uint8_t* b;      // per thread: its kBPart-byte part of activation row tid / kBParts (always a valid row)
+  const float* bs;       // fp8: activation scales of row tid (threads < kTM), indexed by K-block (always valid)
+  bool bok;              // the thread's activation row is real (else it contributes zeros)
+  bool bsok;             // the thread's scale row is real (else zero)
   int nstage;            // K stages of 128 bytes
   int nseg;              // K segments (fp8: over K-blocks; bf16: over 32-deep K steps)
-  bool on;               // wave has rows in range
 };
 
 struct TileLds {
@@ -54,10 +55,17 @@ struct TileLds {
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Weight fragments of one stage, with the fp8 weight scales of that K-block.
+struct AStage {
+  v8i v[kNA];
+  float s[kNA];
+};
+
 template <bool kFp8>
-__device__ __forceinline__ void load_a(v8i (&dst)[kNA], const TileIn& in, int st, int q) {
+__device__ __forceinline__ void load_a(AStage& dst, const TileIn& in, int st, int q) {
 #pragma unroll
   for (int t = 0; t < kNA; ++t) {
+    if (kFp8) dst.s[t] = in.sw[t][st];
     const uint8_t* p = in.a[t] + (size_t)st * kStageBytes;
     uint4 lo, hi;
     if (kFp8) {
@@ -68,7 +76,7 @@ __device__ __forceinline__ void load_a(v8i (&dst)[kNA], const TileIn& in, int st
       hi = ld16(p + 64 + q * 16);
     }
     v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    dst[t] = r;
+    dst.v[t] = r;
   }
 }
 
@@ -77,21 +85,31 @@ struct BStage {
   float s;
 };
 
+// Loads are unconditional (rows out of range read a valid row) so that no
+// branch separates a load from its wait and the compiler's in-order load
+// counting stays exact; rows out of range are zeroed when the registers are
+// written to LDS, stages later, so the loaded values are not touched early.
 template <bool kFp8>
 __device__ __forceinline__ void load_b(BStage& r, const TileIn& in, int st) {
 #pragma unroll
-  for (int i = 0; i < kBVec; ++i)
-    r.v[i] = in.b ? ld16(in.b + (size_t)st * kStageBytes + 16 * i) : make_uint4(0, 0, 0, 0);
-  if (kFp8) r.s = in.bs ? in.bs[st] : 0.0f;
+  for (int i = 0; i < kBVec; ++i) r.v[i] = ld16(in.b + (size_t)st * kStageBytes + 16 * i);
+  if (kFp8) r.s = in.bs[st];
 }
 
 template <bool kFp8>
-__device__ __forceinline__ void store_b(TileLds& L, int buf, const BStage& r) {
+__device__ __forceinline__ void store_b(TileLds& L, int buf, const BStage& r, const TileIn& in) {
   const int tid = threadIdx.x;
   uint8_t* d = &L.b[buf][(tid / kBParts) * kLdsRow + (tid % kBParts) * kBPart];
+  const uint32_t keep = in.bok ? 0xFFFFFFFFu : 0u;       // value select (a select of lvalues would force memory)
 #pragma unroll
-  for (int i = 0; i < kBVec; ++i) *reinterpret_cast<uint4*>(d + 16 * i) = r.v[i];
-  if (kFp8 && tid < kTM) L.s[buf][tid] = r.s;
+  for (int i = 0; i < kBVec; ++i) {
+    const uint4 v = r.v[i];
+    *reinterpret_cast<uint4*>(d + 16 * i) = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+  }
+  if (kFp8 && tid < kTM) {
+    const float sv = r.s;
+    L.s[buf][tid] = in.bsok ? sv : 0.0f;
+  }
 }
 
 // All four results of a group of MFMAs wait out the MFMA latency together
@@ -147,11 +165,12 @@ __device__ __forceinline__ void close_segments(SegState& g, int done, Acc& acc, 
 
 // One K stage on LDS buffer `buf` with A fragments `a`.
 template <bool kFp8>
-__device__ __forceinline__ void tile_stage(const TileIn& in, const TileLds& L, int buf, const v8i (&a)[kNA], int st,
-                                           Acc& acc, Acc& tot, SegState& g) {
+__device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const AStage& as, int st, Acc& acc, Acc& tot,
+                                           SegState& g) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const v8i(&a)[kNA] = as.v;
   if (kFp8) {
-    const float sw0 = in.sw[0][st], sw1 = in.sw[1][st];
+    const float sw0 = as.s[0], sw1 = as.s[1];
 #pragma unroll
     for (int b = 0; b < kNB; b += 2) {
       v8i xb[2];
@@ -193,8 +212,8 @@ __device__ __forceinline__ void tile_stage(const TileIn& in, const TileLds& L, i
 }
 
 // The K loop of one tile: tot[t][b] = the element values of A tile t by slot
-// tile b (lane layout of the 16x16 MFMA output).  Weight fragments are loaded
-// kRingA stages ahead into registers; activation rows two stages ahead into
+// tile b (lane layout of the 16x16 MFMA output).  Weight fragments and their
+// block scales are loaded kRingA stages ahead into registers; activation rows two stages ahead into
 // registers, then into the LDS double buffer one stage ahead.  The stage loop
 // is unrolled by kRingA so every ring index is a compile-time constant.
 template <bool kFp8>
@@ -215,28 +234,36 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
   g.end = seg_begin(g.nunits, 1, g.nseg);
   close_segments<kFp8>(g, 0, acc, tot);
   const int n = in.nstage;
-  v8i ar[kRingA][kNA];
-  BStage br[2];
-#pragma unroll
-  for (int u = 0; u < kRingA; ++u)
-    if (in.on && u < n) load_a<kFp8>(ar[u], in, u, q);
-  load_b<kFp8>(br[0], in, 0);
-  store_b<kFp8>(L, 0, br[0]);
-  if (1 < n) load_b<kFp8>(br[1], in, 1);
-  if (2 < n) load_b<kFp8>(br[0], in, 2);
+  AStage ar0, ar1;                 // weight ring (two stages)
+  BStage br0, br1;                 // activation register ring (two stages)
+  // Ring refills past the last stage reload stage n - 1 (in range, unused):
+  // the loop issues the same loads every stage, with no branch around them.
+  const int last = n - 1;
+  load_a<kFp8>(ar0, in, 0, q);
+  load_a<kFp8>(ar1, in, min(1, last), q);
+  load_b<kFp8>(br0, in, 0);
+  store_b<kFp8>(L, 0, br0, in);
+  load_b<kFp8>(br1, in, min(1, last));
+  load_b<kFp8>(br0, in, min(2, last));
   __syncthreads();
-  for (int st0 = 0; st0 < n; st0 += kRingA) {
-#pragma unroll
-    for (int u = 0; u < kRingA; ++u) {
-      const int st = st0 + u;
-      if (st >= n) break;
-      if (in.on) tile_stage<kFp8>(in, L, u & 1, ar[u], st, acc, tot, g);
-      if (in.on && st + kRingA < n) load_a<kFp8>(ar[u], in, st + kRingA, q);
-      if (st + 1 < n) store_b<kFp8>(L, (u + 1) & 1, br[(u + 1) & 1]);      // stage st + 1
-      if (st + 3 < n) load_b<kFp8>(br[(u + 1) & 1], in, st + 3);          // stored two stages later
-      __syncthreads();
-    }
+  // One stage: compute on LDS buffer U with weights AR, refill AR two stages
+  // ahead, write the next stage's activations (register set BN) to the other
+  // buffer and refill BN three stages ahead.
+#define MOE_TILE_STEP(U, AR, BN)                               \
+  {                                                            \
+    const int st = st0 + (U);                                  \
+    if (st >= n) break;                                        \
+    tile_stage<kFp8>(L, (U), AR, st, acc, tot, g);             \
+    load_a<kFp8>(AR, in, min(st + kRingA, last), q);           \
+    store_b<kFp8>(L, (U) ^ 1, BN, in);                         \
+    load_b<kFp8>(BN, in, min(st + 3, last));                   \
+    __syncthreads();                                           \
   }
+  for (int st0 = 0; st0 < n; st0 += 2) {
+    MOE_TILE_STEP(0, ar0, br1)
+    MOE_TILE_STEP(1, ar1, br0)
+  }
+#undef MOE_TILE_STEP
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -261,12 +288,12 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
     in.a[1] = reinterpret_cast<const uint8_t*>(a.wsu + (size_t)(n0 + c) * a.H);
     in.sw[0] = in.sw[1] = nullptr;
     const int brow = mt * kTM + tid / kBParts;
-    const bool bvalid = brow < a.M && row_real(a.mask, brow);
-    in.b = bvalid ? reinterpret_cast<const uint8_t*>(a.x + (size_t)brow * a.H) + (tid % kBParts) * kBPart : nullptr;
+    in.bok = brow < a.M && row_real(a.mask, brow);
+    in.b = reinterpret_cast<const uint8_t*>(a.x + (size_t)(in.bok ? brow : 0) * a.H) + (tid % kBParts) * kBPart;
     in.bs = nullptr;
+    in.bsok = false;
     in.nstage = a.H * 2 / kStageBytes;
     in.nseg = kSegSG;
-    in.on = true;
     tile_gemm<false>(in, L, tot);
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
@@ -291,13 +318,14 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   {
     const int i = tid / kBParts;
     const int row = i < tl.mcnt ? a.rows[tl.s0 + i] : -1;
-    in.b = (row >= 0 && row < a.M) ? a.xq + (size_t)row * a.H + (tid % kBParts) * kBPart : nullptr;
+    in.bok = row >= 0 && row < a.M;
+    in.b = a.xq + (size_t)(in.bok ? row : 0) * a.H + (tid % kBParts) * kBPart;
     const int rs = (tid < kTM && tid < tl.mcnt) ? a.rows[tl.s0 + tid] : -1;
-    in.bs = (rs >= 0 && rs < a.M) ? a.xs + (size_t)rs * nkb : nullptr;
+    in.bsok = rs >= 0 && rs < a.M;
+    in.bs = a.xs + (size_t)(in.bsok ? rs : 0) * nkb;
   }
   in.nstage = nkb;
   in.nseg = kSegGU;
-  in.on = true;
   tile_gemm<true>(in, L, tot);
   // h = silu(G) U in place of G; 1x128 requantization over the tile's 128 columns
 #pragma unroll
@@ -353,7 +381,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
     const int mt = bid / ntH, nt = bid % ntH;
     const int n0 = nt * kDnCols + 32 * w;
     TileIn in;
-    in.on = true;                                   // waves past H compute on in-range rows, store nothing
+    // waves past H compute on in-range rows and store nothing
     const int nr = n0 < a.H ? n0 : a.H - 32;
 #pragma unroll
     for (int t = 0; t < kNA; ++t) {
@@ -361,9 +389,10 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
       in.sw[t] = nullptr;
     }
     const int brow = mt * kTM + tid / kBParts;
-    const bool bvalid = brow < a.M && row_real(a.mask, brow);
-    in.b = bvalid ? reinterpret_cast<const uint8_t*>(a.hsh + (size_t)brow * a.Is) + (tid % kBParts) * kBPart : nullptr;
+    in.bok = brow < a.M && row_real(a.mask, brow);
+    in.b = reinterpret_cast<const uint8_t*>(a.hsh + (size_t)(in.bok ? brow : 0) * a.Is) + (tid % kBParts) * kBPart;
     in.bs = nullptr;
+    in.bsok = false;
     in.nstage = a.Is * 2 / kStageBytes;
     in.nseg = kSegDN;
     tile_gemm<false>(in, L, tot);
@@ -383,7 +412,6 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   const int n0 = nt * kDnCols + 32 * w;
   const int nkb = a.I / kBlk;
   TileIn in;
-  in.on = true;
   const int nr = n0 < a.H ? n0 : a.H - 32;
 #pragma unroll
   for (int t = 0; t < kNA; ++t) {
@@ -392,8 +420,10 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   }
   {
     const int i = tid / kBParts;
-    in.b = i < tl.mcnt ? a.hq + (size_t)(tl.s0 + i) * a.I + (tid % kBParts) * kBPart : nullptr;
-    in.bs = (tid < kTM && tid < tl.mcnt) ? a.hs + (size_t)(tl.s0 + tid) * nkb : nullptr;
+    in.bok = i < tl.mcnt;
+    in.b = a.hq + (size_t)(tl.s0 + (in.bok ? i : 0)) * a.I + (tid % kBParts) * kBPart;
+    in.bsok = tid < kTM && tid < tl.mcnt;
+    in.bs = a.hs + (size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb;
   }
   in.nstage = nkb;
   in.nseg = kSegDN;
