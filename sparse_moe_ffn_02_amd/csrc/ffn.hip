@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* in, const uint8_t* 
                                                     float* scales) {
   const int lane = threadIdx.x & 63;
   const int nb = C / kBlk;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long item = (long)blockIdx.x * 4 + wave_id();
   const int r = (int)(item / nb);
   const int b = (int)(item % nb);
   if (r >= R || !row_real(mask, r)) return;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64) void k_plan(FfnArgs a) {
 // One wave per work item.  The grid covers the largest item count the call
 // can produce (the union is only known on the device); waves past the real
 // count exit at once, and the hardware dispatcher balances the rest.
-__device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + (threadIdx.x >> 6); }
+__device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + wave_id(); }
 
 // Gate/up tiles: the 16 MFMA A rows are gate rows n0..n0+7 (rows 0-7) and
 // up rows n0..n0+7 (rows 8-15), so lane l (l < 32) holds gate values and
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(512) void k_gateup_split(FfnArgs a) {
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
-  const int t = t0 + (threadIdx.x >> 6);
+  const int t = t0 + wave_id();
   if (t >= n_items) return;
   const int seg = t % kSegGU;
   const int item = t / kSegGU;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(512) void k_gateup_split(FfnArgs a) {
 // from the gate/up segment partials summed in order, h = silu(G) U.
 __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
   const int lane = threadIdx.x & 63;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long item = (long)blockIdx.x * 4 + wave_id();
   const int nbI = a.I / kBlk;
   const int slot = (int)(item / nbI);
   const int b = (int)(item % nbI);

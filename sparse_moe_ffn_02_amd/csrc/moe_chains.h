@@ -1,6 +1,7 @@
 // Device building blocks shared by the routing and expert kernels: vector
 // loads, stores, the 1x128 quantization of a 128-value block held by one
-// wave, and the fp8 / bf16 MFMA chains that define every GEMM element.
+// wave, the fp8 / bf16 MFMA chains of the small-step kernels (one K segment
+// each) and the slot-tile lookup.
 #pragma once
 
 #include "moe_device.h"
@@ -60,103 +61,117 @@ __device__ __forceinline__ void quant_pair(float v0, float v1, uint8_t* codes, f
 constexpr int kRing = 4;      // fp8 K-blocks in flight per wave
 constexpr int kRingBf = 8;    // bf16 K-steps (32 deep) in flight per wave
 
+__device__ __forceinline__ v8i mask8(const v8i& v, int keep) {
+  v8i r = {v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep, v[4] & keep, v[5] & keep, v[6] & keep, v[7] & keep};
+  return r;
+}
+
+__device__ __forceinline__ v4i mask4(const v4i& v, int keep) {
+  v4i r = {v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep};
+  return r;
+}
+
 // fp8 chain over K-blocks [kb0, kb1) for one 16x16 tile.  A (weights) rows
 // stream from global memory through a ring; B is read from global memory
 // (ring) or from LDS (kLdsB: a workgroup-resident copy).  Lanes with
-// bvalid == false contribute a zero B column and a zero activation scale.
+// bvalid == false contribute a zero B column and a zero activation scale
+// (bp must point at a readable row for every lane; the zeros come from a
+// value mask at use).  The main loop runs whole ring turns whose refills all
+// lie inside the range, so its loads are unconditional and no branch
+// separates a load from its wait; the last turns refill only what remains.
 template <bool kLdsB>
 __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, const uint8_t* bp, const float* sxp,
                                          bool bvalid, int kb0, int kb1) {
-  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (kb0 >= kb1) return acc;
+  const int last = kb1 - 1;
+  const int keep = bvalid ? -1 : 0;
   v8i wb[kRing], xb[kRing];
   float swb[kRing], sxb[kRing];
 #pragma unroll
   for (int i = 0; i < kRing; ++i) {
-    const int kb = kb0 + i;
-    if (kb < kb1) {
-      wb[i] = load32(wp + kb * kBlk);
-      swb[i] = swp[kb];
-      if (!kLdsB) {
-        xb[i] = bvalid ? load32(bp + kb * kBlk) : zero8;
-        sxb[i] = bvalid ? sxp[kb] : 0.0f;
-      }
+    const int kb = min(kb0 + i, last);
+    wb[i] = load32(wp + kb * kBlk);
+    swb[i] = swp[kb];
+    if (!kLdsB) {
+      xb[i] = load32(bp + kb * kBlk);
+      sxb[i] = sxp[kb];
     }
   }
-  for (int k0 = kb0; k0 < kb1; k0 += kRing) {
+  auto step = [&](int i, int kb) {
+    v8i x;
+    float sx;
+    if (kLdsB) {
+      x = *reinterpret_cast<const v8i*>(bp + kb * kBlk);
+      sx = sxp[kb];
+    } else {
+      x = xb[i];
+      sx = sxb[i];
+    }
+    const v4f p = mfma_fp8_k128(wb[i], mask8(x, keep));
+    scale_acc(acc, p, bvalid ? sx : 0.0f, swb[i]);
+  };
+  auto refill = [&](int i, int nk) {
+    wb[i] = load32(wp + nk * kBlk);
+    swb[i] = swp[nk];
+    if (!kLdsB) {
+      xb[i] = load32(bp + nk * kBlk);
+      sxb[i] = sxp[nk];
+    }
+  };
+  int k0 = kb0;
+  for (; k0 + 2 * kRing <= kb1; k0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
-      const int kb = k0 + i;
-      if (kb >= kb1) break;
-      v8i x;
-      float sx;
-      if (kLdsB) {
-        x = bvalid ? *reinterpret_cast<const v8i*>(bp + kb * kBlk) : zero8;
-        sx = bvalid ? sxp[kb] : 0.0f;
-      } else {
-        x = xb[i];
-        sx = sxb[i];
-      }
-      const v4f p = mfma_fp8_k128(wb[i], x);
-      scale_acc(acc, p, sx, swb[i]);
-      const int nk = kb + kRing;
-      if (nk < kb1) {
-        wb[i] = load32(wp + nk * kBlk);
-        swb[i] = swp[nk];
-        if (!kLdsB && bvalid) {
-          xb[i] = load32(bp + nk * kBlk);
-          sxb[i] = sxp[nk];
-        }
-      }
+      step(i, k0 + i);
+      refill(i, k0 + i + kRing);
+    }
+  }
+  for (; k0 < kb1; k0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      if (k0 + i < kb1) step(i, k0 + i);
+      if (k0 + i + kRing < kb1) refill(i, k0 + i + kRing);
     }
   }
   return acc;
 }
 
-// bf16 chain over K-steps [s0, s1) (32 deep each) for one 16x16 tile.
+// bf16 chain over K-steps [s0, s1) (32 deep each) for one 16x16 tile; loads
+// as in fp8_chain.
 __device__ __forceinline__ v4f bf16_chain(const uint16_t* wp, const uint16_t* bp, bool bvalid, int s0, int s1) {
-  const v4i zero4 = {0, 0, 0, 0};
   v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (s0 >= s1) return acc;
+  const int last = s1 - 1;
+  const int keep = bvalid ? -1 : 0;
   v4i wb[kRingBf], xb[kRingBf];
 #pragma unroll
   for (int i = 0; i < kRingBf; ++i) {
-    const int st = s0 + i;
-    if (st < s1) {
-      wb[i] = load16(wp + st * 32);
-      xb[i] = bvalid ? load16(bp + st * 32) : zero4;
-    }
+    const int st = min(s0 + i, last);
+    wb[i] = load16(wp + st * 32);
+    xb[i] = load16(bp + st * 32);
   }
-  for (int k0 = s0; k0 < s1; k0 += kRingBf) {
+  int k0 = s0;
+  for (; k0 + 2 * kRingBf <= s1; k0 += kRingBf) {
 #pragma unroll
     for (int i = 0; i < kRingBf; ++i) {
-      const int st = k0 + i;
-      if (st >= s1) break;
-      acc = mfma_bf16_k32(wb[i], xb[i], acc);
-      const int nx = st + kRingBf;
+      acc = mfma_bf16_k32(wb[i], mask4(xb[i], keep), acc);
+      wb[i] = load16(wp + (k0 + i + kRingBf) * 32);
+      xb[i] = load16(bp + (k0 + i + kRingBf) * 32);
+    }
+  }
+  for (; k0 < s1; k0 += kRingBf) {
+#pragma unroll
+    for (int i = 0; i < kRingBf; ++i) {
+      if (k0 + i < s1) acc = mfma_bf16_k32(wb[i], mask4(xb[i], keep), acc);
+      const int nx = k0 + i + kRingBf;
       if (nx < s1) {
         wb[i] = load16(wp + nx * 32);
-        if (bvalid) xb[i] = load16(bp + nx * 32);
+        xb[i] = load16(bp + nx * 32);
       }
     }
   }
   return settle_bf16(acc);
-}
-
-// All segments of an fp8 element, in order.
-template <bool kLdsB>
-__device__ __forceinline__ v4f fp8_full(const uint8_t* wp, const float* swp, const uint8_t* bp, const float* sxp,
-                                        bool bvalid, int nkb, int nseg) {
-  v4f tot = fp8_chain<kLdsB>(wp, swp, bp, sxp, bvalid, 0, seg_begin(nkb, 1, nseg));
-  for (int s = 1; s < nseg; ++s)
-    tot = add4(tot, fp8_chain<kLdsB>(wp, swp, bp, sxp, bvalid, seg_begin(nkb, s, nseg), seg_begin(nkb, s + 1, nseg)));
-  return tot;
-}
-
-__device__ __forceinline__ v4f bf16_full(const uint16_t* wp, const uint16_t* bp, bool bvalid, int nst, int nseg) {
-  v4f tot = bf16_chain(wp, bp, bvalid, 0, seg_begin(nst, 1, nseg));
-  for (int s = 1; s < nseg; ++s)
-    tot = add4(tot, bf16_chain(wp, bp, bvalid, seg_begin(nst, s, nseg), seg_begin(nst, s + 1, nseg)));
-  return tot;
 }
 
 // ---------------------------------------------------------------- slot tiles

@@ -19,6 +19,12 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kBlk = 128;       // quantization block (1x128 activations, 128x128 weights)
 constexpr int kWave = 64;
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: values derived from it (work items, K ranges) then stay in scalar
+// registers and the branches on them are scalar, which keeps the compiler's
+// wait counting across those branches exact.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // ---------------------------------------------------------------- MFMA
 // The matrix core does not interlock a vector-ALU, LDS or memory read of an
 // MFMA result: such a reader has to issue a fixed number of wait states after

@@ -24,7 +24,7 @@ namespace moe {
 template <int EPW>
 __global__ __launch_bounds__(256) void k_router_logits(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int r0 = blockIdx.x * 8;
   const int e0 = (blockIdx.y * 4 + wave) * EPW;
   if (e0 >= a.E) return;
@@ -174,7 +174,7 @@ __device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_
 
 __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + wave_id();
   if (row >= a.M) return;
   select_row(a, row, lane, nullptr);
 }
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kMaxExperts) void k_union_count(RouteArgs a) {
 
 // Inclusive scan over a workgroup of kMaxExperts threads (4 waves).
 __device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const uint32_t x = wave_incl_scan(v, lane);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
@@ -338,7 +338,7 @@ __device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int 
 
 __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int r = threadIdx.x >> 6;          // one wave per row
+  const int r = wave_id();          // one wave per row
   if (r >= a.M || (a.mask != nullptr && a.mask[r] == 0)) return;
   logit_row(a, r, blockIdx.x, lane);
 }
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
 // The shared expert needs no routing, so its weights stream while the router
 // runs.
 __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int b = blockIdx.x;
   if (b < r.E) {
     if (wave < r.M && (r.mask == nullptr || r.mask[wave] != 0)) logit_row(r, wave, b, lane);
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArg
   }
   // Phase A (wave r = row r): top-k, ids in ascending order, row bitmaps.
   const int lane = threadIdx.x & 63;
-  const int r = threadIdx.x >> 6;
+  const int r = wave_id();
   const int nwords = (a.E + 31) / 32;
   const bool real = r < a.M && (a.mask == nullptr || a.mask[r] != 0);
   if (real) {

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   const int total = n_sh + a.sched[SCHED_MTILES] * ntI;
   const int bid = blockIdx.x;
   if (bid >= total) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
   Acc tot;
   if (bid < n_sh) {
     const int mt = bid / ntS, nt = bid % ntS;
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   const int total = n_sh + a.sched[SCHED_MTILES] * ntH;
   const int bid = blockIdx.x;
   if (bid >= total) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
   Acc tot;
   if (bid < n_sh) {
     const int mt = bid / ntH, nt = bid % ntH;
