@@ -93,16 +93,22 @@ def device_layer(cfg, layer, torch, moe, replicas=1):
         r0["sd"][e].copy_(torch.from_numpy(t["s_down"]))
 
     synth.for_each_expert(cfg, layer, put)
+    # weights in the library's packed tile layout (row-major copies freed)
+    for k in ("wg", "wu", "wd"):
+        packed = torch.empty_like(r0[k])
+        moe.pack_weights(r0[k], packed, is_bf16=False)
+        r0[k] = packed
     for r in reps[1:]:
         for k in r:
             r[k].copy_(r0[k])
     sh = synth.shared_expert(cfg, layer)
     t16 = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)
+    shared = moe.pack_shared(moe.Shared(t16(sh["gate"]), t16(sh["up"]), t16(sh["down"])))
     out = []
     for r in reps:
         out.append(dict(
             experts=moe.Experts(r["wg"], r["wu"], r["wd"], r["sg"], r["su"], r["sd"]),
-            shared=moe.Shared(t16(sh["gate"]), t16(sh["up"]), t16(sh["down"])),
+            shared=shared,
             router_w=t16(synth.router_weight(cfg, layer)),
             bias=torch.from_numpy(synth.router_bias(cfg, layer)).to(dev)))
     torch.cuda.synchronize()

@@ -22,9 +22,11 @@
  * - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *   No call synchronizes the host, so calls are safe inside stream capture.
  *   Calls that share a workspace or outputs on different streams race.
- * - Matrices are row-major and dense.  Device pointers must be 16-byte
- *   aligned.  bf16 values are passed as uint16_t bit patterns; e4m3 values as
- *   uint8_t codes (OCP FP8 e4m3fn: bias 7, max 448, no infinities).
+ * - Matrices are row-major and dense, except expert and shared-expert
+ *   weights, which are passed in the packed tile layout written by
+ *   moe_pack_weights (same size).  Device pointers must be 16-byte aligned.
+ *   bf16 values are passed as uint16_t bit patterns; e4m3 values as uint8_t
+ *   codes (OCP FP8 e4m3fn: bias 7, max 448, no infinities).
  * - `row_mask` (device, uint8 [M]) marks real rows with 1 and pad rows with
  *   0; NULL means every row is real.  Kernels read it at run time, so one
  *   captured graph serves every mask.  A pad row's input is never read; its
@@ -86,23 +88,27 @@ typedef struct {
   const float* bias;  /* fp32 [E], e_score_correction_bias, used for selection only */
 } moe_router_w;
 
-/* Routed experts (device): e4m3 codes, output-major with K contiguous, and
- * one fp32 scale per 128x128 block.  All six pointers are required: an fp8
- * expert without its scales is refused (MOE_EINVAL). */
+/* Routed experts (device): e4m3 codes of the output-major matrices below
+ * (K contiguous in the checkpoint), each packed by moe_pack_weights
+ * (is_bf16 = 0), and one fp32 scale per 128x128 block (scales stay
+ * row-major).  The [gate_proj, up_proj, down_proj] triple is consumed by
+ * position (MoE-Infinity PR #140, expert-node commit).  All six pointers are
+ * required: an fp8 expert without its scales is refused (MOE_EINVAL). */
 typedef struct {
-  const uint8_t* w_gate; /* [E, I, H] */
-  const uint8_t* w_up;   /* [E, I, H] */
-  const uint8_t* w_down; /* [E, H, I] */
+  const uint8_t* w_gate; /* [E, I, H], packed */
+  const uint8_t* w_up;   /* [E, I, H], packed */
+  const uint8_t* w_down; /* [E, H, I], packed */
   const float* s_gate;   /* [E, I/128, H/128] */
   const float* s_up;     /* [E, I/128, H/128] */
   const float* s_down;   /* [E, H/128, I/128] */
 } moe_expert_w;
 
-/* Shared expert (device): bf16, output-major. */
+/* Shared expert (device): bf16, output-major, each matrix packed by
+ * moe_pack_weights (is_bf16 = 1). */
 typedef struct {
-  const uint16_t* w_gate; /* [I_s, H] */
-  const uint16_t* w_up;   /* [I_s, H] */
-  const uint16_t* w_down; /* [H, I_s] */
+  const uint16_t* w_gate; /* [I_s, H], packed */
+  const uint16_t* w_up;   /* [I_s, H], packed */
+  const uint16_t* w_down; /* [H, I_s], packed */
 } moe_shared_w;
 
 /* Routing of one step (device buffers, written by moe_route / moe_layer and
@@ -161,6 +167,20 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
  * cols must be a multiple of 128. */
 int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
                   void* stream);
+
+/* Weight packing (once, when weights are loaded).  The expert kernels read
+ * weights in 2048-byte tiles of 16 rows x 128 bytes of K, the tiles of a
+ * 16-row group consecutive along K and the groups consecutive, so that each
+ * load instruction of a wave reads 1 KB of contiguous memory and a wave
+ * streaming K reads whole tiles in address order.  Inside a tile, the 32
+ * bytes an MFMA lane (row r = 0..15, quarter q = 0..3) needs for one fp8
+ * 16x16x128 step (K bytes [32 q, 32 q + 32)) or one pair of bf16 16x16x32
+ * steps (elements [8 q, 8 q + 8) of each step) are split in two 16-byte
+ * halves at (r + 16 q) * 16 and 1024 + (r + 16 q) * 16.
+ * src: row-major [rows, row_bytes] (e4m3 codes, or bf16 with is_bf16 != 0);
+ * dst: same size, must not overlap src.  rows must be a multiple of 16 and
+ * row_bytes of 128 (an expert stack [E, N, K] is rows = E * N). */
+int moe_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes, int32_t is_bf16, void* stream);
 
 /* Kernel timing hook for measurement (host).  The pages time one layer's
  * experts per call with every call's weights read from HBM (mstar PR #388,

@@ -2,14 +2,15 @@
 
 The computation runs in hand-written HIP kernels behind the C ABI declared
 in include/moe_ffn.h (libmoe_ffn.so); this package is the thin Python
-binding with the same entry points (route, ffn_fp8, layer, quant_fp8).
+binding with the same entry points (route, ffn_fp8, layer, quant_fp8,
+pack_weights).
 """
 from ._lib import (EXPORTS, MAX_EXPERTS, MAX_ROWS, MAX_TOPK, MOE_EINVAL, MOE_ELAUNCH, MOE_EUNSUPPORTED,
                    MOE_EWORKSPACE, MOE_OK, Dims, Experts, MoeError, Routing, Shared, Taps, ffn_fp8, layer, load,
-                   quant_fp8, route, workspace, workspace_bytes)
+                   pack_experts, pack_shared, pack_weights, quant_fp8, route, workspace, workspace_bytes)
 
 __all__ = [
     "EXPORTS", "MAX_EXPERTS", "MAX_ROWS", "MAX_TOPK", "MOE_EINVAL", "MOE_ELAUNCH", "MOE_EUNSUPPORTED",
     "MOE_EWORKSPACE", "MOE_OK", "Dims", "Experts", "MoeError", "Routing", "Shared", "Taps", "ffn_fp8", "layer",
-    "load", "quant_fp8", "route", "workspace", "workspace_bytes",
+    "load", "pack_experts", "pack_shared", "pack_weights", "quant_fp8", "route", "workspace", "workspace_bytes",
 ]

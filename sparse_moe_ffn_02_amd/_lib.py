@@ -55,8 +55,8 @@ class CTaps(C.Structure):
                 ("h_scales", C.c_void_p)]
 
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_trace_set",
-           "moe_kernel_name", "moe_status_str")
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights",
+           "moe_trace_set", "moe_kernel_name", "moe_status_str")
 
 _lib = None
 
@@ -79,13 +79,14 @@ def load() -> C.CDLL:
     lib.moe_layer.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter), C.POINTER(CExperts),
                               C.POINTER(CShared), P, C.POINTER(CRouting), C.POINTER(CTaps), P, C.c_size_t, P]
     lib.moe_quant_fp8.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P]
+    lib.moe_pack_weights.argtypes = [P, P, C.c_int64, C.c_int32, C.c_int32, P]
     lib.moe_trace_set.argtypes = [P, C.c_int32, P, P]
     lib.moe_trace_set.restype = C.c_int
     lib.moe_kernel_name.argtypes = [C.c_int32]
     lib.moe_kernel_name.restype = C.c_char_p
     lib.moe_status_str.argtypes = [C.c_int]
     lib.moe_status_str.restype = C.c_char_p
-    for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8"):
+    for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib
@@ -145,9 +146,9 @@ class Routing:
 
 @dataclass
 class Experts:
-    w_gate: torch.Tensor   # uint8 [E, I, H]
+    w_gate: torch.Tensor   # uint8 [E, I, H], packed (pack_experts)
     w_up: torch.Tensor
-    w_down: torch.Tensor   # uint8 [E, H, I]
+    w_down: torch.Tensor   # uint8 [E, H, I], packed
     s_gate: torch.Tensor   # f32 [E, I/128, H/128]
     s_up: torch.Tensor
     s_down: torch.Tensor
@@ -159,9 +160,9 @@ class Experts:
 
 @dataclass
 class Shared:
-    w_gate: torch.Tensor   # bf16 bits (int16/uint16) [I_s, H]
+    w_gate: torch.Tensor   # bf16 bits (int16/uint16) [I_s, H], packed (pack_shared)
     w_up: torch.Tensor
-    w_down: torch.Tensor   # [H, I_s]
+    w_down: torch.Tensor   # [H, I_s], packed
 
     def c(self) -> CShared:
         return CShared(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down))
@@ -229,6 +230,31 @@ def layer(dims: Dims, x: torch.Tensor, row_mask: Optional[torch.Tensor], router_
     _check(load().moe_layer(C.byref(d), x.shape[0], _ptr(x), _ptr(row_mask), C.byref(r), C.byref(ew),
                             C.byref(sw) if sw is not None else None, _ptr(y), C.byref(rt),
                             C.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream()))
+
+
+def pack_weights(src: torch.Tensor, dst: torch.Tensor, is_bf16: bool) -> None:
+    """moe_pack_weights on a row-major weight tensor [..., rows, K] (e4m3 codes
+    or bf16 bits) into dst (same shape and size) on the current stream."""
+    row_bytes = src.shape[-1] * src.element_size()
+    rows = src.numel() * src.element_size() // row_bytes
+    _check(load().moe_pack_weights(_ptr(src), _ptr(dst), rows, row_bytes, 1 if is_bf16 else 0, _stream()))
+
+
+def _packed(t: torch.Tensor, is_bf16: bool) -> torch.Tensor:
+    out = torch.empty_like(t)
+    pack_weights(t, out, is_bf16)
+    return out
+
+
+def pack_experts(row_major: Experts) -> Experts:
+    """Packed copies of row-major expert weights (scales are shared, not copied)."""
+    return Experts(_packed(row_major.w_gate, False), _packed(row_major.w_up, False), _packed(row_major.w_down, False),
+                   row_major.s_gate, row_major.s_up, row_major.s_down)
+
+
+def pack_shared(row_major: Shared) -> Shared:
+    """Packed copies of row-major bf16 shared-expert weights."""
+    return Shared(_packed(row_major.w_gate, True), _packed(row_major.w_up, True), _packed(row_major.w_down, True))
 
 
 def quant_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> None:

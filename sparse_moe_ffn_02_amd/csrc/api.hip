@@ -187,7 +187,7 @@ Tracer g_trace;
 
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
-    "down_combine_decode", "down", "combine", "quant", "select_union", "front",
+    "down_combine_decode", "down", "combine", "quant", "select_union", "front", "pack",
 };
 
 }  // namespace
@@ -319,6 +319,15 @@ int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, u
   if (rows == 0) return MOE_OK;
   return to_status(
       launch_quant_generic(in, is_bf16 ? 1 : 0, rows, cols, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+int moe_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes, int32_t is_bf16, void* stream) {
+  if (rows < 0 || rows % 16 || row_bytes <= 0 || row_bytes % 128) return MOE_EINVAL;
+  if (!ok_ptr(src, 16) || !ok_ptr(dst, 16)) return MOE_EINVAL;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, n = (uintptr_t)rows * (uintptr_t)row_bytes;
+  if (n && a < b + n && b < a + n) return MOE_EINVAL;     // overlapping buffers
+  if (rows == 0) return MOE_OK;
+  return to_status(launch_pack(src, dst, (long)rows, row_bytes, is_bf16 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 const char* moe_status_str(int status) {

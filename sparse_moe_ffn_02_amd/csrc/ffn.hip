@@ -97,7 +97,7 @@ __device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + wave_id(); 
 // up rows n0..n0+7 (rows 8-15), so lane l (l < 32) holds gate values and
 // lane l + 32 the up values of the same (column, n); n = n0 + 4 (kq & 1) + i.
 __device__ __forceinline__ const uint8_t* gu_row(const FfnArgs& a, int e, int n0, int c, int kq) {
-  return (c < 8 ? a.wg : a.wu) + ((size_t)e * a.I + n0 + (c & 7)) * a.H + kq * 32;
+  return tile_row(c < 8 ? a.wg : a.wu, (size_t)e * a.I + n0 + (c & 7), a.H / kBlk, kq);
 }
 __device__ __forceinline__ const float* gu_scale(const FfnArgs& a, int e, int n0, int kq) {
   return (kq < 2 ? a.sg : a.su) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * (a.H / kBlk);
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
     const int seg = t % kSegDN, nt = t / kSegDN;
     const int row = c;
     const bool valid = row < a.M && row_real(a.mask, row);
-    const uint16_t* wp = a.wsd + (size_t)(nt * kCols + c) * a.Is + kq * 8;
+    const uint8_t* wp = tile_row(a.wsd, (size_t)nt * kCols + c, a.Is * 2 / kBlk, kq);
     const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
     const int nst = a.Is / 32;
     const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
   const int nt = it % ntH;
   const int slot = c < tl.mcnt ? tl.s0 + c : -1;
   const int nkb = a.I / kBlk;
-  const uint8_t* wp = a.wd + ((size_t)tl.e * a.H + nt * kCols + c) * a.I + kq * 32;
+  const uint8_t* wp = tile_row(a.wd, (size_t)tl.e * a.H + nt * kCols + c, nkb, kq);
   const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * kCols) / kBlk) * nkb;
   const uint8_t* bp = a.hq + (size_t)(slot < 0 ? 0 : slot) * a.I + kq * 32;
   const float* shp = a.hs + (size_t)(slot < 0 ? 0 : slot) * nkb;
@@ -276,7 +276,34 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
   store_bf16x4(yp, acc);
 }
 
+// ---------------------------------------------------------------- weight packing
+// Row-major [rows, row_bytes] -> packed tiles (see tile_row).  One thread per
+// 16-byte chunk of the destination: tile t = (row group, stage), half h and
+// lane (r, q) of the fragment it holds.  fp8 fragments hold K bytes
+// [32 q, 32 q + 32) of a stage (first 16 in half 0); bf16 fragments hold the
+// two 32-deep steps of a stage (step h, elements [8 q, 8 q + 8)).
+__global__ __launch_bounds__(256) void k_pack(const uint8_t* src, uint8_t* dst, long chunks, int nst, int is_bf16) {
+  const long ci = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (ci >= chunks) return;
+  const long tile = ci >> 7;
+  const int within = (int)(ci & 127);
+  const int h = within >> 6, lane = within & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const long g = tile / nst;
+  const int st = (int)(tile % nst);
+  const long row = g * 16 + r;
+  const int b = is_bf16 ? st * kBlk + 64 * h + 16 * q : st * kBlk + 32 * q + 16 * h;
+  *reinterpret_cast<uint4*>(dst + ci * 16) = *reinterpret_cast<const uint4*>(src + row * ((long)nst * kBlk) + b);
+}
+
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int is_bf16, hipStream_t s) {
+  const long chunks = rows * (row_bytes / 16);
+  MOE_LAUNCH(KID_PACK, k_pack, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, (const uint8_t*)src,
+             (uint8_t*)dst, chunks, row_bytes / kBlk, is_bf16);
+  return hipSuccess;
+}
 
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s) {
   MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(64), 0, s, a);

@@ -42,6 +42,29 @@ __device__ __forceinline__ v4f add4(const v4f& a, const v4f& b) {
 // first K-block (or K-step) of segment s when n blocks are split into S
 __device__ __forceinline__ int seg_begin(int n, int s, int S) { return (n * s) / S; }
 
+// ---------------------------------------------------------------- packed weights
+// Weights are stored in 2048-byte tiles of 16 rows x 128 bytes of K (fp8: one
+// K-block; bf16: two 32-deep K steps), the tiles of a 16-row group
+// consecutive along K.  In a tile, the 16 bytes that lane (row r, quarter q)
+// loads first sit at (r + 16 q) * 16 and the next 16 at 1024 + (r + 16 q) * 16,
+// so each of a wave's two loads reads 1 KB of contiguous memory.
+constexpr int kTile = 2048;
+
+__device__ __forceinline__ int tile_lane(int r, int q) { return (r + 16 * q) * 16; }
+
+// Lane address of row `row` (of a [rows, K] matrix with `nst` tiles per row
+// group) at K stage 0; stage s is + s * kTile.
+__device__ __forceinline__ const uint8_t* tile_row(const void* base, size_t row, int nst, int q) {
+  return reinterpret_cast<const uint8_t*>(base) + (size_t)(row >> 4) * nst * kTile + tile_lane((int)(row & 15), q);
+}
+
+__device__ __forceinline__ v8i load_frag(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 1024);
+  v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  return r;
+}
+
 // ---------------------------------------------------------------- quantization
 // One wave per (row, 128-column block): amax, s = fl32(amax/448) (1 for a
 // zero block), code = e4m3_rne_sat(fl32(v/s)); zero blocks give zero codes.
@@ -71,8 +94,9 @@ __device__ __forceinline__ v4i mask4(const v4i& v, int keep) {
   return r;
 }
 
-// fp8 chain over K-blocks [kb0, kb1) for one 16x16 tile.  A (weights) rows
-// stream from global memory through a ring; B is read from global memory
+// fp8 chain over K-blocks [kb0, kb1) for one 16x16 tile.  A (packed weight
+// tiles; wp = the lane's tile_row address at K-block 0) streams from global
+// memory through a ring; B (row-major) is read from global memory
 // (ring) or from LDS (kLdsB: a workgroup-resident copy).  Lanes with
 // bvalid == false contribute a zero B column and a zero activation scale
 // (bp must point at a readable row for every lane; the zeros come from a
@@ -91,7 +115,7 @@ __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, co
 #pragma unroll
   for (int i = 0; i < kRing; ++i) {
     const int kb = min(kb0 + i, last);
-    wb[i] = load32(wp + kb * kBlk);
+    wb[i] = load_frag(wp + (size_t)kb * kTile);
     swb[i] = swp[kb];
     if (!kLdsB) {
       xb[i] = load32(bp + kb * kBlk);
@@ -112,7 +136,7 @@ __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, co
     scale_acc(acc, p, bvalid ? sx : 0.0f, swb[i]);
   };
   auto refill = [&](int i, int nk) {
-    wb[i] = load32(wp + nk * kBlk);
+    wb[i] = load_frag(wp + (size_t)nk * kTile);
     swb[i] = swp[nk];
     if (!kLdsB) {
       xb[i] = load32(bp + nk * kBlk);
@@ -138,8 +162,15 @@ __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, co
 }
 
 // bf16 chain over K-steps [s0, s1) (32 deep each) for one 16x16 tile; loads
-// as in fp8_chain.
-__device__ __forceinline__ v4f bf16_chain(const uint16_t* wp, const uint16_t* bp, bool bvalid, int s0, int s1) {
+// as in fp8_chain.  wp = the lane's packed tile_row address at stage 0 (step
+// st is in stage st / 2, half st % 2); bp = the lane's row-major B row.
+__device__ __forceinline__ v4i load_step(const uint8_t* wp, int st) {
+  const uint4 v = *reinterpret_cast<const uint4*>(wp + (size_t)(st >> 1) * kTile + (st & 1) * 1024);
+  v4i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  return r;
+}
+
+__device__ __forceinline__ v4f bf16_chain(const uint8_t* wp, const uint16_t* bp, bool bvalid, int s0, int s1) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   if (s0 >= s1) return acc;
   const int last = s1 - 1;
@@ -148,7 +179,7 @@ __device__ __forceinline__ v4f bf16_chain(const uint16_t* wp, const uint16_t* bp
 #pragma unroll
   for (int i = 0; i < kRingBf; ++i) {
     const int st = min(s0 + i, last);
-    wb[i] = load16(wp + st * 32);
+    wb[i] = load_step(wp, st);
     xb[i] = load16(bp + st * 32);
   }
   int k0 = s0;
@@ -156,7 +187,7 @@ __device__ __forceinline__ v4f bf16_chain(const uint16_t* wp, const uint16_t* bp
 #pragma unroll
     for (int i = 0; i < kRingBf; ++i) {
       acc = mfma_bf16_k32(wb[i], mask4(xb[i], keep), acc);
-      wb[i] = load16(wp + (k0 + i + kRingBf) * 32);
+      wb[i] = load_step(wp, k0 + i + kRingBf);
       xb[i] = load16(bp + (k0 + i + kRingBf) * 32);
     }
   }
@@ -166,7 +197,7 @@ __device__ __forceinline__ v4f bf16_chain(const uint16_t* wp, const uint16_t* bp
       if (k0 + i < s1) acc = mfma_bf16_k32(wb[i], mask4(xb[i], keep), acc);
       const int nx = k0 + i + kRingBf;
       if (nx < s1) {
-        wb[i] = load16(wp + nx * 32);
+        wb[i] = load_step(wp, nx);
         xb[i] = load16(bp + nx * 32);
       }
     }

@@ -81,7 +81,7 @@ struct FfnArgs {
 // Kernel ids reported by the timing hook (moe_trace_set).
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
-  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_COUNT
+  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COUNT
 };
 
 void trace_before(hipStream_t s);
@@ -107,6 +107,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // steps that do not take the split path: tiled gate/up (+ SiLU, requant) and down
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s);
 bool use_split(int M, int H);   // M <= kSmallRows and the x codes fit the LDS budget
+hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int is_bf16, hipStream_t s);
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);
 

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
   const int seg = t % kSegSG, nt = t / kSegSG;
   const int n0 = nt * 8;
   const bool valid = c < f.M && row_real(f.mask, c);
-  const uint16_t* wp = (c < 8 ? f.wsg : f.wsu) + (size_t)(n0 + (c & 7)) * f.H + kq * 8;
+  const uint8_t* wp = tile_row(c < 8 ? f.wsg : f.wsu, (size_t)n0 + (c & 7), f.H * 2 / kBlk, kq);
   const uint16_t* bp = f.x + (size_t)(valid ? c : 0) * f.H + kq * 8;
   const int nst = f.H / 32;
   const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));

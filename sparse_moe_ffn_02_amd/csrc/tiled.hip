@@ -32,17 +32,19 @@ constexpr int kWaves = 8;
 constexpr int kTileThreads = 64 * kWaves;
 constexpr int kNA = 2;                     // 16-row weight tiles per wave
 constexpr int kNB = kTM / 16;              // 16-column slot tiles per wave
-constexpr int kBPart = kStageBytes * kTM / kTileThreads;   // activation bytes per thread per stage
-constexpr int kBVec = kBPart / 16;         // 16-byte loads per thread per stage
-constexpr int kBParts = kStageBytes / kBPart;              // threads per activation row
+// Activation staging: each 16-byte load instruction of a wave covers 8 whole
+// 128-byte rows (8 threads per row); thread t loads part t % 8 of rows
+// t / 8 + kBRowStep * i.
+constexpr int kBVec = kStageBytes * kTM / kTileThreads / 16;   // 16-byte loads per thread per stage
+constexpr int kBRowStep = kTileThreads / 8;                    // rows between a thread's loads
 constexpr int kRingA = 2;                  // weight stages in flight per wave (the loop below assumes 2)
 
 struct TileIn {
-  const uint8_t* a[kNA]; // per lane: weight row of each of the wave's A tiles, at K byte 0
+  const uint8_t* a[kNA]; // per lane: packed-tile address (tile_row) of each of the wave's A tiles, stage 0
   const float* sw[kNA];  // fp8: weight scales of each A tile, indexed by K-block
-  const uint8_t* b;      // per thread: its kBPart-byte part of activation row tid / kBParts (always a valid row)
+  const uint8_t* b[kBVec];  // per thread: 16-byte part tid % 8 of activation row tid / 8 + kBRowStep i (always valid)
   const float* bs;       // fp8: activation scales of row tid (threads < kTM), indexed by K-block (always valid)
-  bool bok;              // the thread's activation row is real (else it contributes zeros)
+  bool bok[kBVec];       // the thread's activation rows are real (else they contribute zeros)
   bool bsok;             // the thread's scale row is real (else zero)
   int nstage;            // K stages of 128 bytes
   int nseg;              // K segments (fp8: over K-blocks; bf16: over 32-deep K steps)
@@ -62,21 +64,11 @@ struct AStage {
 };
 
 template <bool kFp8>
-__device__ __forceinline__ void load_a(AStage& dst, const TileIn& in, int st, int q) {
+__device__ __forceinline__ void load_a(AStage& dst, const TileIn& in, int st) {
 #pragma unroll
   for (int t = 0; t < kNA; ++t) {
     if (kFp8) dst.s[t] = in.sw[t][st];
-    const uint8_t* p = in.a[t] + (size_t)st * kStageBytes;
-    uint4 lo, hi;
-    if (kFp8) {
-      lo = ld16(p + q * 32);
-      hi = ld16(p + q * 32 + 16);
-    } else {                         // two 32-deep bf16 steps: 16 bytes each
-      lo = ld16(p + q * 16);
-      hi = ld16(p + 64 + q * 16);
-    }
-    v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    dst.v[t] = r;
+    dst.v[t] = load_frag(in.a[t] + (size_t)st * kTile);
   }
 }
 
@@ -92,19 +84,19 @@ struct BStage {
 template <bool kFp8>
 __device__ __forceinline__ void load_b(BStage& r, const TileIn& in, int st) {
 #pragma unroll
-  for (int i = 0; i < kBVec; ++i) r.v[i] = ld16(in.b + (size_t)st * kStageBytes + 16 * i);
+  for (int i = 0; i < kBVec; ++i) r.v[i] = ld16(in.b[i] + (size_t)st * kStageBytes);
   if (kFp8) r.s = in.bs[st];
 }
 
 template <bool kFp8>
 __device__ __forceinline__ void store_b(TileLds& L, int buf, const BStage& r, const TileIn& in) {
   const int tid = threadIdx.x;
-  uint8_t* d = &L.b[buf][(tid / kBParts) * kLdsRow + (tid % kBParts) * kBPart];
-  const uint32_t keep = in.bok ? 0xFFFFFFFFu : 0u;       // value select (a select of lvalues would force memory)
 #pragma unroll
   for (int i = 0; i < kBVec; ++i) {
+    uint8_t* d = &L.b[buf][(tid / 8 + kBRowStep * i) * kLdsRow + (tid % 8) * 16];
+    const uint32_t keep = in.bok[i] ? 0xFFFFFFFFu : 0u;  // value select (a select of lvalues would force memory)
     const uint4 v = r.v[i];
-    *reinterpret_cast<uint4*>(d + 16 * i) = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    *reinterpret_cast<uint4*>(d) = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
   }
   if (kFp8 && tid < kTM) {
     const float sv = r.s;
@@ -218,7 +210,6 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
 // is unrolled by kRingA so every ring index is a compile-time constant.
 template <bool kFp8>
 __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
-  const int q = (threadIdx.x & 63) >> 4;
   Acc acc;
 #pragma unroll
   for (int t = 0; t < kNA; ++t)
@@ -239,8 +230,8 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
   // Ring refills past the last stage reload stage n - 1 (in range, unused):
   // the loop issues the same loads every stage, with no branch around them.
   const int last = n - 1;
-  load_a<kFp8>(ar0, in, 0, q);
-  load_a<kFp8>(ar1, in, min(1, last), q);
+  load_a<kFp8>(ar0, in, 0);
+  load_a<kFp8>(ar1, in, min(1, last));
   load_b<kFp8>(br0, in, 0);
   store_b<kFp8>(L, 0, br0, in);
   load_b<kFp8>(br1, in, min(1, last));
@@ -254,7 +245,7 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
     const int st = st0 + (U);                                  \
     if (st >= n) break;                                        \
     tile_stage<kFp8>(L, (U), AR, st, acc, tot, g);             \
-    load_a<kFp8>(AR, in, min(st + kRingA, last), q);           \
+    load_a<kFp8>(AR, in, min(st + kRingA, last));              \
     store_b<kFp8>(L, (U) ^ 1, BN, in);                         \
     load_b<kFp8>(BN, in, min(st + 3, last));                   \
     __syncthreads();                                           \
@@ -284,12 +275,15 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
     const int mt = bid / ntS, nt = bid % ntS;
     const int n0 = nt * kBlk + 16 * w;                 // wave's first h column
     TileIn in;
-    in.a[0] = reinterpret_cast<const uint8_t*>(a.wsg + (size_t)(n0 + c) * a.H);
-    in.a[1] = reinterpret_cast<const uint8_t*>(a.wsu + (size_t)(n0 + c) * a.H);
+    in.a[0] = tile_row(a.wsg, (size_t)n0 + c, a.H * 2 / kBlk, q);
+    in.a[1] = tile_row(a.wsu, (size_t)n0 + c, a.H * 2 / kBlk, q);
     in.sw[0] = in.sw[1] = nullptr;
-    const int brow = mt * kTM + tid / kBParts;
-    in.bok = brow < a.M && row_real(a.mask, brow);
-    in.b = reinterpret_cast<const uint8_t*>(a.x + (size_t)(in.bok ? brow : 0) * a.H) + (tid % kBParts) * kBPart;
+#pragma unroll
+    for (int i = 0; i < kBVec; ++i) {
+      const int brow = mt * kTM + tid / 8 + kBRowStep * i;
+      in.bok[i] = brow < a.M && row_real(a.mask, brow);
+      in.b[i] = reinterpret_cast<const uint8_t*>(a.x + (size_t)(in.bok[i] ? brow : 0) * a.H) + (tid % 8) * 16;
+    }
     in.bs = nullptr;
     in.bsok = false;
     in.nstage = a.H * 2 / kStageBytes;
@@ -311,15 +305,18 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   const int n0 = nt * kBlk + 16 * w;
   const int nkb = a.H / kBlk;
   TileIn in;
-  in.a[0] = a.wg + ((size_t)tl.e * a.I + n0 + c) * a.H;
-  in.a[1] = a.wu + ((size_t)tl.e * a.I + n0 + c) * a.H;
+  in.a[0] = tile_row(a.wg, (size_t)tl.e * a.I + n0 + c, nkb, q);
+  in.a[1] = tile_row(a.wu, (size_t)tl.e * a.I + n0 + c, nkb, q);
   in.sw[0] = a.sg + ((size_t)tl.e * ntI + nt) * nkb;
   in.sw[1] = a.su + ((size_t)tl.e * ntI + nt) * nkb;
   {
-    const int i = tid / kBParts;
-    const int row = i < tl.mcnt ? a.rows[tl.s0 + i] : -1;
-    in.bok = row >= 0 && row < a.M;
-    in.b = a.xq + (size_t)(in.bok ? row : 0) * a.H + (tid % kBParts) * kBPart;
+#pragma unroll
+    for (int v = 0; v < kBVec; ++v) {
+      const int i = tid / 8 + kBRowStep * v;
+      const int row = i < tl.mcnt ? a.rows[tl.s0 + i] : -1;
+      in.bok[v] = row >= 0 && row < a.M;
+      in.b[v] = a.xq + (size_t)(in.bok[v] ? row : 0) * a.H + (tid % 8) * 16;
+    }
     const int rs = (tid < kTM && tid < tl.mcnt) ? a.rows[tl.s0 + tid] : -1;
     in.bsok = rs >= 0 && rs < a.M;
     in.bs = a.xs + (size_t)(in.bsok ? rs : 0) * nkb;
@@ -385,12 +382,15 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
     const int nr = n0 < a.H ? n0 : a.H - 32;
 #pragma unroll
     for (int t = 0; t < kNA; ++t) {
-      in.a[t] = reinterpret_cast<const uint8_t*>(a.wsd + (size_t)(nr + 16 * t + c) * a.Is);
+      in.a[t] = tile_row(a.wsd, (size_t)nr + 16 * t + c, a.Is * 2 / kBlk, q);
       in.sw[t] = nullptr;
     }
-    const int brow = mt * kTM + tid / kBParts;
-    in.bok = brow < a.M && row_real(a.mask, brow);
-    in.b = reinterpret_cast<const uint8_t*>(a.hsh + (size_t)(in.bok ? brow : 0) * a.Is) + (tid % kBParts) * kBPart;
+#pragma unroll
+    for (int i = 0; i < kBVec; ++i) {
+      const int brow = mt * kTM + tid / 8 + kBRowStep * i;
+      in.bok[i] = brow < a.M && row_real(a.mask, brow);
+      in.b[i] = reinterpret_cast<const uint8_t*>(a.hsh + (size_t)(in.bok[i] ? brow : 0) * a.Is) + (tid % 8) * 16;
+    }
     in.bs = nullptr;
     in.bsok = false;
     in.nstage = a.Is * 2 / kStageBytes;
@@ -415,13 +415,16 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   const int nr = n0 < a.H ? n0 : a.H - 32;
 #pragma unroll
   for (int t = 0; t < kNA; ++t) {
-    in.a[t] = a.wd + ((size_t)tl.e * a.H + nr + 16 * t + c) * a.I;
+    in.a[t] = tile_row(a.wd, (size_t)tl.e * a.H + nr + 16 * t + c, nkb, q);
     in.sw[t] = a.sd + ((size_t)tl.e * (a.H / kBlk) + nr / kBlk) * nkb;
   }
   {
-    const int i = tid / kBParts;
-    in.bok = i < tl.mcnt;
-    in.b = a.hq + (size_t)(tl.s0 + (in.bok ? i : 0)) * a.I + (tid % kBParts) * kBPart;
+#pragma unroll
+    for (int v = 0; v < kBVec; ++v) {
+      const int i = tid / 8 + kBRowStep * v;
+      in.bok[v] = i < tl.mcnt;
+      in.b[v] = a.hq + (size_t)(tl.s0 + (in.bok[v] ? i : 0)) * a.I + (tid % 8) * 16;
+    }
     in.bsok = tid < kTM && tid < tl.mcnt;
     in.bs = a.hs + (size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb;
   }

@@ -42,16 +42,18 @@ def mdims(d: synth.Dims) -> moe.Dims:
 
 
 class GpuLayer:
-    """A synth.Layer resident in device memory, plus host copies for the oracle."""
+    """A synth.Layer resident in device memory (weights packed for the kernels),
+    plus host row-major copies for the oracle."""
 
     def __init__(self, lay: synth.Layer):
         self.host = lay
         self.dims = mdims(lay.dims)
         self.router_w = t16(lay.router_w)
         self.bias = tf(lay.bias)
-        self.experts = moe.Experts(t8(lay.w_gate), t8(lay.w_up), t8(lay.w_down), tf(lay.s_gate), tf(lay.s_up),
-                                   tf(lay.s_down))
-        self.shared = (moe.Shared(t16(lay.shared["gate"]), t16(lay.shared["up"]), t16(lay.shared["down"]))
+        self.experts = moe.pack_experts(moe.Experts(t8(lay.w_gate), t8(lay.w_up), t8(lay.w_down), tf(lay.s_gate),
+                                                    tf(lay.s_up), tf(lay.s_down)))
+        self.shared = (moe.pack_shared(moe.Shared(t16(lay.shared["gate"]), t16(lay.shared["up"]),
+                                                  t16(lay.shared["down"])))
                        if lay.shared else None)
 
     def with_bias(self, bias: np.ndarray) -> "GpuLayer":

@@ -176,6 +176,19 @@ def test_quant_rejects(lib):
     assert lib.moe_quant_fp8(FAKE, 0, 4, 128, FAKE, None, None) == L.MOE_EINVAL
 
 
+def test_pack_rejects(lib):
+    other = FAKE + (1 << 30)
+    assert lib.moe_pack_weights(FAKE, other, 0, 128, 0, None) == L.MOE_OK          # nothing to do
+    assert lib.moe_pack_weights(FAKE, other, 24, 128, 0, None) == L.MOE_EINVAL     # rows not a multiple of 16
+    assert lib.moe_pack_weights(FAKE, other, 16, 100, 0, None) == L.MOE_EINVAL     # row bytes not a multiple of 128
+    assert lib.moe_pack_weights(FAKE, other, -16, 128, 0, None) == L.MOE_EINVAL
+    assert lib.moe_pack_weights(None, other, 16, 128, 1, None) == L.MOE_EINVAL
+    assert lib.moe_pack_weights(FAKE, None, 16, 128, 1, None) == L.MOE_EINVAL
+    assert lib.moe_pack_weights(FAKE, FAKE, 16, 128, 0, None) == L.MOE_EINVAL      # in place
+    half = FAKE + 1024
+    assert lib.moe_pack_weights(FAKE, half, 16, 128, 0, None) == L.MOE_EINVAL      # overlapping
+
+
 def test_trace_hook_arguments(lib):
     ids = (C.c_int32 * 4)()
     cnt = C.c_int32(0)

@@ -9,7 +9,7 @@ import oracle
 import sparse_moe_ffn_02_amd as moe
 import synth
 from gpu_util import (GpuLayer, assert_routing_equal, assert_y_close, compare_h_codes, run_ffn, run_layer,
-                      run_oracle, say, t16, tf)
+                      run_oracle, say, t8, t16, tf)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,36 @@ def test_quant_unit_bit_exact():
     oc2, os2 = oracle.quant_1x128(oracle.decode_bf16(xb).astype(np.float32))
     assert np.array_equal(gs.cpu().numpy(), os2)
     assert np.array_equal(gc.cpu().numpy(), oc2)
+
+
+def _packed_reference(a: np.ndarray, is_bf16: bool) -> np.ndarray:
+    """The documented tile layout, built index by index from row-major bytes."""
+    b = np.ascontiguousarray(a).view(np.uint8).reshape(a.shape[0], -1)
+    rows, rb = b.shape
+    nst = rb // 128
+    out = np.empty(rows * rb, np.uint8)
+    for g in range(rows // 16):
+        for st in range(nst):
+            base = (g * nst + st) * 2048
+            for r in range(16):
+                for q in range(4):
+                    for h in range(2):
+                        src = st * 128 + (64 * h + 16 * q if is_bf16 else 32 * q + 16 * h)
+                        dst = base + h * 1024 + (r + 16 * q) * 16
+                        out[dst:dst + 16] = b[g * 16 + r, src:src + 16]
+    return out
+
+
+@pytest.mark.parametrize("is_bf16", [False, True])
+def test_pack_weights_layout(is_bf16):
+    """moe_pack_weights writes exactly the documented tile permutation."""
+    rng = np.random.default_rng(33)
+    a = rng.integers(0, 256, (48, 384), dtype=np.uint8)
+    src = t8(a)
+    dst = torch.empty_like(src)
+    moe.pack_weights(src, dst, is_bf16=is_bf16)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().reshape(-1), _packed_reference(a, is_bf16))
 
 
 def test_layer_parity(tiny):
