@@ -104,48 +104,30 @@ __device__ __forceinline__ const float* gu_scale(const FfnArgs& a, int e, int n0
 }
 
 // ---------------------------------------------------------------- gate/up (split small steps)
-// M <= kSmallRows: the workgroup keeps every row's x codes and scales in LDS
-// (rows padded by 16 bytes against bank conflicts) and the MFMA columns are
-// the step's rows (column c is row c; rows not routed to the item's expert
-// are computed and dropped).  Each item is one K segment of one 8-column
-// tile; it writes fp32 partials, reduced in segment order by k_post_gateup.
-constexpr int kLdsPad = 16;
-
-__global__ __launch_bounds__(512) void k_gateup_split(FfnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// M <= kSmallRows: each item is one K segment of one 8-column tile of one
+// union expert (one wave); it writes fp32 partials, reduced in segment order
+// by k_post_gateup.  The MFMA columns are the step's rows (column c is row c;
+// rows not routed to the item's expert are computed and dropped); the x
+// codes (a few KB per row, L2-resident) stream through the chain's ring with
+// the weights.
+__global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a) {
   const int nkb = a.H / kBlk;
-  const int ldx = a.H + kLdsPad;
-  uint8_t* lx = smem;
-  float* lsx = reinterpret_cast<float*>(smem + (size_t)a.M * ldx);
   const int ntI = a.I / 8;
   const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU;
-  const int t0 = blockIdx.x * 8;
-  if (t0 >= n_items) return;                    // workgroup beyond the union: nothing to stage
-  {
-    const int per_row = a.H / 16;
-    for (int i = threadIdx.x; i < a.M * per_row; i += blockDim.x) {
-      const int r = i / per_row, j = i % per_row;
-      const uint4 v = row_real(a.mask, r) ? *reinterpret_cast<const uint4*>(a.xq + (size_t)r * a.H + j * 16)
-                                          : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(lx + (size_t)r * ldx + j * 16) = v;
-    }
-    for (int i = threadIdx.x; i < a.M * nkb; i += blockDim.x)
-      lsx[i] = row_real(a.mask, i / nkb) ? a.xs[i] : 0.0f;
-  }
-  __syncthreads();
+  const int t = wave_item();
+  if (t >= n_items) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
-  const int t = t0 + wave_id();
-  if (t >= n_items) return;
   const int seg = t % kSegGU;
   const int item = t / kSegGU;
   const int u = item / ntI, nt = item % ntI;
   const int n0 = nt * 8;
   const int e = a.union_ids[u];
-  const bool col = c < a.M;
-  const v4f p = fp8_chain<true>(gu_row(a, e, n0, c, kq), gu_scale(a, e, n0, kq), lx + (size_t)(col ? c : 0) * ldx + kq * 32,
-                                lsx + (col ? c : 0) * nkb, col, seg_begin(nkb, seg, kSegGU),
-                                seg_begin(nkb, seg + 1, kSegGU));
+  const bool col = c < a.M && row_real(a.mask, c);
+  const int xr = col ? c : 0;
+  const v4f p = fp8_chain<false>(gu_row(a, e, n0, c, kq), gu_scale(a, e, n0, kq), a.xq + (size_t)xr * a.H + kq * 32,
+                                 a.xs + (size_t)xr * nkb, col, seg_begin(nkb, seg, kSegGU),
+                                 seg_begin(nkb, seg + 1, kSegGU));
   if (!col) return;
   // slot of (row c, expert e): the expert's rows are listed ascending
   const int lo = a.offs[u], hi = a.offs[u + 1];
@@ -331,11 +313,7 @@ hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8
   return hipSuccess;
 }
 
-size_t split_lds_bytes(int M, int H) {
-  return (size_t)M * (H + kLdsPad) + (size_t)M * (H / kBlk) * sizeof(float);
-}
-
-bool use_split(int M, int H) { return M <= kSmallRows && split_lds_bytes(M, H) <= 65536; }
+bool use_split(int M, int H) { return M <= kSmallRows && H > 0; }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const int with_shared = a.Is > 0 ? 1 : 0;
@@ -343,8 +321,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.split) {
     // one slot tile per union expert; the shared expert's gate/up ran in the front launch
     const long items = max_union * (a.I / 8) * kSegGU;
-    MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)((items + 7) / 8)), dim3(512), split_lds_bytes(a.M, a.H), s,
-               a);
+    MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
     const long post_waves = (long)a.M * a.K * (a.I / kBlk);
     MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)((post_waves + 3) / 4)), dim3(256), 0, s, a);
     const long dn_items = ((with_shared ? 1 : 0) + max_union) * (a.H / kCols) * kSegDN;

@@ -106,7 +106,7 @@ hipError_t launch_prep(const FfnArgs& a, hipStream_t s);   // quantize x
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // steps that do not take the split path: tiled gate/up (+ SiLU, requant) and down
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s);
-bool use_split(int M, int H);   // M <= kSmallRows and the x codes fit the LDS budget
+bool use_split(int M, int H);   // M <= kSmallRows
 hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int is_bf16, hipStream_t s);
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);
