@@ -110,11 +110,38 @@ __device__ __forceinline__ const float* gu_scale(const FfnArgs& a, int e, int n0
 // rows not routed to the item's expert are computed and dropped); the x
 // codes (a few KB per row, L2-resident) stream through the chain's ring with
 // the weights.
-__global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a) {
+// Shared expert h_s = bf16(silu(g) u) of row r, columns n, n + 1, from the
+// gate/up segment partials summed in order (2 columns per thread).
+__device__ __forceinline__ void form_hs(const FfnArgs& a, long idx) {
+  const int r = (int)(idx / a.Is), n = (int)(idx % a.Is);
+  if (r >= a.M || !row_real(a.mask, r)) return;
+  const size_t st = (size_t)a.M * 2 * a.Is;
+  const float* pg = a.part_sh + ((size_t)r * 2 + 0) * a.Is + n;
+  const float* pu = a.part_sh + ((size_t)r * 2 + 1) * a.Is + n;
+  float2 g = *reinterpret_cast<const float2*>(pg);
+  float2 u = *reinterpret_cast<const float2*>(pu);
+  for (int s = 1; s < kSegSG; ++s) {
+    const float2 gs = *reinterpret_cast<const float2*>(pg + s * st);
+    const float2 us = *reinterpret_cast<const float2*>(pu + s * st);
+    g.x = g.x + gs.x; g.y = g.y + gs.y;
+    u.x = u.x + us.x; u.y = u.y + us.y;
+  }
+  const uint32_t h = (uint32_t)f32_to_bf16(silu_mul(g.x, u.x)) | ((uint32_t)f32_to_bf16(silu_mul(g.y, u.y)) << 16);
+  *reinterpret_cast<uint32_t*>(a.hsh + (size_t)r * a.Is + n) = h;
+}
+
+// Blocks [0, hs_blocks) form the shared expert's h_s (its gate/up partials
+// are complete by now; first in the grid so they do not extend the tail);
+// the rest run routed items, one wave each.
+__global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) {
+  if ((int)blockIdx.x < hs_blocks) {
+    form_hs(a, ((long)blockIdx.x * blockDim.x + threadIdx.x) * 2);
+    return;
+  }
   const int nkb = a.H / kBlk;
   const int ntI = a.I / 8;
   const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU;
-  const int t = wave_item();
+  const int t = ((int)blockIdx.x - hs_blocks) * 4 + wave_id();
   if (t >= n_items) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
@@ -141,9 +168,31 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a) {
 // ---------------------------------------------------------------- requantization
 // Split steps: routed h per (slot, 128-column block) for the slots in use,
 // from the gate/up segment partials summed in order, h = silu(G) U.
-__global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
+// Shared expert down, one K segment of one 16-column tile of H: fp32
+// partials for every real row (t < (H / 16) * kSegDN).
+__device__ __forceinline__ void shared_down_item(const FfnArgs& a, int t, int lane) {
+  const int c = lane & 15, kq = lane >> 4;
+  const int seg = t % kSegDN, nt = t / kSegDN;
+  const int row = c;
+  const bool valid = row < a.M && row_real(a.mask, row);
+  const uint8_t* wp = tile_row(a.wsd, (size_t)nt * 16 + c, a.Is * 2 / kBlk, kq);
+  const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
+  const int nst = a.Is / 32;
+  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
+  if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * 16 + kq * 4, p);
+}
+
+// Blocks [0, sd_blocks) run the shared expert's down (h_s was formed by the
+// gate/up launch; first in the grid, the longer work); the rest requantize
+// routed h, one wave per (slot, 128-column block).
+__global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
   const int lane = threadIdx.x & 63;
-  const long item = (long)blockIdx.x * 4 + wave_id();
+  if ((int)blockIdx.x < sd_blocks) {
+    const int t = (int)blockIdx.x * 4 + wave_id();
+    if (t < (a.H / 16) * kSegDN) shared_down_item(a, t, lane);
+    return;
+  }
+  const long item = (long)((int)blockIdx.x - sd_blocks) * 4 + wave_id();
   const int nbI = a.I / kBlk;
   const int slot = (int)(item / nbI);
   const int b = (int)(item % nbI);
@@ -166,32 +215,18 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- down (split small steps)
-// Per-segment items: D[slot, n] (routed) and S[r, n] (shared) partials for
-// 16 columns of H and one union expert's slots (at most kSmallRows), or the
-// step's rows for the shared expert.
+// Per-segment items: routed D[slot, n] partials for 16 columns of H and one
+// union expert's slots (at most kSmallRows).
 constexpr int kCols = 16;
 
 __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
   const int ntH = a.H / kCols;
-  const int n_sh = (a.Is > 0) ? ntH * kSegDN : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntH * kSegDN;
+  const int total = a.sched[SCHED_MTILES] * ntH * kSegDN;
   const int t = wave_item();
   if (t >= total) return;
-  if (t < n_sh) {
-    const int seg = t % kSegDN, nt = t / kSegDN;
-    const int row = c;
-    const bool valid = row < a.M && row_real(a.mask, row);
-    const uint8_t* wp = tile_row(a.wsd, (size_t)nt * kCols + c, a.Is * 2 / kBlk, kq);
-    const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
-    const int nst = a.Is / 32;
-    const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
-    if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * kCols + kq * 4, p);
-    return;
-  }
-  const int tt = t - n_sh;
-  const int seg = tt % kSegDN, it = tt / kSegDN;
+  const int seg = t % kSegDN, it = t / kSegDN;
   const Tile tl = routed_tile(a, it / ntH);
   const int nt = it % ntH;
   const int slot = c < tl.mcnt ? tl.s0 + c : -1;
@@ -214,6 +249,20 @@ __device__ __forceinline__ v4f load_f4(const float* p) {
   return r;
 }
 
+// Slots are taken in groups of kCombGroup whose loads are all issued before
+// the first use, so a row costs one memory round trip per group instead of
+// one per slot; the fma chain still runs in j order and skips invalid slots.
+constexpr int kCombGroup = 8;
+
+__device__ __forceinline__ v4f slot_down(const FfnArgs& a, int s, int n) {
+  if (!a.split) return load_f4(a.D + (size_t)s * a.H + n);
+  const size_t st = (size_t)a.M * a.K * a.H;
+  v4f d = load_f4(a.part_d + (size_t)s * a.H + n);
+#pragma unroll
+  for (int g = 1; g < kSegDN; ++g) d = add4(d, load_f4(a.part_d + g * st + (size_t)s * a.H + n));
+  return d;
+}
+
 __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int q = a.H / 4;
@@ -226,35 +275,47 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
     return;
   }
   const int slots = a.sched[SCHED_SLOTS];
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.K; ++j) {
-    const int s = a.slot_of[(size_t)r * a.K + j];
-    if (s < 0 || s >= slots) continue;
-    const float wj = a.w[(size_t)r * a.K + j];
-    v4f d;
-    if (a.split) {
-      const size_t st = (size_t)a.M * a.K * a.H;
-      d = load_f4(a.part_d + (size_t)s * a.H + n);
-      for (int g = 1; g < kSegDN; ++g) d = add4(d, load_f4(a.part_d + g * st + (size_t)s * a.H + n));
-    } else {
-      d = load_f4(a.D + (size_t)s * a.H + n);
-    }
-    acc[0] = __builtin_fmaf(wj, d[0], acc[0]);
-    acc[1] = __builtin_fmaf(wj, d[1], acc[1]);
-    acc[2] = __builtin_fmaf(wj, d[2], acc[2]);
-    acc[3] = __builtin_fmaf(wj, d[3], acc[3]);
-  }
+  v4f sv = {0.f, 0.f, 0.f, 0.f};
   if (with_shared) {
-    v4f sv;
     if (a.split) {
       const size_t st = (size_t)a.M * a.H;
       sv = load_f4(a.part_s + (size_t)r * a.H + n);
+#pragma unroll
       for (int g = 1; g < kSegDN; ++g) sv = add4(sv, load_f4(a.part_s + g * st + (size_t)r * a.H + n));
     } else {
       sv = load_f4(a.S + (size_t)r * a.H + n);
     }
-    acc = add4(acc, sv);
   }
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  const int32_t* slp = a.slot_of + (size_t)r * a.K;
+  const float* wp = a.w + (size_t)r * a.K;
+  for (int j0 = 0; j0 < a.K; j0 += kCombGroup) {
+    int sl[kCombGroup];
+    float wj[kCombGroup];
+    bool ok[kCombGroup];
+#pragma unroll
+    for (int i = 0; i < kCombGroup; ++i) {
+      const int j = min(j0 + i, a.K - 1);
+      sl[i] = slp[j];
+      wj[i] = wp[j];
+    }
+    v4f d[kCombGroup];
+#pragma unroll
+    for (int i = 0; i < kCombGroup; ++i) {
+      ok[i] = j0 + i < a.K && sl[i] >= 0 && sl[i] < slots;
+      d[i] = slot_down(a, ok[i] ? sl[i] : 0, n);
+    }
+#pragma unroll
+    for (int i = 0; i < kCombGroup; ++i) {
+      if (ok[i]) {
+        acc[0] = __builtin_fmaf(wj[i], d[i][0], acc[0]);
+        acc[1] = __builtin_fmaf(wj[i], d[i][1], acc[1]);
+        acc[2] = __builtin_fmaf(wj[i], d[i][2], acc[2]);
+        acc[3] = __builtin_fmaf(wj[i], d[i][3], acc[3]);
+      }
+    }
+  }
+  if (with_shared) acc = add4(acc, sv);
   store_bf16x4(yp, acc);
 }
 
@@ -320,11 +381,18 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const long max_union = std::min<long>(a.E, (long)a.M * a.K);
   if (a.split) {
     // one slot tile per union expert; the shared expert's gate/up ran in the front launch
+    // gate/up also forms the shared h_s; the requantization launch also runs
+    // the shared down, in the time it would spend on latency alone
     const long items = max_union * (a.I / 8) * kSegGU;
-    MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+    const int gu_blocks = (int)((items + 3) / 4);
+    const int hs_blocks = with_shared ? (int)(((long)a.M * a.Is / 2 + 255) / 256) : 0;
+    MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)(hs_blocks + gu_blocks)), dim3(256), 0, s, a, hs_blocks);
     const long post_waves = (long)a.M * a.K * (a.I / kBlk);
-    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)((post_waves + 3) / 4)), dim3(256), 0, s, a);
-    const long dn_items = ((with_shared ? 1 : 0) + max_union) * (a.H / kCols) * kSegDN;
+    const int post_blocks = (int)((post_waves + 3) / 4);
+    const int sd_blocks = with_shared ? ((a.H / 16) * kSegDN + 3) / 4 : 0;
+    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)(sd_blocks + post_blocks)), dim3(256), 0, s, a,
+               sd_blocks);
+    const long dn_items = max_union * (a.H / kCols) * kSegDN;
     MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)((dn_items + 3) / 4)), dim3(256), 0, s, a);
   } else {
     // slot tiles: at most ceil(M*K / kMTile) + (union size), one partial tile per expert

@@ -350,6 +350,24 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
 //                             8-column tile per wave (fp32 partials)
 // The shared expert needs no routing, so its weights stream while the router
 // runs.
+// Shared expert gate/up, one K segment of one 8-column tile (item t of the
+// segments [seg0, seg0 + nseg)): fp32 partials of g and u for every real row.
+__device__ __forceinline__ void shared_gu_item(const FfnArgs& f, int t, int seg0, int nseg, int lane) {
+  const int c = lane & 15, kq = lane >> 4;
+  const int seg = seg0 + t % nseg, nt = t / nseg;
+  const int n0 = nt * 8;
+  const bool valid = c < f.M && row_real(f.mask, c);
+  const uint8_t* wp = tile_row(c < 8 ? f.wsg : f.wsu, (size_t)n0 + (c & 7), f.H * 2 / kBlk, kq);
+  const uint16_t* bp = f.x + (size_t)(valid ? c : 0) * f.H + kq * 8;
+  const int nst = f.H / 32;
+  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));
+  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + (kq >> 1)) * f.Is + n0 + (kq & 1) * 4, p);
+}
+
+// Split steps, first launch: blocks [0, E) logits (one block per expert, one
+// wave per row); then the x quantization; then the shared expert's gate/up
+// for the first half of its K segments (the second half runs beside the
+// top-k in k_select_union_small).
 __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int b = blockIdx.x;
@@ -368,105 +386,87 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
     return;
   }
   const int t = (b - r.E - nq) * 8 + wave;
-  if (f.Is == 0 || t >= (f.Is / 8) * kSegSG) return;
-  const int c = lane & 15, kq = lane >> 4;
-  const int seg = t % kSegSG, nt = t / kSegSG;
-  const int n0 = nt * 8;
-  const bool valid = c < f.M && row_real(f.mask, c);
-  const uint8_t* wp = tile_row(c < 8 ? f.wsg : f.wsu, (size_t)n0 + (c & 7), f.H * 2 / kBlk, kq);
-  const uint16_t* bp = f.x + (size_t)(valid ? c : 0) * f.H + kq * 8;
-  const int nst = f.H / 32;
-  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));
-  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + (kq >> 1)) * f.Is + n0 + (kq & 1) * 4, p);
+  if (f.Is == 0 || t >= (f.Is / 8) * (kSegSG / 2)) return;
+  shared_gu_item(f, t, 0, kSegSG / 2, lane);
 }
 
-// One workgroup (blockIdx 0): top-k of every row by rank (c[e] beats c[e']
-// when larger, or equal with the lower id), then the union and the row lists
-// in LDS, one thread per expert.  With do_hs, blocks >= 1 also form the
-// shared expert's h_s = bf16(silu(g) u) from its segment partials.
-__global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArgs f, int do_hs) {
+// Block 0 (8 waves; wave w serves rows w, w + 8): top-k of every row, then the
+// union and the row lists in LDS.  With do_sh, blocks >= 1 run the shared
+// expert's gate/up for the second half of its K segments.
+constexpr int kSelWaves = 8;
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs a, FfnArgs f, int do_sh) {
   __shared__ double ssig[kDecodeMaxRows][kMaxTopK];
   __shared__ int sid[kDecodeMaxRows][kMaxTopK];
   __shared__ uint32_t sbits[kDecodeMaxRows][8];
   __shared__ int soff[kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
   if (blockIdx.x > 0) {
-    if (!do_hs) return;
-    const long idx = ((long)(blockIdx.x - 1) * blockDim.x + threadIdx.x) * 2;
-    const int r = (int)(idx / f.Is), n = (int)(idx % f.Is);
-    if (r >= f.M || !row_real(f.mask, r)) return;
-    const size_t st = (size_t)f.M * 2 * f.Is;
-    const float* pg = f.part_sh + ((size_t)r * 2 + 0) * f.Is + n;
-    const float* pu = f.part_sh + ((size_t)r * 2 + 1) * f.Is + n;
-    float2 g = *reinterpret_cast<const float2*>(pg);
-    float2 u = *reinterpret_cast<const float2*>(pu);
-    for (int s = 1; s < kSegSG; ++s) {
-      const float2 gs = *reinterpret_cast<const float2*>(pg + s * st);
-      const float2 us = *reinterpret_cast<const float2*>(pu + s * st);
-      g.x = g.x + gs.x; g.y = g.y + gs.y;
-      u.x = u.x + us.x; u.y = u.y + us.y;
-    }
-    const uint32_t h = (uint32_t)f32_to_bf16(silu_mul(g.x, u.x)) | ((uint32_t)f32_to_bf16(silu_mul(g.y, u.y)) << 16);
-    *reinterpret_cast<uint32_t*>(f.hsh + (size_t)r * f.Is + n) = h;
+    if (!do_sh) return;
+    const int t = (blockIdx.x - 1) * kSelWaves + wave;
+    if (t >= (f.Is / 8) * (kSegSG - kSegSG / 2)) return;
+    shared_gu_item(f, t, kSegSG / 2, kSegSG - kSegSG / 2, lane);
     return;
   }
-  // Phase A (wave r = row r): top-k, ids in ascending order, row bitmaps.
-  const int lane = threadIdx.x & 63;
-  const int r = wave_id();
   const int nwords = (a.E + 31) / 32;
-  const bool real = r < a.M && (a.mask == nullptr || a.mask[r] != 0);
-  if (real) {
-    double c[4], sg[4];
-    bool ok[4], picked[4];
+  // Phase A (row r): top-k, ids in ascending order, row bitmaps.
+  for (int r = wave; r < a.M; r += kSelWaves) {
+    const bool real = a.mask == nullptr || a.mask[r] != 0;
+    if (real) {
+      double c[4], sg[4];
+      bool ok[4], picked[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      ok[q] = e < a.E;
-      picked[q] = false;
-      c[q] = -INFINITY;
-      sg[q] = 0.0;
-      if (ok[q]) {
-        c[q] = a.logits[(size_t)r * a.E + e];
-        sg[q] = a.sig[(size_t)r * a.E + e];
-      }
-    }
-    topk_rounds(c, ok, picked, a.K, lane);
-    // ascending id order: id = lane + 64 q, so positions follow q, then lane
-    int base = 0;
-    const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint64_t m = __ballot(picked[q]);
-      if (picked[q]) {
-        const int pos = base + __popcll(m & below);
-        ssig[r][pos] = sg[q];
-        sid[r][pos] = lane + 64 * q;
-        a.ids[(size_t)r * a.K + pos] = lane + 64 * q;
-      }
-      if (lane == 2 * q || lane == 2 * q + 1) {
-        const uint32_t word = (uint32_t)(lane == 2 * q ? m : (m >> 32));
-        if (lane < nwords) {
-          sbits[r][lane] = word;
-          a.rowbits[(size_t)r * nwords + lane] = word;
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        ok[q] = e < a.E;
+        picked[q] = false;
+        c[q] = -INFINITY;
+        sg[q] = 0.0;
+        if (ok[q]) {
+          c[q] = a.logits[(size_t)r * a.E + e];
+          sg[q] = a.sig[(size_t)r * a.E + e];
         }
       }
-      base += __popcll(m);
-    }
-  } else if (r < a.M) {
-    if (lane < a.K) {
-      a.ids[(size_t)r * a.K + lane] = -1;
-      a.w[(size_t)r * a.K + lane] = 0.0f;
-      a.slot_of[(size_t)r * a.K + lane] = -1;
-    }
-    if (lane < nwords) {
-      sbits[r][lane] = 0u;
-      a.rowbits[(size_t)r * nwords + lane] = 0u;
+      topk_rounds(c, ok, picked, a.K, lane);
+      // ascending id order: id = lane + 64 q, so positions follow q, then lane
+      int base = 0;
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t m = __ballot(picked[q]);
+        if (picked[q]) {
+          const int pos = base + __popcll(m & below);
+          ssig[r][pos] = sg[q];
+          sid[r][pos] = lane + 64 * q;
+          a.ids[(size_t)r * a.K + pos] = lane + 64 * q;
+        }
+        if (lane == 2 * q || lane == 2 * q + 1) {
+          const uint32_t word = (uint32_t)(lane == 2 * q ? m : (m >> 32));
+          if (lane < nwords) {
+            sbits[r][lane] = word;
+            a.rowbits[(size_t)r * nwords + lane] = word;
+          }
+        }
+        base += __popcll(m);
+      }
+    } else {
+      if (lane < a.K) {
+        a.ids[(size_t)r * a.K + lane] = -1;
+        a.w[(size_t)r * a.K + lane] = 0.0f;
+        a.slot_of[(size_t)r * a.K + lane] = -1;
+      }
+      if (lane < nwords) {
+        sbits[r][lane] = 0u;
+        a.rowbits[(size_t)r * nwords + lane] = 0u;
+      }
     }
   }
   __syncthreads();
   // Phase B (last wave; lane l owns experts 4 l .. 4 l + 3): per-expert row
   // counts, then one exclusive scan of a packed word gives each expert's
-  // first slot (bits 0-12), union index (bits 13-21) and first M-tile (22-31).
-  if (r == (int)(blockDim.x >> 6) - 1) {
+  // first slot (bits 0-12), union index (bits 13-21) and first tile (22-31).
+  if (wave == kSelWaves - 1) {
     uint32_t cnt[4], pk[4], run = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -505,10 +505,12 @@ __global__ __launch_bounds__(1024) void k_select_union_small(RouteArgs a, FfnArg
     }
   }
   __syncthreads();
-  // Phase C (wave r, lane j = pick j): combine weight and slot.  An expert's
+  // Phase C (row r, lane j = pick j): combine weight and slot.  An expert's
   // slots list its rows ascending, so row r's slot is the expert's first slot
   // plus the number of earlier rows that picked it.
-  if (real && lane < a.K) {
+  for (int r = wave; r < a.M; r += kSelWaves) {
+    const bool real = a.mask == nullptr || a.mask[r] != 0;
+    if (!real || lane >= a.K) continue;
     double tot = 0.0;
     for (int j = 0; j < a.K; ++j) tot += ssig[r][j];     // ascending id order
     a.w[(size_t)r * a.K + lane] = (float)((double)a.scale * (ssig[r][lane] / tot));
@@ -531,7 +533,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     FfnArgs none;
     memset(&none, 0, sizeof(none));
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * a.M), 0, s, a);
-    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(1024), 0, s, a, none, 0);
+    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(64 * kSelWaves), 0, s, a, none, 0);
     return hipSuccess;
   }
   MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((a.M + 7) / 8, (a.E + 15) / 16), blk, 0, s, a);
@@ -544,10 +546,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 
 hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s) {
   const int nq = (f.M * (f.H / kBlk) + 7) / 8;
-  const int ns = f.Is > 0 ? ((f.Is / 8) * kSegSG + 7) / 8 : 0;
-  MOE_LAUNCH(KID_FRONT, k_front, dim3(r.E + nq + ns), dim3(512), 0, s, r, f, nq);
-  const int nh = f.Is > 0 ? (f.M * f.Is / 2 + 1023) / 1024 : 0;
-  MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1 + nh), dim3(1024), 0, s, r, f, f.Is > 0 ? 1 : 0);
+  const int items1 = f.Is > 0 ? (f.Is / 8) * (kSegSG / 2) : 0;
+  const int items2 = f.Is > 0 ? (f.Is / 8) * (kSegSG - kSegSG / 2) : 0;
+  MOE_LAUNCH(KID_FRONT, k_front, dim3(r.E + nq + (items1 + 7) / 8), dim3(512), 0, s, r, f, nq);
+  MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1 + (items2 + kSelWaves - 1) / kSelWaves),
+             dim3(64 * kSelWaves), 0, s, r, f, f.Is > 0 ? 1 : 0);
   return hipSuccess;
 }
 
