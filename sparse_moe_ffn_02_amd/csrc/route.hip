@@ -21,13 +21,20 @@ namespace moe {
 // or expert group it falls in: lane j of a wave accumulates (float64 FMA, in
 // ascending order) the products for h = 512 i + 8 j + t (i ascending, then
 // t = 0..7), and the 64 lane partials are summed by an xor butterfly.
+// A block computes 8 rows by 4 * EPW experts.  Workgroups are dealt to the 8
+// XCDs round-robin, so block b runs on XCD b % 8; the blocks of one row group
+// (all its expert groups) are given indices of one residue and consecutive
+// quotients, so they run together on one XCD and its L2 serves their reads
+// of the rows after the first.
 template <int EPW>
 __global__ __launch_bounds__(256) void k_router_logits(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int r0 = blockIdx.x * 8;
-  const int e0 = (blockIdx.y * 4 + wave) * EPW;
-  if (e0 >= a.E) return;
+  const int neg = (a.E + 4 * EPW - 1) / (4 * EPW);       // expert groups
+  const int j = blockIdx.x / 8;
+  const int r0 = (8 * (j / neg) + (int)(blockIdx.x % 8)) * 8;
+  const int e0 = ((j % neg) * 4 + wave) * EPW;
+  if (r0 >= a.M || e0 >= a.E) return;
   bool rv[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) rv[r] = (r0 + r < a.M) && (a.mask == nullptr || a.mask[r0 + r] != 0);
@@ -37,26 +44,32 @@ __global__ __launch_bounds__(256) void k_router_logits(RouteArgs a) {
 #pragma unroll
     for (int e = 0; e < EPW; ++e) acc[r][e] = 0.0;
 
-  for (int h0 = lane * 8; h0 < a.H; h0 += 512) {
-    uint4 wv[EPW];
+  // rows past M or masked read row r0 (in range) and are never stored
+  const uint16_t* xrow[8];
 #pragma unroll
-    for (int e = 0; e < EPW; ++e)
-      wv[e] = (e0 + e < a.E) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)(e0 + e) * a.H + h0)
-                             : make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < 8; ++r) xrow[r] = a.x + (size_t)(rv[r] ? r0 + r : r0) * a.H;
+  for (int h0 = lane * 8; h0 < a.H; h0 += 512) {
+    // the chunk's weights, converted once for all 8 rows
+    double wd[EPW][8];
+#pragma unroll
+    for (int e = 0; e < EPW; ++e) {
+      const uint4 wv = (e0 + e < a.E) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)(e0 + e) * a.H + h0)
+                                      : make_uint4(0, 0, 0, 0);
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) wd[e][t] = (double)bf16_to_f32((uint16_t)(ww[t >> 1] >> ((t & 1) * 16)));
+    }
+    uint4 xv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) xv[r] = *reinterpret_cast<const uint4*>(xrow[r] + h0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      if (!rv[r]) continue;
-      const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (size_t)(r0 + r) * a.H + h0);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const uint32_t xw[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const double xd = (double)bf16_to_f32((uint16_t)(xw[t >> 1] >> ((t & 1) * 16)));
 #pragma unroll
-        for (int e = 0; e < EPW; ++e) {
-          const uint32_t ww[4] = {wv[e].x, wv[e].y, wv[e].z, wv[e].w};
-          const double wd = (double)bf16_to_f32((uint16_t)(ww[t >> 1] >> ((t & 1) * 16)));
-          acc[r][e] = __builtin_fma(xd, wd, acc[r][e]);
-        }
+        for (int e = 0; e < EPW; ++e) acc[r][e] = __builtin_fma(xd, wd[e][t], acc[r][e]);
       }
     }
   }
@@ -536,7 +549,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(64 * kSelWaves), 0, s, a, none, 0);
     return hipSuccess;
   }
-  MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((a.M + 7) / 8, (a.E + 15) / 16), blk, 0, s, a);
+  {
+    const long groups8 = ((a.M + 7) / 8 + 7) / 8 * 8;     // row groups, padded to a multiple of 8
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((unsigned)(groups8 * ((a.E + 15) / 16))), blk, 0, s, a);
+  }
   MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union_count, dim3(kUChunks), dim3(kMaxExperts), 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union_scan, dim3(1), dim3(kMaxExperts), 0, s, a);

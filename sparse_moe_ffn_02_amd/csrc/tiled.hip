@@ -37,7 +37,6 @@ constexpr int kNB = kTM / 16;              // 16-column slot tiles per wave
 // t / 8 + kBRowStep * i.
 constexpr int kBVec = kStageBytes * kTM / kTileThreads / 16;   // 16-byte loads per thread per stage
 constexpr int kBRowStep = kTileThreads / 8;                    // rows between a thread's loads
-constexpr int kRingA = 2;                  // weight stages in flight per wave (the loop below assumes 2)
 
 struct TileIn {
   const uint8_t* a[kNA]; // per lane: packed-tile address (tile_row) of each of the wave's A tiles, stage 0
@@ -205,11 +204,12 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
 
 // The K loop of one tile: tot[t][b] = the element values of A tile t by slot
 // tile b (lane layout of the 16x16 MFMA output).  Weight fragments and their
-// block scales are loaded kRingA stages ahead into registers; activation rows two stages ahead into
-// registers, then into the LDS double buffer one stage ahead.  The stage loop
-// is unrolled by kRingA so every ring index is a compile-time constant.
-template <bool kFp8>
+// block scales are loaded kRingA stages ahead into registers (3 where the
+// registers allow it, else 2); activation rows two stages ahead into
+// registers, then into the LDS double buffer one stage ahead.
+template <bool kFp8, int kRingA>
 __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
+  static_assert(kRingA == 2 || kRingA == 3, "weight ring of 2 or 3 stages");
   Acc acc;
 #pragma unroll
   for (int t = 0; t < kNA; ++t)
@@ -225,24 +225,27 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
   g.end = seg_begin(g.nunits, 1, g.nseg);
   close_segments<kFp8>(g, 0, acc, tot);
   const int n = in.nstage;
-  AStage ar0, ar1;                 // weight ring (two stages)
+  AStage ar0, ar1, ar2;            // weight ring (kRingA stages)
   BStage br0, br1;                 // activation register ring (two stages)
   // Ring refills past the last stage reload stage n - 1 (in range, unused):
   // the loop issues the same loads every stage, with no branch around them.
   const int last = n - 1;
   load_a<kFp8>(ar0, in, 0);
   load_a<kFp8>(ar1, in, min(1, last));
+  if (kRingA == 3) load_a<kFp8>(ar2, in, min(2, last));
   load_b<kFp8>(br0, in, 0);
   store_b<kFp8>(L, 0, br0, in);
   load_b<kFp8>(br1, in, min(1, last));
   load_b<kFp8>(br0, in, min(2, last));
   __syncthreads();
-  // One stage: compute on LDS buffer U with weights AR, refill AR two stages
-  // ahead, write the next stage's activations (register set BN) to the other
-  // buffer and refill BN three stages ahead.
-#define MOE_TILE_STEP(U, AR, BN)                               \
+  // One stage (st0 + D): compute on LDS buffer U with weights AR, refill AR
+  // kRingA stages ahead, write the next stage's activations (register set
+  // BN) to the other buffer and refill BN three stages ahead.  The loop is
+  // unrolled by 6 so that the weight ring (3) and the LDS / activation
+  // rings (2) all use compile-time indices.
+#define MOE_TILE_STEP(D, U, AR, BN)                            \
   {                                                            \
-    const int st = st0 + (U);                                  \
+    const int st = st0 + (D);                                  \
     if (st >= n) break;                                        \
     tile_stage<kFp8>(L, (U), AR, st, acc, tot, g);             \
     load_a<kFp8>(AR, in, min(st + kRingA, last));              \
@@ -250,9 +253,20 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
     load_b<kFp8>(BN, in, min(st + 3, last));                   \
     __syncthreads();                                           \
   }
-  for (int st0 = 0; st0 < n; st0 += 2) {
-    MOE_TILE_STEP(0, ar0, br1)
-    MOE_TILE_STEP(1, ar1, br0)
+  if (kRingA == 3) {
+    for (int st0 = 0; st0 < n; st0 += 6) {
+      MOE_TILE_STEP(0, 0, ar0, br1)
+      MOE_TILE_STEP(1, 1, ar1, br0)
+      MOE_TILE_STEP(2, 0, ar2, br1)
+      MOE_TILE_STEP(3, 1, ar0, br0)
+      MOE_TILE_STEP(4, 0, ar1, br1)
+      MOE_TILE_STEP(5, 1, ar2, br0)
+    }
+  } else {
+    for (int st0 = 0; st0 < n; st0 += 2) {
+      MOE_TILE_STEP(0, 0, ar0, br1)
+      MOE_TILE_STEP(1, 1, ar1, br0)
+    }
   }
 #undef MOE_TILE_STEP
 }
@@ -288,7 +302,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
     in.bsok = false;
     in.nstage = a.H * 2 / kStageBytes;
     in.nseg = kSegSG;
-    tile_gemm<false>(in, L, tot);
+    tile_gemm<false, 3>(in, L, tot);
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const int row = mt * kTM + 16 * b + c;
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   }
   in.nstage = nkb;
   in.nseg = kSegGU;
-  tile_gemm<true>(in, L, tot);
+  tile_gemm<true, 3>(in, L, tot);
   // h = silu(G) U in place of G; 1x128 requantization over the tile's 128 columns
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
     in.bsok = false;
     in.nstage = a.Is * 2 / kStageBytes;
     in.nseg = kSegDN;
-    tile_gemm<false>(in, L, tot);
+    tile_gemm<false, 2>(in, L, tot);
     if (n0 >= a.H) return;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
@@ -430,7 +444,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   }
   in.nstage = nkb;
   in.nseg = kSegDN;
-  tile_gemm<true>(in, L, tot);
+  tile_gemm<true, 2>(in, L, tot);
   if (n0 >= a.H) return;
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
