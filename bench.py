@@ -133,26 +133,39 @@ def gateup_bytes(nu, d, m):
 
 
 def down_decode_bytes(nu, d, m):
-    """Algorithmic bytes of the down kernel: down codes + scales of the union
-    experts, the shared down bf16 weights, h codes + scales, shared h (bf16)."""
-    H, I, Is, K = d.hidden, d.inter, d.shared_inter, d.top_k
-    return (nu * (I * H + 4 * (H // 128) * (I // 128)) + H * Is * 2 + m * K * (I + 4 * (I // 128))
-            + m * Is * 2)
+    """Algorithmic bytes of the routed down kernel (small steps): down codes +
+    scales of the union experts, h codes + scales."""
+    H, I, K = d.hidden, d.inter, d.top_k
+    return nu * (I * H + 4 * (H // 128) * (I // 128)) + m * K * (I + 4 * (I // 128))
 
 
 def front_bytes(d, m):
     """Algorithmic bytes of the fused front kernel (small steps): the router
-    weights, the shared gate/up bf16 weights, x (bf16) once, x codes and
-    scales out."""
+    weights, the first half of the shared gate/up K range (bf16), x (bf16)
+    once, x codes and scales out."""
     H, Is, E = d.hidden, d.shared_inter, d.n_experts
-    return E * H * 2 + 2 * Is * H * 2 + m * H * 2 + m * H + m * (H // 128) * 4
+    return E * H * 2 + Is * H * 2 + m * H * 2 + m * H + m * (H // 128) * 4
+
+
+def select_bytes(d, m):
+    """Algorithmic bytes of the select/union launch (small steps): the second
+    half of the shared gate/up K range (bf16)."""
+    return d.shared_inter * d.hidden * 2
+
+
+def post_bytes(d, m):
+    """Algorithmic bytes of the requantization launch (small steps): the
+    shared down weights (bf16) and the shared h rows."""
+    return d.hidden * d.shared_inter * 2 + m * d.shared_inter * 2
 
 
 def kernel_bytes(name, nu, d, m):
     """Algorithmic bytes per launch of the kernels that stream weights."""
     return {"gateup": gateup_bytes(nu, d, m),
             "down": down_decode_bytes(nu, d, m),
-            "front": front_bytes(d, m)}.get(name)
+            "front": front_bytes(d, m),
+            "select_union": select_bytes(d, m),
+            "post_gateup": post_bytes(d, m)}.get(name)
 
 
 def layer_flops(d, m_real, slots):

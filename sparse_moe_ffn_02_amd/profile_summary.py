@@ -40,12 +40,18 @@ def source_digest() -> str:
 
 
 def short_name(kernel: str) -> str:
-    """moe::k_gateup_split(moe::FfnArgs) -> gateup_split."""
+    """moe::k_gateup_split(moe::FfnArgs) -> gateup_split;
+    void moe::k_router_logits<4>(moe::RouteArgs) -> router_logits."""
     k = kernel.split("(")[0]
+    k = k.split("<")[0]
     k = k.split("::")[-1]
     if k.startswith("k_"):
         k = k[2:]
     return k
+
+
+def is_library_kernel(kernel: str) -> bool:
+    return kernel.startswith("moe::") or kernel.startswith("void moe::")
 
 
 def trace_summary(d: str, out: str, command: str) -> None:
@@ -90,7 +96,7 @@ def counters_summary(fd: str, wd: str, cfd: str, cwd: str, copy_bytes: int, out:
              "|---|---|---|---|---|---|"]
     table = {}
     for k in sorted(set(fetch) | set(write)):
-        if not k.startswith("moe::"):
+        if not is_library_kernel(k):
             continue
         f = fetch.get(k, [0.0])
         w = write.get(k, [0.0])

@@ -19,3 +19,6 @@ def test_traffic_digest_gate(tmp_path):
 def test_short_names():
     assert ps.short_name("moe::k_gateup_split(moe::FfnArgs)") == "gateup_split"
     assert ps.short_name("moe::k_front(moe::RouteArgs, moe::FfnArgs, int)") == "front"
+    assert ps.short_name("void moe::k_router_logits<4>(moe::RouteArgs)") == "router_logits"
+    assert ps.is_library_kernel("void moe::k_quant_rows<unsigned short>(unsigned short const*)")
+    assert not ps.is_library_kernel("__amd_rocclr_copyBuffer")
