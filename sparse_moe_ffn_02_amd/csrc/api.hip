@@ -48,7 +48,7 @@ Layout make_layout(const moe_dims& d, int M) {
   L.part_gu = take(sp * kSegGU * m * K * 2 * I * sizeof(float));
   L.part_sh = take(sp * kSegSG * m * 2 * Is * sizeof(float));
   L.part_d = take(sp * kSegDN * m * K * H * sizeof(float));
-  L.part_s = take(sp * kSegDN * m * H * sizeof(float));
+  L.part_s = take(sp * kSegSD * m * H * sizeof(float));
   L.total = off;
   return L;
 }

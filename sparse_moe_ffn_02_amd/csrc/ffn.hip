@@ -16,7 +16,7 @@
 //                K-blocks kb ascending, acc = fma(s_act[kb] * s_w[kb], P_kb,
 //                acc) with P_kb one 16x16x128 fp8 MFMA from a zero
 //                accumulator; the element is ((seg0 + seg1) + seg2) + ...;
-//   shared GEMM  fixed K segments (kSegSG for gate/up, kSegDN for down),
+//   shared GEMM  fixed K segments (kSegSG for gate/up, kSegSD for down),
 //                each a bf16 16x16x32 MFMA chain from zero, summed in order;
 //   combine      acc = fma(w_j, D[slot(r, j)], acc) for j ascending, then
 //                + S[r] when the shared expert is present, then bf16 RNE.
@@ -169,16 +169,16 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
 // Split steps: routed h per (slot, 128-column block) for the slots in use,
 // from the gate/up segment partials summed in order, h = silu(G) U.
 // Shared expert down, one K segment of one 16-column tile of H: fp32
-// partials for every real row (t < (H / 16) * kSegDN).
+// partials for every real row (t < (H / 16) * kSegSD).
 __device__ __forceinline__ void shared_down_item(const FfnArgs& a, int t, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int seg = t % kSegDN, nt = t / kSegDN;
+  const int seg = t % kSegSD, nt = t / kSegSD;
   const int row = c;
   const bool valid = row < a.M && row_real(a.mask, row);
   const uint8_t* wp = tile_row(a.wsd, (size_t)nt * 16 + c, a.Is * 2 / kBlk, kq);
   const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
   const int nst = a.Is / 32;
-  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegDN), seg_begin(nst, seg + 1, kSegDN));
+  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSD), seg_begin(nst, seg + 1, kSegSD));
   if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * 16 + kq * 4, p);
 }
 
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
   const int lane = threadIdx.x & 63;
   if ((int)blockIdx.x < sd_blocks) {
     const int t = (int)blockIdx.x * 4 + wave_id();
-    if (t < (a.H / 16) * kSegDN) shared_down_item(a, t, lane);
+    if (t < (a.H / 16) * kSegSD) shared_down_item(a, t, lane);
     return;
   }
   const long item = (long)((int)blockIdx.x - sd_blocks) * 4 + wave_id();
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
       const size_t st = (size_t)a.M * a.H;
       sv = load_f4(a.part_s + (size_t)r * a.H + n);
 #pragma unroll
-      for (int g = 1; g < kSegDN; ++g) sv = add4(sv, load_f4(a.part_s + g * st + (size_t)r * a.H + n));
+      for (int g = 1; g < kSegSD; ++g) sv = add4(sv, load_f4(a.part_s + g * st + (size_t)r * a.H + n));
     } else {
       sv = load_f4(a.S + (size_t)r * a.H + n);
     }
@@ -389,7 +389,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)(hs_blocks + gu_blocks)), dim3(256), 0, s, a, hs_blocks);
     const long post_waves = (long)a.M * a.K * (a.I / kBlk);
     const int post_blocks = (int)((post_waves + 3) / 4);
-    const int sd_blocks = with_shared ? ((a.H / 16) * kSegDN + 3) / 4 : 0;
+    const int sd_blocks = with_shared ? ((a.H / 16) * kSegSD + 3) / 4 : 0;
     MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)(sd_blocks + post_blocks)), dim3(256), 0, s, a,
                sd_blocks);
     const long dn_items = max_union * (a.H / kCols) * kSegDN;

@@ -13,10 +13,11 @@ constexpr int kSmallRows = 8;       // rows served by the split small-step exper
 constexpr int kUChunks = 64;        // row chunks of the larger-step union
 // Every GEMM element is the fixed-order sum of its K-segment chains:
 // routed gate/up over kSegGU segments of K = H, shared gate/up over kSegSG,
-// routed and shared down over kSegDN segments of K = I.  Small steps run each segment as its own work
+// routed down over kSegDN and shared down over kSegSD segments of K = I.  Small steps run each segment as its own work
 // item and reduce the fp32 partials later; larger steps run them in-wave.
-constexpr int kSegGU = 4;
-constexpr int kSegDN = 2;
+constexpr int kSegGU = 2;
+constexpr int kSegDN = 1;
+constexpr int kSegSD = 2;           // shared expert down
 constexpr int kSegSG = 8;           // shared expert gate/up (bf16 steps stream half the bytes per load)
 
 // sched[] words written by the union / plan kernels and read by the FFN kernels
@@ -74,7 +75,7 @@ struct FfnArgs {
   float* part_gu;          // [kSegGU][M*K][2][I]  routed gate / up
   float* part_sh;          // [kSegSG][M][2][Is]   shared gate / up
   float* part_d;           // [kSegDN][M*K][H]     routed down
-  float* part_s;           // [kSegDN][M][H]       shared down
+  float* part_s;           // [kSegSD][M][H]       shared down
   uint16_t* y;             // bf16 [M, H]
 };
 

@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
     in.bs = nullptr;
     in.bsok = false;
     in.nstage = a.Is * 2 / kStageBytes;
-    in.nseg = kSegDN;
+    in.nseg = kSegSD;
     tile_gemm<false, 2>(in, L, tot);
     if (n0 >= a.H) return;
 #pragma unroll
