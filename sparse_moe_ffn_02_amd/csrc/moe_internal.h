@@ -17,8 +17,8 @@ constexpr int kUChunks = 64;        // row chunks of the larger-step union
 // item and reduce the fp32 partials later; larger steps run them in-wave.
 constexpr int kSegGU = 2;
 constexpr int kSegDN = 1;
-constexpr int kSegSD = 2;           // shared expert down
-constexpr int kSegSG = 8;           // shared expert gate/up (bf16 steps stream half the bytes per load)
+constexpr int kSegSD = 4;           // shared expert down
+constexpr int kSegSG = 16;          // shared expert gate/up (bf16 steps stream half the bytes per load)
 
 // sched[] words written by the union / plan kernels and read by the FFN kernels
 enum { SCHED_NUNION = 0, SCHED_MTILES = 1, SCHED_SLOTS = 2, SCHED_BAD = 3, SCHED_WORDS = 8 };
