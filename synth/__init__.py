@@ -64,6 +64,9 @@ class Config:
 
 TINY = Dims(hidden=512, n_experts=16, top_k=4, inter=256, shared_inter=256)
 GLM = Dims(hidden=6144, n_experts=256, top_k=8, inter=2048, shared_inter=2048)
+# edge shapes: H not a multiple of 256 or 512, E not a multiple of 64, odd
+# counts of 128-blocks in I and H, a single-block shared expert
+ODD = Dims(hidden=640, n_experts=40, top_k=6, inter=384, shared_inter=128)
 
 CONFIGS: Dict[str, Config] = {
     # 8 rows, tiny layer, every row real
@@ -76,6 +79,8 @@ CONFIGS: Dict[str, Config] = {
     "prefill512": Config("prefill512", GLM, 512, 1001, bias_kind="zipf"),
     # large prefill over 4 independent layers
     "prefill4096x4": Config("prefill4096x4", GLM, 4096, 1004, n_layers=4, bias_kind="zipf"),
+    # edge-shape layer (parity only), 8 rows with one pad
+    "odd": Config("odd", ODD, 8, 1005, pad_slots=(3,)),
 }
 
 
