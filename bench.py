@@ -133,10 +133,12 @@ def gateup_bytes(nu, d, m):
 
 
 def down_decode_bytes(nu, d, m):
-    """Algorithmic bytes of the routed down kernel (small steps): down codes +
-    scales of the union experts, h codes + scales."""
-    H, I, K = d.hidden, d.inter, d.top_k
-    return nu * (I * H + 4 * (H // 128) * (I // 128)) + m * K * (I + 4 * (I // 128))
+    """Algorithmic bytes of the down kernel (small steps): down codes + scales
+    of the union experts, h codes + scales, the shared down weights (bf16)
+    and the shared h rows."""
+    H, I, K, Is = d.hidden, d.inter, d.top_k, d.shared_inter
+    return (nu * (I * H + 4 * (H // 128) * (I // 128)) + m * K * (I + 4 * (I // 128))
+            + H * Is * 2 + m * Is * 2)
 
 
 def front_bytes(d, m):
@@ -153,19 +155,12 @@ def select_bytes(d, m):
     return d.shared_inter * d.hidden * 2
 
 
-def post_bytes(d, m):
-    """Algorithmic bytes of the requantization launch (small steps): the
-    shared down weights (bf16) and the shared h rows."""
-    return d.hidden * d.shared_inter * 2 + m * d.shared_inter * 2
-
-
 def kernel_bytes(name, nu, d, m):
     """Algorithmic bytes per launch of the kernels that stream weights."""
     return {"gateup": gateup_bytes(nu, d, m),
             "down": down_decode_bytes(nu, d, m),
             "front": front_bytes(d, m),
-            "select_union": select_bytes(d, m),
-            "post_gateup": post_bytes(d, m)}.get(name)
+            "select_union": select_bytes(d, m)}.get(name)
 
 
 def layer_flops(d, m_real, slots):

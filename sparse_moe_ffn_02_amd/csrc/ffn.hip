@@ -219,12 +219,17 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
 // union expert's slots (at most kSmallRows).
 constexpr int kCols = 16;
 
-__global__ __launch_bounds__(256, 2) void k_down(FfnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_down(FfnArgs a, int sd_blocks) {
   const int lane = threadIdx.x & 63;
+  if ((int)blockIdx.x < sd_blocks) {
+    const int t = (int)blockIdx.x * 4 + wave_id();
+    if (t < (a.H / 16) * kSegSD) shared_down_item(a, t, lane);
+    return;
+  }
   const int c = lane & 15, kq = lane >> 4;
   const int ntH = a.H / kCols;
   const int total = a.sched[SCHED_MTILES] * ntH * kSegDN;
-  const int t = wave_item();
+  const int t = ((int)blockIdx.x - sd_blocks) * 4 + wave_id();
   if (t >= total) return;
   const int seg = t % kSegDN, it = t / kSegDN;
   const Tile tl = routed_tile(a, it / ntH);
@@ -389,11 +394,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)(hs_blocks + gu_blocks)), dim3(256), 0, s, a, hs_blocks);
     const long post_waves = (long)a.M * a.K * (a.I / kBlk);
     const int post_blocks = (int)((post_waves + 3) / 4);
+    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)post_blocks), dim3(256), 0, s, a, 0);
     const int sd_blocks = with_shared ? ((a.H / 16) * kSegSD + 3) / 4 : 0;
-    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)(sd_blocks + post_blocks)), dim3(256), 0, s, a,
-               sd_blocks);
     const long dn_items = max_union * (a.H / kCols) * kSegDN;
-    MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)((dn_items + 3) / 4)), dim3(256), 0, s, a);
+    MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)(sd_blocks + (dn_items + 3) / 4)), dim3(256), 0, s, a, sd_blocks);
   } else {
     // slot tiles: at most ceil(M*K / kMTile) + (union size), one partial tile per expert
     const long mtiles_max = ((long)a.M * a.K + kMTile - 1) / kMTile + max_union;
