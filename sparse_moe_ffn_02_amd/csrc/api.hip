@@ -187,7 +187,7 @@ Tracer g_trace;
 
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
-    "down_combine_decode", "down", "combine", "quant", "select_union", "front", "pack",
+    "down", "combine", "quant", "select_union", "front", "pack",
 };
 
 }  // namespace

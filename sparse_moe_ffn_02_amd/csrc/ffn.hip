@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
   const int e = a.union_ids[u];
   const bool col = c < a.M && row_real(a.mask, c);
   const int xr = col ? c : 0;
-  const v4f p = fp8_chain<false>(gu_row(a, e, n0, c, kq), gu_scale(a, e, n0, kq), a.xq + (size_t)xr * a.H + kq * 32,
+  const v4f p = fp8_chain(gu_row(a, e, n0, c, kq), gu_scale(a, e, n0, kq), a.xq + (size_t)xr * a.H + kq * 32,
                                  a.xs + (size_t)xr * nkb, col, seg_begin(nkb, seg, kSegGU),
                                  seg_begin(nkb, seg + 1, kSegGU));
   if (!col) return;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a, int sd_blocks) {
   const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * kCols) / kBlk) * nkb;
   const uint8_t* bp = a.hq + (size_t)(slot < 0 ? 0 : slot) * a.I + kq * 32;
   const float* shp = a.hs + (size_t)(slot < 0 ? 0 : slot) * nkb;
-  const v4f p = fp8_chain<false>(wp, swp, bp, shp, slot >= 0, seg_begin(nkb, seg, kSegDN),
+  const v4f p = fp8_chain(wp, swp, bp, shp, slot >= 0, seg_begin(nkb, seg, kSegDN),
                                  seg_begin(nkb, seg + 1, kSegDN));
   if (slot >= 0) store_f4(a.part_d + ((size_t)seg * a.M * a.K + slot) * a.H + nt * kCols + kq * 4, p);
 }

@@ -95,15 +95,13 @@ __device__ __forceinline__ v4i mask4(const v4i& v, int keep) {
 }
 
 // fp8 chain over K-blocks [kb0, kb1) for one 16x16 tile.  A (packed weight
-// tiles; wp = the lane's tile_row address at K-block 0) streams from global
-// memory through a ring; B (row-major) is read from global memory
-// (ring) or from LDS (kLdsB: a workgroup-resident copy).  Lanes with
-// bvalid == false contribute a zero B column and a zero activation scale
-// (bp must point at a readable row for every lane; the zeros come from a
-// value mask at use).  The main loop runs whole ring turns whose refills all
-// lie inside the range, so its loads are unconditional and no branch
-// separates a load from its wait; the last turns refill only what remains.
-template <bool kLdsB>
+// tiles; wp = the lane's tile_row address at K-block 0) and B (row-major)
+// stream from global memory through a ring.  Lanes with bvalid == false
+// contribute a zero B column and a zero activation scale (bp must point at a
+// readable row for every lane; the zeros come from a value mask at use).
+// The main loop runs whole ring turns whose refills all lie inside the
+// range, so its loads are unconditional and no branch separates a load from
+// its wait; the last turns refill only what remains.
 __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, const uint8_t* bp, const float* sxp,
                                          bool bvalid, int kb0, int kb1) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -117,44 +115,31 @@ __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, co
     const int kb = min(kb0 + i, last);
     wb[i] = load_frag(wp + (size_t)kb * kTile);
     swb[i] = swp[kb];
-    if (!kLdsB) {
-      xb[i] = load32(bp + kb * kBlk);
-      sxb[i] = sxp[kb];
-    }
+    xb[i] = load32(bp + kb * kBlk);
+    sxb[i] = sxp[kb];
   }
-  auto step = [&](int i, int kb) {
-    v8i x;
-    float sx;
-    if (kLdsB) {
-      x = *reinterpret_cast<const v8i*>(bp + kb * kBlk);
-      sx = sxp[kb];
-    } else {
-      x = xb[i];
-      sx = sxb[i];
-    }
-    const v4f p = mfma_fp8_k128(wb[i], mask8(x, keep));
-    scale_acc(acc, p, bvalid ? sx : 0.0f, swb[i]);
+  auto step = [&](int i) {
+    const v4f p = mfma_fp8_k128(wb[i], mask8(xb[i], keep));
+    scale_acc(acc, p, bvalid ? sxb[i] : 0.0f, swb[i]);
   };
   auto refill = [&](int i, int nk) {
     wb[i] = load_frag(wp + (size_t)nk * kTile);
     swb[i] = swp[nk];
-    if (!kLdsB) {
-      xb[i] = load32(bp + nk * kBlk);
-      sxb[i] = sxp[nk];
-    }
+    xb[i] = load32(bp + nk * kBlk);
+    sxb[i] = sxp[nk];
   };
   int k0 = kb0;
   for (; k0 + 2 * kRing <= kb1; k0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
-      step(i, k0 + i);
+      step(i);
       refill(i, k0 + i + kRing);
     }
   }
   for (; k0 < kb1; k0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
-      if (k0 + i < kb1) step(i, k0 + i);
+      if (k0 + i < kb1) step(i);
       if (k0 + i + kRing < kb1) refill(i, k0 + i + kRing);
     }
   }

@@ -82,7 +82,7 @@ struct FfnArgs {
 // Kernel ids reported by the timing hook (moe_trace_set).
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
-  KID_DOWN_DECODE, KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COUNT
+  KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COUNT
 };
 
 void trace_before(hipStream_t s);
