@@ -201,6 +201,110 @@ def cpu_info():
     return threads, model
 
 
+def graph_replay_us(torch, step, n_graphs, steps, warmup, rt_lib, stream):
+    """One captured step per weight replica, replayed in rotation.  Returns the
+    mean us per step over `steps` back-to-back replays and the p10/p50/p90 of
+    single replays (each bracketed by its own events)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n_graphs):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for i in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % n_graphs].replay()
+    torch.cuda.synchronize()
+    ev = HipEvents(2 + 2 * steps)
+    rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+    for i in range(steps):
+        graphs[i % n_graphs].replay()
+    rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+    torch.cuda.synchronize()
+    mean_us = 1e3 * ev.elapsed_ms(ev.ev[0], ev.ev[1]) / steps
+    for i in range(steps):
+        rt_lib.hipEventRecord(ev.ev[2 + 2 * i], C.c_void_p(stream))
+        graphs[i % n_graphs].replay()
+        rt_lib.hipEventRecord(ev.ev[3 + 2 * i], C.c_void_p(stream))
+    torch.cuda.synchronize()
+    each = np.array([1e3 * ev.elapsed_ms(ev.ev[2 + 2 * i], ev.ev[3 + 2 * i]) for i in range(steps)])
+    ev.close()
+    del graphs
+    p10, p50, p90 = (float(np.percentile(each, q)) for q in (10, 50, 90))
+    return mean_us, p10, p50, p90
+
+
+def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
+    """Layer time against the row count on the span-8 layer (one committed row
+    plus drafts, the same recipe at every count): the small-step path serves
+    up to 16 rows, the tiled path from 17."""
+    out = []
+    for m in (1, 2, 4, 8, 9, 12, 16, 17, 24, 32, 48, 64):
+        cfg = synth.with_rows(synth.CONFIGS["span8"], m)
+        x_np, mask_np = synth.activations(cfg)
+        x = torch.from_numpy(x_np.view(np.int16)).cuda()
+        mask = torch.from_numpy(mask_np).cuda()
+        ws = moe.workspace(md, m)
+        y = torch.empty((m, d.hidden), dtype=torch.int16, device="cuda")
+        rt = moe.Routing.empty(md, m)
+
+        def step(i):
+            r = reps[i % len(reps)]
+            moe.layer(md, x, mask, r["router_w"], r["bias"], r["experts"], r["shared"], y, rt, ws)
+
+        us, p10, p50, p90 = graph_replay_us(torch, step, len(reps), steps, warmup, rt_lib, stream)
+        nu = int(rt.n_union.item())
+        rb, fb = decode_bytes(nu, d, m)
+        out.append({"rows": m, "path": "split" if m <= 16 else "tiled", "union_experts": nu, "us": round(us, 2),
+                    "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                    "gbs": round((rb + fb) / (us * 1e-6) / 1e9, 1)})
+        log(f"[bench] rows sweep M={m}: {us:.1f} us, |U|={nu}, {(rb + fb) / (us * 1e-6) / 1e9:.0f} GB/s")
+    return out
+
+
+def tp8_rank_sweep(torch, moe, synth, rt_lib, stream, steps, warmup, replicas):
+    """One TP8 rank's share of the layer on one GPU: every expert's I/8 = 256
+    slice (shared expert likewise), span-decode token counts 1..10, no
+    collective (the rank's partial outputs are what it would reduce-scatter)."""
+    cfg0 = synth.CONFIGS["tp8rank"]
+    d = cfg0.dims
+    md = moe.Dims(d.hidden, d.n_experts, d.top_k, d.inter, d.shared_inter, d.routed_scale)
+    t0 = time.time()
+    reps = device_layer(cfg0, 0, torch, moe, replicas=replicas)
+    log(f"[bench] tp8-rank layer (I={d.inter}) ready in {time.time() - t0:.1f}s")
+    out = []
+    for m in (1, 2, 4, 5, 6, 8, 9, 10):
+        cfg = synth.with_rows(cfg0, m)
+        x_np, mask_np = synth.activations(cfg)
+        x = torch.from_numpy(x_np.view(np.int16)).cuda()
+        mask = torch.from_numpy(mask_np).cuda()
+        ws = moe.workspace(md, m)
+        y = torch.empty((m, d.hidden), dtype=torch.int16, device="cuda")
+        rt = moe.Routing.empty(md, m)
+
+        def step(i):
+            r = reps[i % len(reps)]
+            moe.layer(md, x, mask, r["router_w"], r["bias"], r["experts"], r["shared"], y, rt, ws)
+
+        us, p10, p50, p90 = graph_replay_us(torch, step, len(reps), steps, warmup, rt_lib, stream)
+        nu = int(rt.n_union.item())
+        rb, fb = decode_bytes(nu, d, m)
+        out.append({"tokens": m, "union_experts": nu, "us": round(us, 2), "us_p10": round(p10, 2),
+                    "us_p90": round(p90, 2), "gbs": round((rb + fb) / (us * 1e-6) / 1e9, 1)})
+        log(f"[bench] tp8-rank M={m}: {us:.1f} us, |U|={nu}, {(rb + fb) / (us * 1e-6) / 1e9:.0f} GB/s")
+    del reps
+    torch.cuda.empty_cache()
+    return {"workload": "one TP8 rank's share on one GPU: hidden 6144, 256 experts top-8, expert inter 256 "
+                        "(I/8) fp8 e4m3 128x128 scales, shared expert inter 256 bf16, span-decode rows "
+                        "(1 committed + drafts), weights rotated over device replicas, no collective",
+            "points": out}
+
+
 def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
     """4096-token prefill chunk over `args.prefill_layers` stacked layers."""
     pcfg = synth.CONFIGS["prefill4096x4"]
@@ -269,6 +373,7 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="only the prefill part (profiling)")
     ap.add_argument("--prefill-layers", type=int, default=4, help="stacked layers of the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweeps", action="store_true", help="skip the row-count and TP8-rank sweeps")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -347,30 +452,12 @@ def main():
         f"{total_b / (ms_eager * 1e-3) / 1e9:.0f} GB/s")
 
     # graph replay: one captured step per weight replica, replayed in rotation
-    graphs = []
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(len(reps)):
-            step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    for i in range(len(reps)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
-    rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
-    torch.cuda.synchronize()
-    ms_step = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.steps
+    us_step, us_p10, us_p50, us_p90 = graph_replay_us(torch, step, len(reps), args.steps, args.warmup, rt_lib,
+                                                      stream)
+    ms_step = us_step * 1e-3
     gbs = total_b / (ms_step * 1e-3) / 1e9
-    log(f"[bench] span8 graph replay: {ms_step * 1e3:.1f} us/step -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak)")
-    del graphs
+    log(f"[bench] span8 graph replay: {ms_step * 1e3:.1f} us/step (single replays p10/p50/p90 "
+        f"{us_p10:.1f}/{us_p50:.1f}/{us_p90:.1f}) -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak)")
 
     # traced pass: per-kernel HIP events, same steps, same stream
     nk = 16
@@ -417,6 +504,7 @@ def main():
                    "rows": M, "union_experts": nu, "slots": slots, "seed": cfg.seed},
         "layer_us": round(ms_step * 1e3, 2),
         "layer_us_eager": round(ms_eager * 1e3, 2),
+        "layer_us_single_replay_p10_p50_p90": [round(us_p10, 2), round(us_p50, 2), round(us_p90, 2)],
         "timing": "hipGraph replay of one moe_layer call per step (eager launches also reported)",
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "bytes_per_step": total_b,
@@ -457,8 +545,14 @@ def main():
                                             f"{model}; float64 numpy",
                                   "seconds": round(cpu_s, 3)}
         log(f"[bench] oracle: {cpu_s:.2f} s")
+    if not args.no_sweeps:
+        result["rows_sweep"] = rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, min(args.steps, 100),
+                                          args.warmup)
     del reps
     torch.cuda.empty_cache()
+    if not args.no_sweeps:
+        result["tp8_rank_sweep"] = tp8_rank_sweep(torch, moe, synth, rt_lib, stream, min(args.steps, 100),
+                                                  args.warmup, args.replicas)
 
     if not args.no_prefill:
         result["prefill"] = prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream)

@@ -9,7 +9,7 @@ namespace moe {
 
 constexpr int kMTile = 128;          // slots (or rows) per tile of the tiled grouped GEMMs
 constexpr int kDecodeMaxRows = 16;  // rows served by the small-step router kernels
-constexpr int kSmallRows = 8;       // rows served by the split small-step expert kernels
+constexpr int kSmallRows = 16;      // rows served by the split small-step expert kernels (one MFMA column each)
 constexpr int kUChunks = 64;        // row chunks of the larger-step union
 // Every GEMM element is the fixed-order sum of its K-segment chains:
 // routed gate/up over kSegGU segments of K = H, shared gate/up over kSegSG,

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
 }
 
 // The front of a split small step (M <= kSmallRows), one launch:
-//   blocks [0, E)             logits of expert b, wave = row
+//   blocks [0, E)             logits of expert b, wave w: rows w, w + 8
 //   blocks [E, E + nq)        x quantization, one (row, 128-block) per wave
 //   blocks [E + nq, ...)      shared expert gate/up, one K segment of one
 //                             8-column tile per wave (fp32 partials)
@@ -377,15 +377,16 @@ __device__ __forceinline__ void shared_gu_item(const FfnArgs& f, int t, int seg0
   if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + (kq >> 1)) * f.Is + n0 + (kq & 1) * 4, p);
 }
 
-// Split steps, first launch: blocks [0, E) logits (one block per expert, one
-// wave per row); then the x quantization; then the shared expert's gate/up
+// Split steps, first launch: blocks [0, E) logits (one block per expert, wave
+// w serving rows w, w + 8); then the x quantization; then the shared expert's gate/up
 // for the first half of its K segments (the second half runs beside the
 // top-k in k_select_union_small).
 __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int b = blockIdx.x;
   if (b < r.E) {
-    if (wave < r.M && (r.mask == nullptr || r.mask[wave] != 0)) logit_row(r, wave, b, lane);
+    for (int row = wave; row < r.M; row += 8)
+      if (r.mask == nullptr || r.mask[row] != 0) logit_row(r, row, b, lane);
     return;
   }
   if (b < r.E + nq) {

@@ -67,6 +67,9 @@ GLM = Dims(hidden=6144, n_experts=256, top_k=8, inter=2048, shared_inter=2048)
 # edge shapes: H not a multiple of 256 or 512, E not a multiple of 64, odd
 # counts of 128-blocks in I and H, a single-block shared expert
 ODD = Dims(hidden=640, n_experts=40, top_k=6, inter=384, shared_inter=128)
+# one TP8 rank's share of the GLM layer: every expert's (and the shared
+# expert's) inter slice of 2048 / 8
+TP8R = Dims(hidden=6144, n_experts=256, top_k=8, inter=256, shared_inter=256)
 
 CONFIGS: Dict[str, Config] = {
     # 8 rows, tiny layer, every row real
@@ -81,6 +84,8 @@ CONFIGS: Dict[str, Config] = {
     "prefill4096x4": Config("prefill4096x4", GLM, 4096, 1004, n_layers=4, bias_kind="zipf"),
     # edge-shape layer (parity only), 8 rows with one pad
     "odd": Config("odd", ODD, 8, 1005, pad_slots=(3,)),
+    # one TP8 rank's share, span-decode rows (token count set per use)
+    "tp8rank": Config("tp8rank", TP8R, 10, 1006, row_kind="span"),
 }
 
 
