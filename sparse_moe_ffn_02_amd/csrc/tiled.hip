@@ -3,16 +3,18 @@
 // A workgroup of eight waves computes one tile of kTM = 128 slots (routed
 // experts) or rows (shared expert) by the tile's output columns:
 //   gate/up: 128 h columns, i.e. 128 gate rows and 128 up rows of the weights;
-//   down:    256 columns of H.
+//   down:    256 columns of H (shared expert) or 512 (routed experts).
 // Each wave owns 32 weight rows (two 16-row MFMA tiles; for gate/up the gate
-// and the up rows of the same 16 h columns), streams them from global memory
+// and the up rows of the same 16 h columns; 64 rows in the routed down tiles,
+// see the wide tiles below), streams them from global memory
 // straight into MFMA operand registers two K stages ahead, and applies them to
 // all 128 slots (eight 16-column MFMA tiles).  The tile's activation rows,
 // which all eight waves read, are staged through a double-buffered LDS ring.
 // The weight rows of one (expert, column tile) are shared by the expert's
 // slot tiles; their blocks are numbered so that they land on the same XCD
 // (blocks are dealt to the 8 XCDs round-robin and the column-tile count is a
-// multiple of 8), where the L2 serves the re-reads.
+// multiple of 8), where the L2 serves the re-reads.  The routed down tiles
+// (12 of them at H = 6144) do not have that alignment.
 //
 // Every output element follows the same procedure as in the small-step
 // kernels: one fp8 16x16x128 MFMA per 128-deep K-block scaled into a fp32
@@ -271,6 +273,137 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
 #undef MOE_TILE_STEP
 }
 
+// ---------------------------------------------------------------- fp8 wide tiles
+// The routed down tiles (one K segment) give each wave a wider register tile:
+// 4 weight tiles (64 weight rows) by the 8 slot tiles, so every activation
+// fragment read from LDS feeds 4 MFMAs instead of 2, the LDS bytes and
+// barriers per MFMA halve, and each wave keeps twice the weight bytes in
+// flight.  Its 128 accumulators leave no room for a second (segment) set, so
+// the form serves the one-segment down GEMM; gate/up (two segments) keeps the
+// tile above.
+constexpr int kWA = 4;                                                // 16-row weight tiles per wave
+constexpr int kWBV = kTM * kStageBytes / kTileThreads / 16;           // 16-byte activation loads per thread per K-block
+constexpr int kWBRow = kTileThreads / 8;                              // rows between a thread's loads
+constexpr int kWBuf = kTM * kLdsRow;                                  // one activation stage in LDS
+constexpr int kWLdsB = 2 * kWBuf;                                     // double buffer
+constexpr int kWLds = kWLdsB + 2 * kTM * (int)sizeof(float);         // + the activation scales
+
+struct WideIn {
+  const uint8_t* a[kWA];  // per lane: packed-tile address of each weight tile at K-block 0
+  const float* sw;        // weight scales of the wave's 64 rows (one 128-row block), indexed by K-block
+  const uint8_t* b[kWBV]; // per thread: activation row part at K-block 0 (always a valid row)
+  bool bok[kWBV];         // those rows are real (else they contribute zeros)
+  const float* bs;        // scale row of thread tid < kTM (always valid)
+  bool bsok;
+  int nkb;                // K-blocks
+};
+
+struct WStage {
+  v8i v[kWA];
+  float s;
+};
+
+struct WB {
+  uint4 v[kWBV];
+  float s;
+};
+
+using WAcc = v4f[kWA][kNB];
+
+__device__ __forceinline__ void wide_load_a(WStage& d, const WideIn& in, int kb) {
+  d.s = in.sw[kb];
+#pragma unroll
+  for (int t = 0; t < kWA; ++t) d.v[t] = load_frag(in.a[t] + (size_t)kb * kTile);
+}
+
+__device__ __forceinline__ void wide_load_b(WB& r, const WideIn& in, int kb) {
+#pragma unroll
+  for (int i = 0; i < kWBV; ++i) r.v[i] = ld16(in.b[i] + (size_t)kb * kStageBytes);
+  r.s = in.bs[kb];
+}
+
+// Write a thread's activation registers (and scale) to stage buffer `buf`;
+// rows out of range become zero codes and a zero scale.
+__device__ __forceinline__ void wide_store_b(uint8_t* smem, int buf, const WB& r, const WideIn& in) {
+  const int tid = threadIdx.x;
+  uint8_t* base = smem + buf * kWBuf;
+#pragma unroll
+  for (int i = 0; i < kWBV; ++i) {
+    const uint32_t keep = in.bok[i] ? 0xFFFFFFFFu : 0u;
+    const uint4 v = r.v[i];
+    *reinterpret_cast<uint4*>(base + (tid / 8 + kWBRow * i) * kLdsRow + (tid % 8) * 16) =
+        make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+  }
+  if (tid < kTM) {
+    const float sv = r.s;
+    reinterpret_cast<float*>(smem + kWLdsB)[buf * kTM + tid] = in.bsok ? sv : 0.0f;
+  }
+}
+
+// One K-block on stage buffer `buf`: 32 MFMAs, each partial scaled into its
+// chain as in every other kernel.
+__device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const WStage& as, WAcc& acc) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const uint8_t* lb = smem + buf * kWBuf;
+  const float* ls = reinterpret_cast<const float*>(smem + kWLdsB) + buf * kTM;
+  const float sw = as.s;
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    const uint8_t* src = lb + (16 * b + c) * kLdsRow + q * 32;
+    const uint4 lo = ld16(src), hi = ld16(src + 16);
+    const v8i xb = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const float sx = ls[16 * b + c];
+    v4f p0 = mfma_fp8_raw(as.v[0], xb), p1 = mfma_fp8_raw(as.v[1], xb);
+    v4f p2 = mfma_fp8_raw(as.v[2], xb), p3 = mfma_fp8_raw(as.v[3], xb);
+    settle4(p0, p1, p2, p3);
+    scale_acc(acc[0][b], p0, sx, sw);
+    scale_acc(acc[1][b], p1, sx, sw);
+    scale_acc(acc[2][b], p2, sx, sw);
+    scale_acc(acc[3][b], p3, sx, sw);
+    // pin the chain updates here: left free, the compiler sinks them below
+    // later MFMAs and keeps every partial of the K-block live at once
+    asm volatile("" : "+v"(acc[0][b]), "+v"(acc[1][b]), "+v"(acc[2][b]), "+v"(acc[3][b]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The K loop of one wide tile: acc = the element chains over all K-blocks.
+// Weight fragments are loaded two K-blocks ahead into registers; a thread's
+// activation rows one K-block ahead into registers, then into the LDS double
+// buffer.  Loads past the last K-block reload it (valid, unused), so every
+// step issues the same loads with no branch around them.
+__device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc& acc) {
+  const int n = in.nkb, last = n - 1;
+#pragma unroll
+  for (int t = 0; t < kWA; ++t)
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) acc[t][b] = v4f{0.f, 0.f, 0.f, 0.f};
+  WStage ar0, ar1;
+  WB br;
+  wide_load_a(ar0, in, 0);
+  wide_load_a(ar1, in, min(1, last));
+  wide_load_b(br, in, 0);
+  wide_store_b(smem, 0, br, in);
+  wide_load_b(br, in, min(1, last));
+  __syncthreads();
+#define MOE_WIDE_STEP(S, D, AR)                         \
+  {                                                     \
+    wide_stage(smem, (D), AR, acc);                     \
+    wide_load_a(AR, in, min((S) + 2, last));            \
+    wide_store_b(smem, (D) ^ 1, br, in);                \
+    wide_load_b(br, in, min((S) + 2, last));            \
+    __syncthreads();                                    \
+  }
+  // pairs of steps (the ring indices are compile-time), then an odd last step
+  int s0 = 0;
+  for (; s0 + 2 <= n; s0 += 2) {
+    MOE_WIDE_STEP(s0, 0, ar0)
+    MOE_WIDE_STEP(s0 + 1, 1, ar1)
+  }
+  if (s0 < n) MOE_WIDE_STEP(s0, 0, ar0)
+#undef MOE_WIDE_STEP
+}
+
 // ---------------------------------------------------------------- gate/up
 // Blocks [0, n_sh): shared-expert tiles (row tile, 128-column tile); then
 // routed tiles (slot tile of one expert, 128-column tile).  Wave w holds the
@@ -374,16 +507,24 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- down
-// Blocks [0, n_sh): shared-expert tiles (row tile, 256-column tile of H);
-// then routed tiles (slot tile of one expert, 256-column tile).  Wave w holds
-// output columns n0 + 32 w .. + 31 (A tiles 0 and 1).
+// Blocks [0, n_sh): shared-expert tiles (row tile, 256-column tile of H;
+// wave w holds output columns n0 + 32 w .. + 31, A tiles 0 and 1); then
+// routed wide tiles (slot tile of one expert, 512-column tile).
 constexpr int kDnCols = 32 * kWaves;
 
+// Routed tiles: 512 columns of H (wave w: columns n0 + 64 w .. + 63, weight
+// tiles 0-3), one K segment over the whole I.
+static_assert(kSegDN == 1, "the routed down tiles run one K segment per wave");
+constexpr int kDnColsW = 16 * kWA * kWaves;
+constexpr int kDnLds = kWLds > (int)sizeof(TileLds) ? kWLds : (int)sizeof(TileLds);
+
 __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
-  __shared__ TileLds L;
+  __shared__ __align__(16) uint8_t smem[kDnLds];
+  TileLds& L = *reinterpret_cast<TileLds*>(smem);
   const int ntH = (a.H + kDnCols - 1) / kDnCols;
+  const int ntW = (a.H + kDnColsW - 1) / kDnColsW;
   const int n_sh = a.Is > 0 ? ((a.M + kTM - 1) / kTM) * ntH : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntH;
+  const int total = n_sh + a.sched[SCHED_MTILES] * ntW;
   const int bid = blockIdx.x;
   if (bid >= total) return;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
@@ -421,37 +562,34 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
     return;
   }
   const int rb = bid - n_sh;
-  const int nt = rb % ntH;
-  const Tile tl = routed_tile(a, rb / ntH);
-  const int n0 = nt * kDnCols + 32 * w;
+  const int nt = rb % ntW;
+  const Tile tl = routed_tile(a, rb / ntW);
+  const int n0 = nt * kDnColsW + 16 * kWA * w;
   const int nkb = a.I / kBlk;
-  TileIn in;
-  const int nr = n0 < a.H ? n0 : a.H - 32;
+  // waves past H compute on in-range rows and store nothing
+  const int nr = n0 < a.H ? n0 : a.H - 16 * kWA;
+  WideIn in;
 #pragma unroll
-  for (int t = 0; t < kNA; ++t) {
-    in.a[t] = tile_row(a.wd, (size_t)tl.e * a.H + nr + 16 * t + c, nkb, q);
-    in.sw[t] = a.sd + ((size_t)tl.e * (a.H / kBlk) + nr / kBlk) * nkb;
-  }
-  {
+  for (int t = 0; t < kWA; ++t) in.a[t] = tile_row(a.wd, (size_t)tl.e * a.H + nr + 16 * t + c, nkb, q);
+  in.sw = a.sd + ((size_t)tl.e * (a.H / kBlk) + nr / kBlk) * nkb;
 #pragma unroll
-    for (int v = 0; v < kBVec; ++v) {
-      const int i = tid / 8 + kBRowStep * v;
-      in.bok[v] = i < tl.mcnt;
-      in.b[v] = a.hq + (size_t)(tl.s0 + (in.bok[v] ? i : 0)) * a.I + (tid % 8) * 16;
-    }
-    in.bsok = tid < kTM && tid < tl.mcnt;
-    in.bs = a.hs + (size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb;
+  for (int v = 0; v < kWBV; ++v) {
+    const int i = tid / 8 + kWBRow * v;
+    in.bok[v] = i < tl.mcnt;
+    in.b[v] = a.hq + (size_t)(tl.s0 + (in.bok[v] ? i : 0)) * a.I + (tid % 8) * 16;
   }
-  in.nstage = nkb;
-  in.nseg = kSegDN;
-  tile_gemm<true, 2>(in, L, tot);
+  in.bsok = tid < kTM && tid < tl.mcnt;
+  in.bs = a.hs + (size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb;
+  in.nkb = nkb;
+  WAcc acc;
+  wide_gemm(in, smem, acc);
   if (n0 >= a.H) return;
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
     const int i = 16 * b + c;
     if (i >= tl.mcnt) continue;
 #pragma unroll
-    for (int t = 0; t < kNA; ++t) store_f4(a.D + (size_t)(tl.s0 + i) * a.H + n0 + 16 * t + 4 * q, tot[t][b]);
+    for (int t = 0; t < kWA; ++t) store_f4(a.D + (size_t)(tl.s0 + i) * a.H + n0 + 16 * t + 4 * q, acc[t][b]);
   }
 }
 
@@ -460,7 +598,8 @@ hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s) {
   const long gu = sh_tiles * (a.Is / kBlk) + mtiles_max * (a.I / kBlk);
   MOE_LAUNCH(KID_GATEUP, k_gateup_tiled, dim3((unsigned)gu), dim3(kTileThreads), 0, s, a);
   const long ntH = (a.H + kDnCols - 1) / kDnCols;
-  const long dn = (sh_tiles + mtiles_max) * ntH;
+  const long ntW = (a.H + kDnColsW - 1) / kDnColsW;
+  const long dn = sh_tiles * ntH + mtiles_max * ntW;
   MOE_LAUNCH(KID_DOWN, k_down_tiled, dim3((unsigned)dn), dim3(kTileThreads), 0, s, a);
   return hipSuccess;
 }
