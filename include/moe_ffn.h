@@ -63,13 +63,15 @@ extern "C" {
 /* status codes */
 #define MOE_OK 0
 #define MOE_EINVAL 1       /* null required pointer, bad dims, misaligned pointer, M < 0 */
-#define MOE_EUNSUPPORTED 2 /* n_experts > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOPK or > n_experts, M > MOE_MAX_ROWS */
+#define MOE_EUNSUPPORTED 2 /* n_experts > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOPK or > n_experts, M > MOE_MAX_ROWS,
+                              inter > MOE_MAX_INTER */
 #define MOE_EWORKSPACE 3   /* ws_bytes smaller than moe_workspace_bytes() for this M */
 #define MOE_ELAUNCH 4      /* a kernel launch failed (hipGetLastError after each launch) */
 
 #define MOE_MAX_ROWS 16384
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_INTER 8192 /* keeps every byte offset into the [M*top_k, inter] activation codes below 2^31 */
 
 /* Layer dimensions (host struct).  hidden, inter and shared_inter must be
  * multiples of 128; shared_inter may be 0 (no shared expert). */

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = range(5)
-MAX_ROWS, MAX_EXPERTS, MAX_TOPK = 16384, 256, 16
+MAX_ROWS, MAX_EXPERTS, MAX_TOPK, MAX_INTER = 16384, 256, 16, 8192
 
 
 class MoeError(RuntimeError):

@@ -62,6 +62,7 @@ int check_dims(const moe_dims* d) {
   if (d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
   if (!isfinite(d->routed_scale)) return MOE_EINVAL;
   if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK || d->top_k > d->n_experts) return MOE_EUNSUPPORTED;
+  if (d->inter > MOE_MAX_INTER) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

@@ -156,6 +156,19 @@ __device__ __forceinline__ void close_segments(SegState& g, int done, Acc& acc, 
   }
 }
 
+// MFMA B fragments (and activation scales) of slot tiles b and b + 1 from an
+// LDS activation stage: lane (q, c) takes 32 bytes of row 16 b + c at 32 q.
+__device__ __forceinline__ void lds_frag_pair(const uint8_t* lb, const float* ls, int b, int c, int q, v8i (&x)[2],
+                                              float (&s)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint8_t* src = lb + (16 * (b + j) + c) * kLdsRow + q * 32;
+    const uint4 lo = ld16(src), hi = ld16(src + 16);
+    x[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    s[j] = ls[16 * (b + j) + c];
+  }
+}
+
 // One K stage on LDS buffer `buf` with A fragments `a`.
 template <bool kFp8>
 __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const AStage& as, int st, Acc& acc, Acc& tot,
@@ -164,17 +177,15 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
   const v8i(&a)[kNA] = as.v;
   if (kFp8) {
     const float sw0 = as.s[0], sw1 = as.s[1];
+    // The fragments of the next pair of slot tiles are read from LDS while
+    // the MFMAs of this pair run, so the LDS latency is not waited out once
+    // per pair.
+    v8i xb[2], xn[2];
+    float sx[2], sxn[2];
+    lds_frag_pair(L.b[buf], L.s[buf], 0, c, q, xb, sx);
 #pragma unroll
     for (int b = 0; b < kNB; b += 2) {
-      v8i xb[2];
-      float sx[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint8_t* src = &L.b[buf][(16 * (b + j) + c) * kLdsRow + q * 32];
-        const uint4 lo = ld16(src), hi = ld16(src + 16);
-        xb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sx[j] = L.s[buf][16 * (b + j) + c];
-      }
+      if (b + 2 < kNB) lds_frag_pair(L.b[buf], L.s[buf], b + 2, c, q, xn, sxn);
       v4f p0 = mfma_fp8_raw(a[0], xb[0]), p1 = mfma_fp8_raw(a[1], xb[0]);
       v4f p2 = mfma_fp8_raw(a[0], xb[1]), p3 = mfma_fp8_raw(a[1], xb[1]);
       settle4(p0, p1, p2, p3);
@@ -182,21 +193,32 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
       scale_acc(acc[1][b], p1, sx[0], sw1);
       scale_acc(acc[0][b + 1], p2, sx[1], sw0);
       scale_acc(acc[1][b + 1], p3, sx[1], sw1);
-      __builtin_amdgcn_sched_barrier(0);     // keep one pair of slot tiles' operands live at a time
+      asm volatile("" : "+v"(acc[0][b]), "+v"(acc[1][b]), "+v"(acc[0][b + 1]), "+v"(acc[1][b + 1]));
+      if (b + 2 < kNB) {
+        xb[0] = xn[0];
+        xb[1] = xn[1];
+        sx[0] = sxn[0];
+        sx[1] = sxn[1];
+      }
+      __builtin_amdgcn_sched_barrier(0);     // one pair in flight, the next pair's fragments loading
     }
     close_segments<true>(g, st + 1, acc, tot);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      // the next slot tile's fragment is read while this tile's MFMAs run
+      uint4 xv = ld16(&L.b[buf][c * kLdsRow + j * 64 + q * 16]);
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
-        const uint4 xv = ld16(&L.b[buf][(16 * b + c) * kLdsRow + j * 64 + q * 16]);
+        uint4 xnv = xv;
+        if (b + 1 < kNB) xnv = ld16(&L.b[buf][(16 * (b + 1) + c) * kLdsRow + j * 64 + q * 16]);
         const v4i xb = {(int)xv.x, (int)xv.y, (int)xv.z, (int)xv.w};
 #pragma unroll
         for (int t = 0; t < kNA; ++t) {
           const v4i ah = {a[t][4 * j], a[t][4 * j + 1], a[t][4 * j + 2], a[t][4 * j + 3]};
           acc[t][b] = mfma_bf16_k32(ah, xb, acc[t][b]);
         }
+        xv = xnv;
         __builtin_amdgcn_sched_barrier(0);
       }
       close_segments<false>(g, 2 * st + j + 1, acc, tot);
@@ -289,11 +311,17 @@ constexpr int kWLdsB = 2 * kWBuf;                                     // double 
 constexpr int kWLds = kWLdsB + 2 * kTM * (int)sizeof(float);         // + the activation scales
 
 struct WideIn {
-  const uint8_t* a[kWA];  // per lane: packed-tile address of each weight tile at K-block 0
+  const uint8_t* a;       // per lane: packed-tile address of weight tile 0 at K-block 0
+  long astep;             // bytes from one weight tile (16 rows) to the next
   const float* sw;        // weight scales of the wave's 64 rows (one 128-row block), indexed by K-block
-  const uint8_t* b[kWBV]; // per thread: activation row part at K-block 0 (always a valid row)
+  // Activation rows and scales as one uniform base plus 32-bit per-thread
+  // offsets (fewer registers than 64-bit pointers; the offsets stay below
+  // 2^32 for every supported row count).
+  const uint8_t* bbase;
+  uint32_t boff[kWBV];    // per thread: byte offset of its activation row part at K-block 0 (a valid row)
   bool bok[kWBV];         // those rows are real (else they contribute zeros)
-  const float* bs;        // scale row of thread tid < kTM (always valid)
+  const float* sbase;
+  uint32_t soff;          // scale row of thread tid < kTM, in floats (a valid row)
   bool bsok;
   int nkb;                // K-blocks
 };
@@ -313,13 +341,13 @@ using WAcc = v4f[kWA][kNB];
 __device__ __forceinline__ void wide_load_a(WStage& d, const WideIn& in, int kb) {
   d.s = in.sw[kb];
 #pragma unroll
-  for (int t = 0; t < kWA; ++t) d.v[t] = load_frag(in.a[t] + (size_t)kb * kTile);
+  for (int t = 0; t < kWA; ++t) d.v[t] = load_frag(in.a + t * in.astep + (long)kb * kTile);
 }
 
 __device__ __forceinline__ void wide_load_b(WB& r, const WideIn& in, int kb) {
 #pragma unroll
-  for (int i = 0; i < kWBV; ++i) r.v[i] = ld16(in.b[i] + (size_t)kb * kStageBytes);
-  r.s = in.bs[kb];
+  for (int i = 0; i < kWBV; ++i) r.v[i] = ld16(in.bbase + (in.boff[i] + (uint32_t)kb * kStageBytes));
+  r.s = in.sbase[in.soff + (uint32_t)kb];
 }
 
 // Write a thread's activation registers (and scale) to stage buffer `buf`;
@@ -347,12 +375,19 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
   const uint8_t* lb = smem + buf * kWBuf;
   const float* ls = reinterpret_cast<const float*>(smem + kWLdsB) + buf * kTM;
   const float sw = as.s;
-#pragma unroll
-  for (int b = 0; b < kNB; ++b) {
+  // the next slot tile's fragment is read from LDS while this tile's MFMAs run
+  auto frag = [&](int b, v8i& x, float& sx) {
     const uint8_t* src = lb + (16 * b + c) * kLdsRow + q * 32;
     const uint4 lo = ld16(src), hi = ld16(src + 16);
-    const v8i xb = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    const float sx = ls[16 * b + c];
+    x = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    sx = ls[16 * b + c];
+  };
+  v8i xb, xn;
+  float sx, sxn;
+  frag(0, xb, sx);
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    if (b + 1 < kNB) frag(b + 1, xn, sxn);
     v4f p0 = mfma_fp8_raw(as.v[0], xb), p1 = mfma_fp8_raw(as.v[1], xb);
     v4f p2 = mfma_fp8_raw(as.v[2], xb), p3 = mfma_fp8_raw(as.v[3], xb);
     settle4(p0, p1, p2, p3);
@@ -363,6 +398,10 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
     // pin the chain updates here: left free, the compiler sinks them below
     // later MFMAs and keeps every partial of the K-block live at once
     asm volatile("" : "+v"(acc[0][b]), "+v"(acc[1][b]), "+v"(acc[2][b]), "+v"(acc[3][b]));
+    if (b + 1 < kNB) {
+      xb = xn;
+      sx = sxn;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -470,7 +509,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   }
   in.nstage = nkb;
   in.nseg = kSegGU;
-  tile_gemm<true, 3>(in, L, tot);
+  tile_gemm<true, 2>(in, L, tot);
   // h = silu(G) U in place of G; 1x128 requantization over the tile's 128 columns
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
@@ -569,17 +608,19 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   // waves past H compute on in-range rows and store nothing
   const int nr = n0 < a.H ? n0 : a.H - 16 * kWA;
   WideIn in;
-#pragma unroll
-  for (int t = 0; t < kWA; ++t) in.a[t] = tile_row(a.wd, (size_t)tl.e * a.H + nr + 16 * t + c, nkb, q);
+  in.a = tile_row(a.wd, (size_t)tl.e * a.H + nr + c, nkb, q);
+  in.astep = (long)nkb * kTile;
   in.sw = a.sd + ((size_t)tl.e * (a.H / kBlk) + nr / kBlk) * nkb;
 #pragma unroll
   for (int v = 0; v < kWBV; ++v) {
     const int i = tid / 8 + kWBRow * v;
     in.bok[v] = i < tl.mcnt;
-    in.b[v] = a.hq + (size_t)(tl.s0 + (in.bok[v] ? i : 0)) * a.I + (tid % 8) * 16;
+    in.boff[v] = (uint32_t)((size_t)(tl.s0 + (in.bok[v] ? i : 0)) * a.I + (tid % 8) * 16);
   }
+  in.bbase = a.hq;
   in.bsok = tid < kTM && tid < tl.mcnt;
-  in.bs = a.hs + (size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb;
+  in.sbase = a.hs;
+  in.soff = (uint32_t)((size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb);
   in.nkb = nkb;
   WAcc acc;
   wide_gemm(in, smem, acc);

@@ -109,6 +109,7 @@ def _layer(lib, d, m, *, x=FAKE, router=None, experts=None, shared=None, y=FAKE,
     (dict(n_experts=512), L.MOE_EUNSUPPORTED),
     (dict(top_k=17), L.MOE_EUNSUPPORTED),
     (dict(n_experts=4, top_k=8), L.MOE_EUNSUPPORTED),
+    (dict(inter=L.MAX_INTER + 128), L.MOE_EUNSUPPORTED),
 ])
 def test_layer_rejects_bad_dims(lib, kw, status):
     assert _layer(lib, _dims(**kw), 8) == status
