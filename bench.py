@@ -517,6 +517,31 @@ def main():
                      "algorithmic_bytes": dom_bytes, "kernel_us": round(kern_us[dom], 2)},
     }
 
+    # ---------------- the layer with the next layer's residual add + RMSNorm, unfused and fused
+    res_np, gam_np = synth.norm_inputs(cfg, rows=M)
+    res = torch.from_numpy(res_np.view(np.int16)).cuda()
+    gam = torch.from_numpy(gam_np.view(np.int16)).cuda()
+    r_out = torch.empty_like(res)
+    n_out = torch.empty_like(res)
+
+    def step_unfused(i):
+        step(i)
+        moe.add_rmsnorm(y, mask, res, gam, 1e-6, r_out, n_out)
+
+    def step_fused(i):
+        r = reps[i % len(reps)]
+        moe.layer_add_rmsnorm(md, x, mask, r["router_w"], r["bias"], r["experts"], r["shared"], res, gam, 1e-6,
+                              y, r_out, n_out, rt, ws)
+
+    us_unf = graph_replay_us(torch, step_unfused, len(reps), args.steps, args.warmup, rt_lib, stream)[0]
+    us_fus = graph_replay_us(torch, step_fused, len(reps), args.steps, args.warmup, rt_lib, stream)[0]
+    log(f"[bench] span8 + residual add + RMSNorm: unfused {us_unf:.1f} us, fused {us_fus:.1f} us")
+    result["add_rmsnorm"] = {"workload": "span-8 step followed by the next layer's residual add + RMSNorm "
+                                         "(bf16 residual [8, 6144], gamma [6144], eps 1e-6)",
+                             "unfused_us": round(us_unf, 2), "fused_us": round(us_fus, 2),
+                             "layer_only_us": round(ms_step * 1e3, 2),
+                             "timing": "hipGraph replay, weights rotated as above"}
+
     # ---------------- CPU oracle baseline on the same decode step
     if not args.no_cpu_baseline:
         import oracle

@@ -163,6 +163,31 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
               const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
               moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream);
 
+/* Residual add + RMSNorm, the epilogue that feeds the next layer (mstar PR
+ * #388: the "kernel switches" note fuses each all-reduce with the next add +
+ * RMSNorm; its "Tests" list checks that the fused wiring emits what the
+ * unfused ops do).  Per real row r, over its H columns:
+ *   residual_out = bf16(fl32(residual) + fl32(y))
+ *   out          = bf16(residual_out * (1 / sqrt(mean(residual_out^2) + eps)) * gamma)
+ * with a fixed float32 reduction order, so the same y gives the same bits
+ * from either call below.  Pad rows (row_mask 0): residual_out = out = +0.0,
+ * their y and residual never read.  y, residual, residual_out, out: bf16
+ * [M, H] (device); gamma: bf16 [H]; eps >= 0 (else MOE_EINVAL).
+ * residual_out may be residual itself (in place); no other overlap.
+ * H must be a multiple of 128. */
+int moe_add_rmsnorm(int32_t M, int32_t H, const uint16_t* y, const uint8_t* row_mask, const uint16_t* residual,
+                    const uint16_t* gamma, float eps, uint16_t* residual_out, uint16_t* out, void* stream);
+
+/* moe_layer with the combine running the residual add + RMSNorm above in the
+ * same pass (one launch instead of two, y never re-read).  y (the layer
+ * output, bf16 [M, H]) is also stored unless y is NULL; residual_out and out
+ * as in moe_add_rmsnorm with H = dims->hidden. */
+int moe_layer_add_rmsnorm(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+                          const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared,
+                          const uint16_t* residual, const uint16_t* gamma, float eps, uint16_t* y,
+                          uint16_t* residual_out, uint16_t* out, moe_routing* routing, moe_taps* taps, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* The 1x128 activation quantization step on its own (mstar PR #388,
  * FlashInfer crossover note): rows x cols values (fp32 if is_bf16 == 0, else
  * bf16 bits) -> e4m3 codes [rows, cols] and fp32 scales [rows, cols/128].

@@ -56,7 +56,7 @@ class CTaps(C.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights",
-           "moe_trace_set", "moe_kernel_name", "moe_status_str")
+           "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_trace_set", "moe_kernel_name", "moe_status_str")
 
 _lib = None
 
@@ -78,6 +78,10 @@ def load() -> C.CDLL:
                                 C.POINTER(CTaps), P, C.c_size_t, P]
     lib.moe_layer.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter), C.POINTER(CExperts),
                               C.POINTER(CShared), P, C.POINTER(CRouting), C.POINTER(CTaps), P, C.c_size_t, P]
+    lib.moe_add_rmsnorm.argtypes = [C.c_int32, C.c_int32, P, P, P, P, C.c_float, P, P, P]
+    lib.moe_layer_add_rmsnorm.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter),
+                                          C.POINTER(CExperts), C.POINTER(CShared), P, P, C.c_float, P, P, P,
+                                          C.POINTER(CRouting), C.POINTER(CTaps), P, C.c_size_t, P]
     lib.moe_quant_fp8.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P]
     lib.moe_pack_weights.argtypes = [P, P, C.c_int64, C.c_int32, C.c_int32, P]
     lib.moe_trace_set.argtypes = [P, C.c_int32, P, P]
@@ -86,7 +90,8 @@ def load() -> C.CDLL:
     lib.moe_kernel_name.restype = C.c_char_p
     lib.moe_status_str.argtypes = [C.c_int]
     lib.moe_status_str.restype = C.c_char_p
-    for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights"):
+    for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights", "moe_add_rmsnorm",
+              "moe_layer_add_rmsnorm"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib
@@ -230,6 +235,31 @@ def layer(dims: Dims, x: torch.Tensor, row_mask: Optional[torch.Tensor], router_
     _check(load().moe_layer(C.byref(d), x.shape[0], _ptr(x), _ptr(row_mask), C.byref(r), C.byref(ew),
                             C.byref(sw) if sw is not None else None, _ptr(y), C.byref(rt),
                             C.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream()))
+
+
+def add_rmsnorm(y: torch.Tensor, row_mask: Optional[torch.Tensor], residual: torch.Tensor, gamma: torch.Tensor,
+                eps: float, residual_out: torch.Tensor, out: torch.Tensor) -> None:
+    """moe_add_rmsnorm on bf16 [M, H] tensors (uint16 bits or bfloat16)."""
+    m, h = y.shape
+    _check(load().moe_add_rmsnorm(m, h, _ptr(y), _ptr(row_mask), _ptr(residual), _ptr(gamma), eps,
+                                  _ptr(residual_out), _ptr(out), _stream()))
+
+
+def layer_add_rmsnorm(dims: Dims, x: torch.Tensor, row_mask: Optional[torch.Tensor], router_w: torch.Tensor,
+                      bias: torch.Tensor, experts: Experts, shared: Optional[Shared], residual: torch.Tensor,
+                      gamma: torch.Tensor, eps: float, y: Optional[torch.Tensor], residual_out: torch.Tensor,
+                      out: torch.Tensor, routing: Routing, ws: torch.Tensor, taps: Optional[Taps] = None) -> None:
+    """moe_layer_add_rmsnorm: the layer with the residual add + RMSNorm in its combine."""
+    d = dims.c()
+    r = CRouter(_ptr(router_w), _ptr(bias))
+    ew = experts.c()
+    sw = shared.c() if shared is not None else None
+    rt = routing.c()
+    tp = taps.c() if taps is not None else None
+    _check(load().moe_layer_add_rmsnorm(C.byref(d), x.shape[0], _ptr(x), _ptr(row_mask), C.byref(r), C.byref(ew),
+                                        C.byref(sw) if sw is not None else None, _ptr(residual), _ptr(gamma), eps,
+                                        _ptr(y), _ptr(residual_out), _ptr(out), C.byref(rt),
+                                        C.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream()))
 
 
 def pack_weights(src: torch.Tensor, dst: torch.Tensor, is_bf16: bool) -> None:

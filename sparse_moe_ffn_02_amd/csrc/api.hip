@@ -188,7 +188,7 @@ Tracer g_trace;
 
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
-    "down", "combine", "quant", "select_union", "front", "pack",
+    "down", "combine", "quant", "select_union", "front", "pack", "combine_norm", "add_rmsnorm",
 };
 
 }  // namespace
@@ -277,9 +277,24 @@ int moe_ffn_fp8(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_
   return to_status(launch_ffn(a, s));
 }
 
-int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
-              const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
-              moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Pointers and eps of the residual add + RMSNorm epilogue: MOE_OK or MOE_EINVAL.
+int check_norm(const uint16_t* residual, const uint16_t* gamma, float eps, const uint16_t* residual_out,
+               const uint16_t* out) {
+  if (!ok_ptr(residual, 16) || !ok_ptr(gamma, 16) || !ok_ptr(residual_out, 16) || !ok_ptr(out, 16))
+    return MOE_EINVAL;
+  if (!isfinite(eps) || eps < 0.0f) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// moe_layer, with the combine optionally running the add + RMSNorm epilogue
+// (nm != nullptr; y may then be null).
+int layer_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+               const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
+               const NormArgs* nm, moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_rows(M)) != MOE_OK) return st;
@@ -293,7 +308,8 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
   } else {
     shared = nullptr;
   }
-  if (!ok_ptr(x, 16) || !ok_ptr(y, 16) || !ok_ptr(ws, 16)) return MOE_EINVAL;
+  if (!ok_ptr(x, 16) || !ok_ptr(ws, 16)) return MOE_EINVAL;
+  if (nm ? !ok_opt(y, 16) : !ok_ptr(y, 16)) return MOE_EINVAL;
   if (M == 0) return MOE_OK;
   const Layout L = make_layout(*dims, M);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
@@ -309,7 +325,50 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
     if ((st = to_status(launch_prep(a, s))) != MOE_OK) return st;
     if ((st = to_status(launch_route(ra, s))) != MOE_OK) return st;
   }
-  return to_status(launch_ffn(a, s));
+  return to_status(launch_ffn(a, s, nm));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+              const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
+              moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+  return layer_impl(dims, M, x, row_mask, router, experts, shared, y, nullptr, out, taps, ws, ws_bytes, stream);
+}
+
+int moe_layer_add_rmsnorm(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+                          const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared,
+                          const uint16_t* residual, const uint16_t* gamma, float eps, uint16_t* y,
+                          uint16_t* residual_out, uint16_t* out, moe_routing* routing, moe_taps* taps, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const int st = check_norm(residual, gamma, eps, residual_out, out);
+  if (st != MOE_OK) return st;
+  NormArgs nm;
+  nm.res = residual;
+  nm.gamma = gamma;
+  nm.eps = eps;
+  nm.res_out = residual_out;
+  nm.out = out;
+  return layer_impl(dims, M, x, row_mask, router, experts, shared, y, &nm, routing, taps, ws, ws_bytes, stream);
+}
+
+int moe_add_rmsnorm(int32_t M, int32_t H, const uint16_t* y, const uint8_t* row_mask, const uint16_t* residual,
+                    const uint16_t* gamma, float eps, uint16_t* residual_out, uint16_t* out, void* stream) {
+  if (H <= 0 || H % 128) return MOE_EINVAL;
+  int st = check_rows(M);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(y, 16)) return MOE_EINVAL;
+  if ((st = check_norm(residual, gamma, eps, residual_out, out)) != MOE_OK) return st;
+  if (M == 0) return MOE_OK;
+  NormArgs nm;
+  nm.res = residual;
+  nm.gamma = gamma;
+  nm.eps = eps;
+  nm.res_out = residual_out;
+  nm.out = out;
+  return to_status(launch_add_rmsnorm(y, row_mask, M, H, nm, static_cast<hipStream_t>(stream)));
 }
 
 int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, uint8_t* codes, float* scales,

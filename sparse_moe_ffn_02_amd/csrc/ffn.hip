@@ -268,17 +268,8 @@ __device__ __forceinline__ v4f slot_down(const FfnArgs& a, int s, int n) {
   return d;
 }
 
-__global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int q = a.H / 4;
-  const int r = (int)(idx / q);
-  if (r >= a.M) return;
-  const int n = (int)(idx % q) * 4;
-  uint16_t* yp = a.y + (size_t)r * a.H + n;
-  if (!row_real(a.mask, r)) {
-    *reinterpret_cast<uint2*>(yp) = make_uint2(0u, 0u);
-    return;
-  }
+// The fp32 value of y[r, n .. n + 3] before its bf16 rounding (real row r).
+__device__ __forceinline__ v4f combine_at(const FfnArgs& a, int r, int n, int with_shared) {
   const int slots = a.sched[SCHED_SLOTS];
   v4f sv = {0.f, 0.f, 0.f, 0.f};
   if (with_shared) {
@@ -321,7 +312,131 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
     }
   }
   if (with_shared) acc = add4(acc, sv);
-  store_bf16x4(yp, acc);
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int q = a.H / 4;
+  const int r = (int)(idx / q);
+  if (r >= a.M) return;
+  const int n = (int)(idx % q) * 4;
+  uint16_t* yp = a.y + (size_t)r * a.H + n;
+  if (!row_real(a.mask, r)) {
+    *reinterpret_cast<uint2*>(yp) = make_uint2(0u, 0u);
+    return;
+  }
+  store_bf16x4(yp, combine_at(a, r, n, with_shared));
+}
+
+// ---------------------------------------------------------------- residual add + RMSNorm
+// The epilogue that feeds the next layer (mstar PR #388: each all-reduce
+// fused with the next add + RMSNorm; fused and unfused emit the same bits).
+// One workgroup per row, one procedure whether y comes from memory or from
+// the combine in the same pass:
+//   r_new = bf16(fl32(residual) + fl32(y))                 (y: the bf16 layer output)
+//   ss    = sum of r_new^2: each thread fma-accumulates its 4-column groups
+//           (g = tid, tid + kNormThreads, ...) in order, then an xor
+//           butterfly inside each wave (lane 0's result), then the waves'
+//           sums in ascending wave order
+//   inv   = 1 / sqrt(ss / H + eps)                         (IEEE division and square root)
+//   out   = bf16((r_new * inv) * gamma)
+// Pad rows: r_new = out = +0.0 (and y = +0.0); their inputs are never read.
+constexpr int kNormThreads = 1024;
+constexpr int kNormWaves = kNormThreads / 64;
+
+__device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
+  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+}
+
+__device__ __forceinline__ void unpack_bf16x4(uint2 b, float (&v)[4]) {
+  v[0] = __uint_as_float(b.x << 16);
+  v[1] = __uint_as_float(b.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(b.y << 16);
+  v[3] = __uint_as_float(b.y & 0xFFFF0000u);
+}
+
+// yfn(n) returns the bf16 bits of y[r, n .. n + 3] (as a uint2).
+template <typename YFn>
+__device__ __forceinline__ void add_rmsnorm_row(const NormArgs& nm, int r, int H, YFn yfn) {
+  __shared__ float red[kNormWaves];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const size_t row = (size_t)r * H;
+  float ss = 0.0f;
+  for (int g = tid; g < H / 4; g += kNormThreads) {
+    const int n = 4 * g;
+    float y[4], res[4], s[4];
+    unpack_bf16x4(yfn(n), y);
+    unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.res + row + n), res);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = res[i] + y[i];
+    const uint2 b = pack_bf16x4(s);
+    *reinterpret_cast<uint2*>(nm.res_out + row + n) = b;
+    float f[4];
+    unpack_bf16x4(b, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  ss = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ss)));   // lane 0's order for the whole wave
+  if (lane == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = red[0];
+#pragma unroll
+  for (int w = 1; w < kNormWaves; ++w) tot += red[w];
+  const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(tot, (float)H) + nm.eps));
+  for (int g = tid; g < H / 4; g += kNormThreads) {
+    const int n = 4 * g;
+    float f[4], gm[4], o[4];
+    unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.res_out + row + n), f);   // this thread's own writes
+    unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.gamma + n), gm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (f[i] * inv) * gm[i];
+    *reinterpret_cast<uint2*>(nm.out + row + n) = pack_bf16x4(o);
+  }
+}
+
+__device__ __forceinline__ void zero_row(uint16_t* p, int H) {
+  if (p == nullptr) return;
+  for (int g = threadIdx.x; g < H / 4; g += kNormThreads) *reinterpret_cast<uint2*>(p + 4 * g) = make_uint2(0u, 0u);
+}
+
+// Standalone: y read from memory.
+__global__ __launch_bounds__(kNormThreads) void k_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int H,
+                                                              NormArgs nm) {
+  const int r = blockIdx.x;
+  if (!row_real(mask, r)) {
+    zero_row(nm.res_out + (size_t)r * H, H);
+    zero_row(nm.out + (size_t)r * H, H);
+    return;
+  }
+  add_rmsnorm_row(nm, r, H, [&](int n) { return *reinterpret_cast<const uint2*>(y + (size_t)r * H + n); });
+}
+
+// Fused: y computed by the combine in the same pass (and stored when a.y is set).
+__global__ __launch_bounds__(kNormThreads) void k_combine_norm(FfnArgs a, NormArgs nm, int with_shared) {
+  const int r = blockIdx.x;
+  if (!row_real(a.mask, r)) {
+    zero_row(a.y ? a.y + (size_t)r * a.H : nullptr, a.H);
+    zero_row(nm.res_out + (size_t)r * a.H, a.H);
+    zero_row(nm.out + (size_t)r * a.H, a.H);
+    return;
+  }
+  add_rmsnorm_row(nm, r, a.H, [&](int n) {
+    const v4f acc = combine_at(a, r, n, with_shared);
+    const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+    const uint2 b = pack_bf16x4(v);
+    if (a.y) *reinterpret_cast<uint2*>(a.y + (size_t)r * a.H + n) = b;
+    return b;
+  });
+}
+
+hipError_t launch_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int M, int H, const NormArgs& nm,
+                              hipStream_t s) {
+  MOE_LAUNCH(KID_ADD_NORM, k_add_rmsnorm, dim3((unsigned)M), dim3(kNormThreads), 0, s, y, mask, H, nm);
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- weight packing
@@ -381,7 +496,7 @@ hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8
 
 bool use_split(int M, int H) { return M <= kSmallRows && H > 0; }
 
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, const NormArgs* nm) {
   const int with_shared = a.Is > 0 ? 1 : 0;
   const long max_union = std::min<long>(a.E, (long)a.M * a.K);
   if (a.split) {
@@ -403,6 +518,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     const long mtiles_max = ((long)a.M * a.K + kMTile - 1) / kMTile + max_union;
     const hipError_t e = launch_tiled(a, mtiles_max, s);
     if (e != hipSuccess) return e;
+  }
+  if (nm != nullptr) {
+    MOE_LAUNCH(KID_COMBINE_NORM, k_combine_norm, dim3((unsigned)a.M), dim3(kNormThreads), 0, s, a, *nm, with_shared);
+    return hipSuccess;
   }
   const long threads = (long)a.M * (a.H / 4);
   MOE_LAUNCH(KID_COMBINE, k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, with_shared);

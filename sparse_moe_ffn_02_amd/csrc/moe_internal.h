@@ -79,10 +79,20 @@ struct FfnArgs {
   uint16_t* y;             // bf16 [M, H]
 };
 
+// Residual add + RMSNorm epilogue (bf16 [M, H] rows; gamma bf16 [H]).
+struct NormArgs {
+  const uint16_t* res;     // residual in
+  const uint16_t* gamma;
+  float eps;
+  uint16_t* res_out;       // r_new (may equal res)
+  uint16_t* out;           // normalized rows
+};
+
 // Kernel ids reported by the timing hook (moe_trace_set).
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
-  KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COUNT
+  KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COMBINE_NORM, KID_ADD_NORM,
+  KID_COUNT
 };
 
 void trace_before(hipStream_t s);
@@ -104,7 +114,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s);
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prep(const FfnArgs& a, hipStream_t s);   // quantize x
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// nm != nullptr: the combine also runs the residual add + RMSNorm epilogue
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, const NormArgs* nm = nullptr);
+hipError_t launch_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int M, int H, const NormArgs& nm,
+                              hipStream_t s);
 // steps that do not take the split path: tiled gate/up (+ SiLU, requant) and down
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s);
 bool use_split(int M, int H);   // M <= kSmallRows

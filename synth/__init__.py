@@ -17,7 +17,10 @@ table note, MoE-Infinity PR #140 fp8 store commits).  Distributions:
   with one fp32 scale per 128x128 block: s = amax/448 (fp32), codes are
   torch's float8_e4m3fn cast of w/s (a library conversion; weight preparation
   happens offline, outside the layer);
-* shared expert ~N(0, 0.02) -> bf16.
+* shared expert ~N(0, 0.02) -> bf16;
+* for the residual add + RMSNorm epilogue: residual stream ~N(0, 4) -> bf16
+  [M, H] (larger than a layer output, as a residual stream is) and the norm
+  weight gamma ~N(1, 0.1) -> bf16 [H].
 
 Every tensor draws from its own PCG64 stream,
 SeedSequence(entropy=seed, spawn_key=(layer, tensor_id, expert)), so experts
@@ -34,7 +37,7 @@ import numpy as np
 import torch
 
 # tensor ids in the spawn key
-T_X, T_WR, T_BIAS, T_WG, T_WU, T_WD, T_SG, T_SU, T_SD, T_PERT, T_ZIPF = range(11)
+T_X, T_WR, T_BIAS, T_WG, T_WU, T_WD, T_SG, T_SU, T_SD, T_PERT, T_ZIPF, T_RES, T_GAMMA = range(13)
 
 BLOCK = 128
 
@@ -253,3 +256,13 @@ def make_layer(cfg: Config, layer: int = 0, threads: Optional[int] = None) -> La
 
 def with_rows(cfg: Config, rows: int) -> Config:
     return replace(cfg, rows=rows)
+
+
+def norm_inputs(cfg: Config, layer: int = 0, rows: Optional[int] = None) -> tuple:
+    """(residual bf16 bits [rows, H], gamma bf16 bits [H]) for the residual
+    add + RMSNorm epilogue; rows defaults to the config's row count."""
+    m = cfg.rows if rows is None else rows
+    h = cfg.dims.hidden
+    res = _rng(cfg.seed, layer, T_RES).standard_normal((m, h), dtype=np.float32) * np.float32(2.0)
+    gamma = np.float32(1.0) + np.float32(0.1) * _rng(cfg.seed, layer, T_GAMMA).standard_normal(h, dtype=np.float32)
+    return to_bf16_bits(res), to_bf16_bits(gamma)

@@ -209,3 +209,41 @@ def test_binding_raises_on_error(lib):
         moe.quant_fp8(torch.zeros((4, 100), dtype=torch.float32), torch.zeros((4, 100), dtype=torch.uint8),
                       torch.zeros((4, 1), dtype=torch.float32))
     assert ei.value.status == L.MOE_EINVAL
+
+
+def _norm(lib, m=8, h=512, y=FAKE, res=FAKE, gamma=FAKE, eps=1e-6, res_out=FAKE, out=FAKE):
+    return lib.moe_add_rmsnorm(m, h, y, None, res, gamma, eps, res_out, out, None)
+
+
+def _layer_norm(lib, d, m, y=FAKE, res=FAKE, gamma=FAKE, eps=1e-6, res_out=FAKE, out=FAKE, ws_bytes=1 << 40):
+    return lib.moe_layer_add_rmsnorm(C.byref(d), m, FAKE, None, C.byref(L.CRouter(FAKE, FAKE)), C.byref(_experts()),
+                                     C.byref(L.CShared(FAKE, FAKE, FAKE)), res, gamma, eps, y, res_out, out, C.byref(_routing()), None,
+                                     FAKE, ws_bytes, None)
+
+
+def test_add_rmsnorm_rejects(lib):
+    assert _norm(lib, m=0) == L.MOE_OK                       # nothing to do, nothing launched
+    assert _norm(lib, m=-1) == L.MOE_EINVAL
+    assert _norm(lib, m=L.MAX_ROWS + 1) == L.MOE_EUNSUPPORTED
+    assert _norm(lib, h=0) == L.MOE_EINVAL
+    assert _norm(lib, h=520) == L.MOE_EINVAL                 # not a multiple of 128
+    assert _norm(lib, y=None) == L.MOE_EINVAL
+    assert _norm(lib, res=None) == L.MOE_EINVAL
+    assert _norm(lib, gamma=FAKE + 2) == L.MOE_EINVAL        # misaligned
+    assert _norm(lib, res_out=None) == L.MOE_EINVAL
+    assert _norm(lib, out=None) == L.MOE_EINVAL
+    assert _norm(lib, eps=-1.0) == L.MOE_EINVAL
+    assert _norm(lib, eps=float("nan")) == L.MOE_EINVAL
+
+
+def test_layer_add_rmsnorm_rejects(lib):
+    d = _dims()
+    assert _layer_norm(lib, d, 0, ws_bytes=0) == L.MOE_OK
+    assert _layer_norm(lib, d, 0, y=None, ws_bytes=0) == L.MOE_OK      # y is optional here
+    assert _layer_norm(lib, d, 8, y=FAKE + 2) == L.MOE_EINVAL
+    assert _layer_norm(lib, d, 8, res=None) == L.MOE_EINVAL
+    assert _layer_norm(lib, d, 8, out=None) == L.MOE_EINVAL
+    assert _layer_norm(lib, d, 8, eps=float("inf")) == L.MOE_EINVAL
+    assert _layer_norm(lib, d, 8, ws_bytes=16) == L.MOE_EWORKSPACE
+    assert _layer_norm(lib, _dims(hidden=6000), 8) == L.MOE_EINVAL
+    assert _layer_norm(lib, _dims(top_k=17), 8) == L.MOE_EUNSUPPORTED

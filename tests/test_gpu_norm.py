@@ -1,0 +1,127 @@
+"""GPU parity of the residual add + RMSNorm epilogue (moe_add_rmsnorm and the
+fused moe_layer_add_rmsnorm) against the CPU oracle, and fused against
+unfused, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_02_amd as moe
+import synth
+from gpu_util import DEV, GpuLayer, np16, say, t8, t16
+from test_gpu_full import glm_layer
+
+pytestmark = pytest.mark.gpu
+
+OUT_REL = 2.0 ** -8      # bf16 rounding (2^-9) + float32 sum of squares over H (< 2^-12 at H = 6144)
+NAN16 = 0x7FC0
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load()
+
+
+def _check_against_oracle(y_bits, r_bits, g_bits, eps, mask, r_new, out):
+    want_r, ref = oracle.add_rmsnorm(y_bits, r_bits, g_bits, eps, mask)
+    assert np.array_equal(r_new, want_r), f"{int((r_new != want_r).sum())} residual values differ"
+    real = mask.astype(bool)
+    got = oracle.decode_bf16(out).astype(np.float64)
+    err = np.abs(got[real] - ref[real])
+    assert np.all(err <= OUT_REL * np.abs(ref[real]) + 1e-30), f"worst rel {np.max(err / np.abs(ref[real])):.3e}"
+    assert not out[~real].any() and not r_new[~real].any(), "pad rows must be +0.0"
+    diff = int((out[real] != oracle.encode_bf16(ref[real])).sum())
+    say(f"add+rmsnorm: {diff} of {out[real].size} outputs one bf16 step from the rounded reference")
+
+
+def _run_norm(y_bits, mask, r_bits, g_bits, eps, in_place=False):
+    m, h = y_bits.shape
+    y, res, gam = t16(y_bits), t16(r_bits), t16(g_bits)
+    res_out = res if in_place else torch.full((m, h), -1, dtype=torch.int16, device=DEV)
+    out = torch.full((m, h), -1, dtype=torch.int16, device=DEV)
+    moe.add_rmsnorm(y, t8(mask), res, gam, eps, res_out, out)
+    torch.cuda.synchronize()
+    return np16(res_out), np16(out)
+
+
+@pytest.mark.parametrize("name,m,pads", [("tiny", 1, ()), ("odd", 8, (2, 5)), ("span8", 37, (0, 36))])
+@pytest.mark.parametrize("eps", [1e-6, 1e-2])
+def test_add_rmsnorm_unit(name, m, pads, eps):
+    _need_gpu()
+    cfg = synth.CONFIGS[name]
+    rng = np.random.default_rng(m)
+    y = synth.to_bf16_bits(rng.standard_normal((m, cfg.dims.hidden)).astype(np.float32))
+    r, g = synth.norm_inputs(cfg, rows=m)
+    mask = np.ones(m, np.uint8)
+    for p in pads:
+        mask[p] = 0
+        y[p] = NAN16                      # pad inputs are never read
+        r[p] = NAN16
+    say(f"add+rmsnorm unit: H={cfg.dims.hidden} M={m} pads={pads} eps={eps}")
+    r_new, out = _run_norm(y, mask, r, g, eps)
+    _check_against_oracle(y, r, g, eps, mask, r_new, out)
+    r_new2, out2 = _run_norm(y, mask, r, g, eps, in_place=True)
+    assert np.array_equal(r_new2, r_new) and np.array_equal(out2, out), "in-place call differs"
+
+
+def _layer_both(gl, x_bits, mask, r_bits, g_bits, eps):
+    """(moe_layer + moe_add_rmsnorm, moe_layer_add_rmsnorm with y, the same with y = NULL)."""
+    m, d = x_bits.shape[0], gl.dims
+    x, mk, res, gam = t16(x_bits), t8(mask), t16(r_bits), t16(g_bits)
+    ws = moe.workspace(d, m)
+    outs = []
+    for mode in ("unfused", "fused", "fused_noy"):
+        y = torch.full((m, d.hidden), -1, dtype=torch.int16, device=DEV)
+        r_out = torch.full((m, d.hidden), -1, dtype=torch.int16, device=DEV)
+        o = torch.full((m, d.hidden), -1, dtype=torch.int16, device=DEV)
+        rt = moe.Routing.empty(d, m)
+        if mode == "unfused":
+            moe.layer(d, x, mk, gl.router_w, gl.bias, gl.experts, gl.shared, y, rt, ws)
+            moe.add_rmsnorm(y, mk, res, gam, eps, r_out, o)
+        else:
+            moe.layer_add_rmsnorm(d, x, mk, gl.router_w, gl.bias, gl.experts, gl.shared, res, gam, eps,
+                                  y if mode == "fused" else None, r_out, o, rt, ws)
+        torch.cuda.synchronize()
+        outs.append((np16(y), np16(r_out), np16(o)))
+    return outs
+
+
+def _fused_case(gl, cfg, x, mask, eps=1e-6):
+    r, g = synth.norm_inputs(cfg, rows=x.shape[0])
+    for p in np.nonzero(mask == 0)[0]:
+        r[p] = NAN16
+    (y, r1, o1), (y2, r2, o2), (_, r3, o3) = _layer_both(gl, x, mask, r, g, eps)
+    assert np.array_equal(y2, y), "fused y differs from moe_layer's"
+    assert np.array_equal(r2, r1) and np.array_equal(o2, o1), "fused epilogue differs from the unfused call"
+    assert np.array_equal(r3, r1) and np.array_equal(o3, o1), "fused epilogue without y differs"
+    _check_against_oracle(y, r, g, eps, mask, r1, o1)
+
+
+def test_fused_tiny():
+    _need_gpu()
+    cfg = synth.CONFIGS["tiny"]
+    gl = GpuLayer(synth.make_layer(cfg, threads=4))
+    x, mask = synth.activations(cfg)
+    mask = mask.copy()
+    mask[6] = 0
+    x = x.copy()
+    x[6] = NAN16
+    say("fused add+rmsnorm: tiny layer, 8 rows, one pad")
+    _fused_case(gl, cfg, x, mask)
+
+
+@pytest.mark.parametrize("rows", [8, 40])
+def test_fused_glm(rows):
+    """8 rows take the split small-step kernels, 40 rows the tiled ones."""
+    cfg, gl = glm_layer("span8")
+    base, _ = synth.activations(cfg)
+    rng = np.random.default_rng(rows)
+    x = np.concatenate([base, synth.to_bf16_bits(rng.standard_normal((rows - 8, cfg.dims.hidden)).astype(np.float32))]
+                       ) if rows > 8 else base
+    mask = np.ones(rows, np.uint8)
+    mask[3] = 0
+    x = x.copy()
+    x[3] = NAN16
+    say(f"fused add+rmsnorm: GLM layer, {rows} rows")
+    _fused_case(gl, cfg, x, mask)
