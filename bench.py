@@ -358,6 +358,43 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
         "expert_rows_mean": round(float(np.mean([l.mean() for l in loads])), 1),
     }
     log(f"[bench] prefill4096 x{n_layers} layers: {ms_p:.2f} ms/step, {out['tflops_total']} TFLOPS")
+
+    # layer 0 followed by the next layer's residual add + RMSNorm, unfused and fused
+    res_np, gam_np = synth.norm_inputs(pcfg, rows=Mp)
+    res = torch.from_numpy(res_np.view(np.int16)).cuda()
+    gam = torch.from_numpy(gam_np.view(np.int16)).cuda()
+    r_out = torch.empty_like(res)
+    n_out = torch.empty_like(res)
+    L0 = layers[0]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+        for _ in range(args.prefill_steps):
+            fn()
+        rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+        torch.cuda.synchronize()
+        return ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.prefill_steps
+
+    def unfused():
+        moe.layer(md, xs[0], None, L0["router_w"], L0["bias"], L0["experts"], L0["shared"], yp, rts[0], wsp)
+        moe.add_rmsnorm(yp, None, res, gam, 1e-6, r_out, n_out)
+
+    def fused():
+        moe.layer_add_rmsnorm(md, xs[0], None, L0["router_w"], L0["bias"], L0["experts"], L0["shared"], res, gam,
+                              1e-6, yp, r_out, n_out, rts[0], wsp)
+    # alternate the two so that clock drift does not favour either; medians of 3
+    t_unf, t_fus = [], []
+    for _ in range(3):
+        t_unf.append(timed(unfused))
+        t_fus.append(timed(fused))
+    ms_unf, ms_fus = float(np.median(t_unf)), float(np.median(t_fus))
+    out["add_rmsnorm"] = {"unfused_ms": round(ms_unf, 4), "fused_ms": round(ms_fus, 4),
+                          "timing": "median of 3 alternating runs of --prefill-steps calls each",
+                          "workload": "layer 0 of the chunk followed by the residual add + RMSNorm "
+                                      "(bf16 residual [4096, 6144], gamma [6144], eps 1e-6)"}
+    log(f"[bench] prefill layer + add/RMSNorm: unfused {ms_unf:.3f} ms, fused {ms_fus:.3f} ms")
     return out
 
 
