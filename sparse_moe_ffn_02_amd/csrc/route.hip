@@ -17,6 +17,12 @@
 namespace moe {
 
 // ---------------------------------------------------------------- logits
+// bf16 element t (0..7) of 8 packed in a uint4
+__device__ __forceinline__ uint16_t u16_of(const uint4& v, int t) {
+  const uint32_t w = t < 2 ? v.x : t < 4 ? v.y : t < 6 ? v.z : v.w;
+  return (uint16_t)(w >> ((t & 1) * 16));
+}
+
 // Every logit l[r, e] is computed by one fixed procedure, whatever row tile
 // or expert group it falls in: lane j of a wave accumulates (float64 FMA, in
 // ascending order) the products for h = 512 i + 8 j + t (i ascending, then
@@ -49,27 +55,26 @@ __global__ __launch_bounds__(256) void k_router_logits(RouteArgs a) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) xrow[r] = a.x + (size_t)(rv[r] ? r0 + r : r0) * a.H;
   for (int h0 = lane * 8; h0 < a.H; h0 += 512) {
-    // the chunk's weights, converted once for all 8 rows
-    double wd[EPW][8];
+    uint4 wv[EPW], xv[8];
 #pragma unroll
-    for (int e = 0; e < EPW; ++e) {
-      const uint4 wv = (e0 + e < a.E) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)(e0 + e) * a.H + h0)
-                                      : make_uint4(0, 0, 0, 0);
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) wd[e][t] = (double)bf16_to_f32((uint16_t)(ww[t >> 1] >> ((t & 1) * 16)));
-    }
-    uint4 xv[8];
+    for (int e = 0; e < EPW; ++e)
+      wv[e] = (e0 + e < a.E) ? *reinterpret_cast<const uint4*>(a.wr + (size_t)(e0 + e) * a.H + h0)
+                             : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) xv[r] = *reinterpret_cast<const uint4*>(xrow[r] + h0);
+    // element t of the chunk: each weight converted once for the 8 rows, each
+    // x value once for the EPW experts; every accumulator still takes its
+    // products in ascending t
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t xw[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
+    for (int t = 0; t < 8; ++t) {
+      double wd[EPW];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const double xd = (double)bf16_to_f32((uint16_t)(xw[t >> 1] >> ((t & 1) * 16)));
+      for (int e = 0; e < EPW; ++e) wd[e] = (double)bf16_to_f32(u16_of(wv[e], t));
 #pragma unroll
-        for (int e = 0; e < EPW; ++e) acc[r][e] = __builtin_fma(xd, wd[e][t], acc[r][e]);
+      for (int r = 0; r < 8; ++r) {
+        const double xd = (double)bf16_to_f32(u16_of(xv[r], t));
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) acc[r][e] = __builtin_fma(xd, wd[e], acc[r][e]);
       }
     }
   }
@@ -552,7 +557,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   }
   {
     const long groups8 = ((a.M + 7) / 8 + 7) / 8 * 8;     // row groups, padded to a multiple of 8
-    MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<4>, dim3((unsigned)(groups8 * ((a.E + 15) / 16))), blk, 0, s, a);
+    constexpr int kEpw = 8;                                 // experts per wave (32 per workgroup)
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<kEpw>, dim3((unsigned)(groups8 * ((a.E + 4 * kEpw - 1) / (4 * kEpw)))),
+               blk, 0, s, a);
   }
   MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union_count, dim3(kUChunks), dim3(kMaxExperts), 0, s, a);
