@@ -36,18 +36,33 @@ template <>
 __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
 // rows [0, R) of a [R, C] matrix; rows with mask 0 are skipped (never read).
+// One wave per (row, group of kQGroup 128-column blocks): the group's loads
+// are issued together, then each block is quantized as on its own.
+constexpr int kQGroup = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant_rows(const T* in, const uint8_t* mask, int R, int C, uint8_t* codes,
                                                     float* scales) {
   const int lane = threadIdx.x & 63;
   const int nb = C / kBlk;
+  const int ng = (nb + kQGroup - 1) / kQGroup;
   const long item = (long)blockIdx.x * 4 + wave_id();
-  const int r = (int)(item / nb);
-  const int b = (int)(item % nb);
+  const int r = (int)(item / ng);
+  const int b0 = (int)(item % ng) * kQGroup;
   if (r >= R || !row_real(mask, r)) return;
-  const T* p = in + (size_t)r * C + b * kBlk + 2 * lane;
-  quant_pair(load_as_f32<T>(p), load_as_f32<T>(p + 1), codes + (size_t)r * C + b * kBlk, scales + (size_t)r * nb + b,
-             lane);
+  const T* p = in + (size_t)r * C + 2 * lane;
+  float v[kQGroup][2];
+#pragma unroll
+  for (int i = 0; i < kQGroup; ++i) {
+    const int b = min(b0 + i, nb - 1);          // past the row's end: reload its last block, not stored
+    v[i][0] = load_as_f32<T>(p + b * kBlk);
+    v[i][1] = load_as_f32<T>(p + b * kBlk + 1);
+  }
+#pragma unroll
+  for (int i = 0; i < kQGroup; ++i) {
+    const int b = b0 + i;
+    if (b < nb) quant_pair(v[i][0], v[i][1], codes + (size_t)r * C + b * kBlk, scales + (size_t)r * nb + b, lane);
+  }
 }
 
 // ---------------------------------------------------------------- plan
@@ -474,7 +489,7 @@ hipError_t launch_plan(const FfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_prep(const FfnArgs& a, hipStream_t s) {
-  const long waves = (long)a.M * (a.H / kBlk);
+  const long waves = (long)a.M * ((a.H / kBlk + kQGroup - 1) / kQGroup);
   MOE_LAUNCH(KID_QUANT_X, k_quant_rows<uint16_t>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a.x, a.mask,
              a.M, a.H, a.xq, a.xs);
   return hipSuccess;
@@ -482,7 +497,7 @@ hipError_t launch_prep(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s) {
-  const long waves = (long)R * (C / kBlk);
+  const long waves = (long)R * ((C / kBlk + kQGroup - 1) / kQGroup);
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (is_bf16) {
     MOE_LAUNCH(KID_QUANT, k_quant_rows<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in, nullptr, R, C, codes,

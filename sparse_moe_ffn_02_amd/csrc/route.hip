@@ -278,6 +278,11 @@ __global__ __launch_bounds__(kMaxExperts) void k_union_scan(RouteArgs a) {
   }
 }
 
+// Rows are taken 8 at a time: their expert bitmasks are loaded together, so
+// a chunk costs one memory round trip per 8 rows instead of one per row.
+constexpr int kScatterRows = 8;
+constexpr int kMaskWords = kMaxExperts / 32;
+
 __global__ __launch_bounds__(kMaxExperts) void k_union_scatter(RouteArgs a) {
   const int c = blockIdx.x, e = threadIdx.x;
   if (e >= a.E) return;
@@ -287,15 +292,33 @@ __global__ __launch_bounds__(kMaxExperts) void k_union_scatter(RouteArgs a) {
   const int wi = e >> 5;
   const uint32_t bit = 1u << (e & 31);
   int slot = a.ucount[(size_t)c * a.E + e];
-  for (int r = r0; r < r1; ++r) {
-    const uint32_t* rb = a.rowbits + (size_t)r * nwords;
-    const uint32_t word = rb[wi];
-    if (!(word & bit)) continue;
-    int j = __popc(word & (bit - 1u));
-    for (int w2 = 0; w2 < wi; ++w2) j += __popc(rb[w2]);
-    a.rows[slot] = r;
-    a.slot_of[(size_t)r * a.K + j] = slot;
-    ++slot;
+  for (int rb0 = r0; rb0 < r1; rb0 += kScatterRows) {
+    uint32_t m[kScatterRows][kMaskWords];
+#pragma unroll
+    for (int i = 0; i < kScatterRows; ++i) {
+      const uint32_t* rb = a.rowbits + (size_t)min(rb0 + i, r1 - 1) * nwords;   // rows past r1: a valid row, unused
+#pragma unroll
+      for (int w2 = 0; w2 < kMaskWords; ++w2) m[i][w2] = rb[min(w2, nwords - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < kScatterRows; ++i) {
+      const int r = rb0 + i;
+      if (r >= r1) break;
+      // the row's word holding e, and the count of the row's experts in lower words
+      uint32_t word = 0;
+      int below = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kMaskWords; ++w2) {
+        const uint32_t mw = w2 < nwords ? m[i][w2] : 0u;
+        if (w2 < wi) below += __popc(mw);
+        word = w2 == wi ? mw : word;
+      }
+      if (!(word & bit)) continue;
+      const int j = below + __popc(word & (bit - 1u));
+      a.rows[slot] = r;
+      a.slot_of[(size_t)r * a.K + j] = slot;
+      ++slot;
+    }
   }
 }
 
