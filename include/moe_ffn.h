@@ -179,9 +179,11 @@ int moe_add_rmsnorm(int32_t M, int32_t H, const uint16_t* y, const uint8_t* row_
                     const uint16_t* gamma, float eps, uint16_t* residual_out, uint16_t* out, void* stream);
 
 /* moe_layer with the combine running the residual add + RMSNorm above in the
- * same pass (one launch instead of two, y never re-read).  y (the layer
- * output, bf16 [M, H]) is also stored unless y is NULL; residual_out and out
- * as in moe_add_rmsnorm with H = dims->hidden. */
+ * same pass (one launch instead of two, y never re-read), except for steps of
+ * at most 16 rows, where the element-wise combine and the row epilogue run
+ * as two launches (more workgroups; the same bits).  y (the layer output,
+ * bf16 [M, H]) is also stored unless y is NULL; residual_out and out as in
+ * moe_add_rmsnorm with H = dims->hidden. */
 int moe_layer_add_rmsnorm(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
                           const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared,
                           const uint16_t* residual, const uint16_t* gamma, float eps, uint16_t* y,

@@ -347,17 +347,17 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a, int with_shared) {
 // ---------------------------------------------------------------- residual add + RMSNorm
 // The epilogue that feeds the next layer (mstar PR #388: each all-reduce
 // fused with the next add + RMSNorm; fused and unfused emit the same bits).
-// One workgroup per row, one procedure whether y comes from memory or from
-// the combine in the same pass:
+// One workgroup of norm_threads(H) threads per row, one procedure whether y
+// comes from memory or from the combine in the same pass:
 //   r_new = bf16(fl32(residual) + fl32(y))                 (y: the bf16 layer output)
 //   ss    = sum of r_new^2: each thread fma-accumulates its 4-column groups
-//           (g = tid, tid + kNormThreads, ...) in order, then an xor
+//           (g = tid, tid + norm_threads(H), ...) in order, then an xor
 //           butterfly inside each wave (lane 0's result), then the waves'
 //           sums in ascending wave order
 //   inv   = 1 / sqrt(ss / H + eps)                         (IEEE division and square root)
 //   out   = bf16((r_new * inv) * gamma)
 // Pad rows: r_new = out = +0.0 (and y = +0.0); their inputs are never read.
-constexpr int kNormThreads = 1024;
+constexpr int kNormThreads = 1024;                 // most threads per row workgroup
 constexpr int kNormWaves = kNormThreads / 64;
 
 __device__ __forceinline__ uint2 pack_bf16x4(const float (&v)[4]) {
@@ -372,26 +372,71 @@ __device__ __forceinline__ void unpack_bf16x4(uint2 b, float (&v)[4]) {
   v[3] = __uint_as_float(b.y & 0xFFFF0000u);
 }
 
-// yfn(n) returns the bf16 bits of y[r, n .. n + 3] (as a uint2).
+// yfn(n) returns the bf16 bits of y[r, n .. n + 3] (as a uint2).  Rows of up
+// to kNormRegGroups * kNormThreads 4-column groups keep r_new in registers
+// and take all their y values before the first store (so the loads of a
+// thread's groups overlap); longer rows stream group by group and re-read
+// their own r_new.  Both give the same bits.
+constexpr int kNormRegGroups = 2;
+
+// Threads of the row workgroup for rows of H columns: enough for
+// kNormRegGroups 4-column groups each (whole waves), at most kNormThreads, so
+// every thread of a row of up to 8192 columns takes the same number of
+// groups.  A function of H alone: both kernels reduce in the same order.
+__host__ __device__ __forceinline__ int norm_threads(int H) {
+  const int ng = H / 4;
+  const int t = ((ng + kNormRegGroups - 1) / kNormRegGroups + 63) / 64 * 64;
+  return t < 64 ? 64 : (t > kNormThreads ? kNormThreads : t);
+}
+
+__device__ __forceinline__ void add_group(const NormArgs& nm, size_t row, int n, uint2 yb, uint2& b, float& ss) {
+  float y[4], res[4], s[4], f[4];
+  unpack_bf16x4(yb, y);
+  unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.res + row + n), res);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = res[i] + y[i];
+  b = pack_bf16x4(s);
+  *reinterpret_cast<uint2*>(nm.res_out + row + n) = b;
+  unpack_bf16x4(b, f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
+}
+
+__device__ __forceinline__ void norm_group(const NormArgs& nm, size_t row, int n, uint2 b, float inv) {
+  float f[4], gm[4], o[4];
+  unpack_bf16x4(b, f);
+  unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.gamma + n), gm);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (f[i] * inv) * gm[i];
+  *reinterpret_cast<uint2*>(nm.out + row + n) = pack_bf16x4(o);
+}
+
 template <typename YFn>
 __device__ __forceinline__ void add_rmsnorm_row(const NormArgs& nm, int r, int H, YFn yfn) {
   __shared__ float red[kNormWaves];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, nt = blockDim.x;   // nt = norm_threads(H)
   const size_t row = (size_t)r * H;
+  const int ng = H / 4;
+  const bool in_regs = ng <= kNormRegGroups * nt;
   float ss = 0.0f;
-  for (int g = tid; g < H / 4; g += kNormThreads) {
-    const int n = 4 * g;
-    float y[4], res[4], s[4];
-    unpack_bf16x4(yfn(n), y);
-    unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.res + row + n), res);
+  uint2 keep[kNormRegGroups];
+  if (in_regs) {
+    uint2 yb[kNormRegGroups];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = res[i] + y[i];
-    const uint2 b = pack_bf16x4(s);
-    *reinterpret_cast<uint2*>(nm.res_out + row + n) = b;
-    float f[4];
-    unpack_bf16x4(b, f);
+    for (int k = 0; k < kNormRegGroups; ++k) {
+      const int g = tid + k * nt;
+      yb[k] = g < ng ? yfn(4 * g) : make_uint2(0u, 0u);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
+    for (int k = 0; k < kNormRegGroups; ++k) {
+      const int g = tid + k * nt;
+      if (g < ng) add_group(nm, row, 4 * g, yb[k], keep[k], ss);
+    }
+  } else {
+    for (int g = tid; g < ng; g += nt) {
+      uint2 b;
+      add_group(nm, row, 4 * g, yfn(4 * g), b, ss);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
@@ -399,23 +444,23 @@ __device__ __forceinline__ void add_rmsnorm_row(const NormArgs& nm, int r, int H
   if (lane == 0) red[tid >> 6] = ss;
   __syncthreads();
   float tot = red[0];
-#pragma unroll
-  for (int w = 1; w < kNormWaves; ++w) tot += red[w];
+  for (int w = 1; w < nt / 64; ++w) tot += red[w];
   const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(tot, (float)H) + nm.eps));
-  for (int g = tid; g < H / 4; g += kNormThreads) {
-    const int n = 4 * g;
-    float f[4], gm[4], o[4];
-    unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.res_out + row + n), f);   // this thread's own writes
-    unpack_bf16x4(*reinterpret_cast<const uint2*>(nm.gamma + n), gm);
+  if (in_regs) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (f[i] * inv) * gm[i];
-    *reinterpret_cast<uint2*>(nm.out + row + n) = pack_bf16x4(o);
+    for (int k = 0; k < kNormRegGroups; ++k) {
+      const int g = tid + k * nt;
+      if (g < ng) norm_group(nm, row, 4 * g, keep[k], inv);
+    }
+  } else {
+    for (int g = tid; g < ng; g += nt)
+      norm_group(nm, row, 4 * g, *reinterpret_cast<const uint2*>(nm.res_out + row + 4 * g), inv);   // own writes
   }
 }
 
 __device__ __forceinline__ void zero_row(uint16_t* p, int H) {
   if (p == nullptr) return;
-  for (int g = threadIdx.x; g < H / 4; g += kNormThreads) *reinterpret_cast<uint2*>(p + 4 * g) = make_uint2(0u, 0u);
+  for (int g = threadIdx.x; g < H / 4; g += blockDim.x) *reinterpret_cast<uint2*>(p + 4 * g) = make_uint2(0u, 0u);
 }
 
 // Standalone: y read from memory.
@@ -450,7 +495,7 @@ __global__ __launch_bounds__(kNormThreads) void k_combine_norm(FfnArgs a, NormAr
 
 hipError_t launch_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int M, int H, const NormArgs& nm,
                               hipStream_t s) {
-  MOE_LAUNCH(KID_ADD_NORM, k_add_rmsnorm, dim3((unsigned)M), dim3(kNormThreads), 0, s, y, mask, H, nm);
+  MOE_LAUNCH(KID_ADD_NORM, k_add_rmsnorm, dim3((unsigned)M), dim3(norm_threads(H)), 0, s, y, mask, H, nm);
   return hipSuccess;
 }
 
@@ -534,8 +579,21 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, const NormArgs* nm) {
     const hipError_t e = launch_tiled(a, mtiles_max, s);
     if (e != hipSuccess) return e;
   }
+  if (nm != nullptr && a.split) {
+    // Few rows: one row workgroup per row would run the combine on a handful
+    // of CUs, so the element-wise combine runs first and the row epilogue
+    // after it (the same bits as the single pass).  Without a caller y the
+    // combine writes into S, which small steps leave unused (they keep the
+    // shared expert's down partials apart).
+    FfnArgs b = a;
+    if (b.y == nullptr) b.y = reinterpret_cast<uint16_t*>(a.S);
+    const long threads = (long)a.M * (a.H / 4);
+    MOE_LAUNCH(KID_COMBINE, k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, b, with_shared);
+    return launch_add_rmsnorm(b.y, a.mask, a.M, a.H, *nm, s);
+  }
   if (nm != nullptr) {
-    MOE_LAUNCH(KID_COMBINE_NORM, k_combine_norm, dim3((unsigned)a.M), dim3(kNormThreads), 0, s, a, *nm, with_shared);
+    MOE_LAUNCH(KID_COMBINE_NORM, k_combine_norm, dim3((unsigned)a.M), dim3(norm_threads(a.H)), 0, s, a, *nm,
+               with_shared);
     return hipSuccess;
   }
   const long threads = (long)a.M * (a.H / 4);

@@ -1,6 +1,8 @@
 """GPU parity of the residual add + RMSNorm epilogue (moe_add_rmsnorm and the
 fused moe_layer_add_rmsnorm) against the CPU oracle, and fused against
 unfused, through the C ABI."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -45,11 +47,16 @@ def _run_norm(y_bits, mask, r_bits, g_bits, eps, in_place=False):
     return np16(res_out), np16(out)
 
 
-@pytest.mark.parametrize("name,m,pads", [("tiny", 1, ()), ("odd", 8, (2, 5)), ("span8", 37, (0, 36))])
+@pytest.mark.parametrize("name,hidden,m,pads", [("tiny", None, 1, ()), ("odd", None, 8, (2, 5)),
+                                               ("span8", None, 37, (0, 36)),
+                                               # rows longer than the register-resident form (H > 8192)
+                                               ("span8", 8320, 5, (1,))])
 @pytest.mark.parametrize("eps", [1e-6, 1e-2])
-def test_add_rmsnorm_unit(name, m, pads, eps):
+def test_add_rmsnorm_unit(name, hidden, m, pads, eps):
     _need_gpu()
     cfg = synth.CONFIGS[name]
+    if hidden is not None:
+        cfg = dataclasses.replace(cfg, dims=dataclasses.replace(cfg.dims, hidden=hidden))
     rng = np.random.default_rng(m)
     y = synth.to_bf16_bits(rng.standard_normal((m, cfg.dims.hidden)).astype(np.float32))
     r, g = synth.norm_inputs(cfg, rows=m)
