@@ -108,19 +108,15 @@ __global__ __launch_bounds__(64) void k_plan(FfnArgs a) {
 // count exit at once, and the hardware dispatcher balances the rest.
 __device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + wave_id(); }
 
-// Gate/up tiles: the 16 MFMA A rows are gate rows n0..n0+7 (rows 0-7) and
-// up rows n0..n0+7 (rows 8-15), so lane l (l < 32) holds gate values and
-// lane l + 32 the up values of the same (column, n); n = n0 + 4 (kq & 1) + i.
-__device__ __forceinline__ const uint8_t* gu_row(const FfnArgs& a, int e, int n0, int c, int kq) {
-  return tile_row(c < 8 ? a.wg : a.wu, (size_t)e * a.I + n0 + (c & 7), a.H / kBlk, kq);
-}
-__device__ __forceinline__ const float* gu_scale(const FfnArgs& a, int e, int n0, int kq) {
-  return (kq < 2 ? a.sg : a.su) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * (a.H / kBlk);
-}
+// Gate/up tiles: the 16 MFMA A rows are the 16 rows n0..n0+15 of one packed
+// weight group, gate rows or up rows (items alternate: gate, then up of the
+// same columns), so each load instruction of the wave reads 1 KB of
+// contiguous memory; lane (kq, c) holds columns n = n0 + 4 kq + i of row c.
 
 // ---------------------------------------------------------------- gate/up (split small steps)
-// M <= kSmallRows: each item is one K segment of one 8-column tile of one
-// union expert (one wave); it writes fp32 partials, reduced in segment order
+// M <= kSmallRows: each item is one K segment of the gate (or the up) rows of
+// one 16-column tile of one union expert (one wave); it writes fp32
+// partials, reduced in segment order
 // by k_post_gateup.  The MFMA columns are the step's rows (column c is row c;
 // rows not routed to the item's expert are computed and dropped); the x
 // codes (a few KB per row, L2-resident) stream through the chain's ring with
@@ -154,7 +150,7 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
     return;
   }
   const int nkb = a.H / kBlk;
-  const int ntI = a.I / 8;
+  const int ntI = a.I / 8;                 // (16-column tile, gate | up) pairs per expert
   const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU;
   const int t = ((int)blockIdx.x - hs_blocks) * 4 + wave_id();
   if (t >= n_items) return;
@@ -162,14 +158,15 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
   const int c = lane & 15, kq = lane >> 4;
   const int seg = t % kSegGU;
   const int item = t / kSegGU;
-  const int u = item / ntI, nt = item % ntI;
-  const int n0 = nt * 8;
+  const int u = item / ntI, rem = item % ntI;
+  const int gu = rem & 1, n0 = (rem >> 1) * 16;
   const int e = a.union_ids[u];
   const bool col = c < a.M && row_real(a.mask, c);
   const int xr = col ? c : 0;
-  const v4f p = fp8_chain(gu_row(a, e, n0, c, kq), gu_scale(a, e, n0, kq), a.xq + (size_t)xr * a.H + kq * 32,
-                                 a.xs + (size_t)xr * nkb, col, seg_begin(nkb, seg, kSegGU),
-                                 seg_begin(nkb, seg + 1, kSegGU));
+  const uint8_t* wp = tile_row(gu ? a.wu : a.wg, (size_t)e * a.I + n0 + c, nkb, kq);
+  const float* swp = (gu ? a.su : a.sg) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * nkb;
+  const v4f p = fp8_chain(wp, swp, a.xq + (size_t)xr * a.H + kq * 32, a.xs + (size_t)xr * nkb, col,
+                          seg_begin(nkb, seg, kSegGU), seg_begin(nkb, seg + 1, kSegGU));
   if (!col) return;
   // slot of (row c, expert e): the expert's rows are listed ascending
   const int lo = a.offs[u], hi = a.offs[u + 1];
@@ -177,7 +174,7 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
   for (int s = lo; s < hi; ++s)
     if (a.rows[s] == c) slot = s;
   if (slot >= 0)
-    store_f4(a.part_gu + (((size_t)seg * a.M * a.K + slot) * 2 + (kq >> 1)) * a.I + n0 + (kq & 1) * 4, p);
+    store_f4(a.part_gu + (((size_t)seg * a.M * a.K + slot) * 2 + gu) * a.I + n0 + 4 * kq, p);
 }
 
 // ---------------------------------------------------------------- requantization
