@@ -387,22 +387,26 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
 // The front of a split small step (M <= kSmallRows), one launch:
 //   blocks [0, E)             logits of expert b, wave w: rows w, w + 8
 //   blocks [E, E + nq)        x quantization, one (row, 128-block) per wave
-//   blocks [E + nq, ...)      shared expert gate/up, one K segment of one
-//                             8-column tile per wave (fp32 partials)
+//   blocks [E + nq, ...)      shared expert gate/up, one K segment of the
+//                             gate or up rows of one 16-column tile per wave
+//                             (fp32 partials)
 // The shared expert needs no routing, so its weights stream while the router
 // runs.
-// Shared expert gate/up, one K segment of one 8-column tile (item t of the
-// segments [seg0, seg0 + nseg)): fp32 partials of g and u for every real row.
+// Shared expert gate/up, one K segment of the gate (or the up) rows of one
+// 16-column tile (item t of the segments [seg0, seg0 + nseg); items
+// alternate gate and up of the same columns, and the 16 rows of one packed
+// group make each load read 1 KB of contiguous memory): fp32 partials of g
+// or u for every real row.
 __device__ __forceinline__ void shared_gu_item(const FfnArgs& f, int t, int seg0, int nseg, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int seg = seg0 + t % nseg, nt = t / nseg;
-  const int n0 = nt * 8;
+  const int seg = seg0 + t % nseg, it = t / nseg;
+  const int gu = it & 1, n0 = (it >> 1) * 16;
   const bool valid = c < f.M && row_real(f.mask, c);
-  const uint8_t* wp = tile_row(c < 8 ? f.wsg : f.wsu, (size_t)n0 + (c & 7), f.H * 2 / kBlk, kq);
+  const uint8_t* wp = tile_row(gu ? f.wsu : f.wsg, (size_t)n0 + c, f.H * 2 / kBlk, kq);
   const uint16_t* bp = f.x + (size_t)(valid ? c : 0) * f.H + kq * 8;
   const int nst = f.H / 32;
   const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));
-  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + (kq >> 1)) * f.Is + n0 + (kq & 1) * 4, p);
+  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + gu) * f.Is + n0 + 4 * kq, p);
 }
 
 // Split steps, first launch: blocks [0, E) logits (one block per expert, wave
