@@ -242,9 +242,9 @@ def graph_replay_us(torch, step, n_graphs, steps, warmup, rt_lib, stream):
 def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
     """Layer time against the row count on the span-8 layer (one committed row
     plus drafts, the same recipe at every count): the small-step path serves
-    up to 16 rows, the tiled path from 17."""
+    up to moe.SMALL_ROWS rows, the tiled path above."""
     out = []
-    for m in (1, 2, 4, 8, 9, 12, 16, 17, 24, 32, 48, 64):
+    for m in (1, 2, 4, 8, 9, 12, 16, 17, 24, 32, 33, 48, 64):
         cfg = synth.with_rows(synth.CONFIGS["span8"], m)
         x_np, mask_np = synth.activations(cfg)
         x = torch.from_numpy(x_np.view(np.int16)).cuda()
@@ -260,7 +260,8 @@ def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
         us, p10, p50, p90 = graph_replay_us(torch, step, len(reps), steps, warmup, rt_lib, stream)
         nu = int(rt.n_union.item())
         rb, fb = decode_bytes(nu, d, m)
-        out.append({"rows": m, "path": "split" if m <= 16 else "tiled", "union_experts": nu, "us": round(us, 2),
+        out.append({"rows": m, "path": "split" if m <= moe.SMALL_ROWS else "tiled", "union_experts": nu,
+                    "us": round(us, 2),
                     "us_p10": round(p10, 2), "us_p90": round(p90, 2),
                     "gbs": round((rb + fb) / (us * 1e-6) / 1e9, 1)})
         log(f"[bench] rows sweep M={m}: {us:.1f} us, |U|={nu}, {(rb + fb) / (us * 1e-6) / 1e9:.0f} GB/s")

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = range(5)
 MAX_ROWS, MAX_EXPERTS, MAX_TOPK, MAX_INTER = 16384, 256, 16, 8192
+SMALL_ROWS = 24      # steps of up to this many rows take the split small-step kernels
 
 
 class MoeError(RuntimeError):

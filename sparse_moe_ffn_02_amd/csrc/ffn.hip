@@ -115,10 +115,10 @@ __device__ __forceinline__ int wave_item() { return blockIdx.x * 4 + wave_id(); 
 
 // ---------------------------------------------------------------- gate/up (split small steps)
 // M <= kSmallRows: each item is one K segment of the gate (or the up) rows of
-// one 16-column tile of one union expert (one wave); it writes fp32
-// partials, reduced in segment order
-// by k_post_gateup.  The MFMA columns are the step's rows (column c is row c;
-// rows not routed to the item's expert are computed and dropped); the x
+// one 16-column tile of one union expert for one row half (one wave); it
+// writes fp32 partials, reduced in segment order by k_post_gateup.  The MFMA
+// columns are the half's rows (column c is row 16 h + c; rows not routed to
+// the item's expert are computed and dropped); the x
 // codes (a few KB per row, L2-resident) stream through the chain's ring with
 // the weights.
 // Shared expert h_s = bf16(silu(g) u) of row r, columns n, n + 1, from the
@@ -151,28 +151,30 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
   }
   const int nkb = a.H / kBlk;
   const int ntI = a.I / 8;                 // (16-column tile, gate | up) pairs per expert
-  const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU;
+  const int nh = row_halves(a.M);
+  const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU * nh;
   const int t = ((int)blockIdx.x - hs_blocks) * 4 + wave_id();
   if (t >= n_items) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
   const int seg = t % kSegGU;
-  const int item = t / kSegGU;
+  const int row = ((t / kSegGU) % nh) * kColRows + c;
+  const int item = t / kSegGU / nh;
   const int u = item / ntI, rem = item % ntI;
   const int gu = rem & 1, n0 = (rem >> 1) * 16;
   const int e = a.union_ids[u];
-  const bool col = c < a.M && row_real(a.mask, c);
-  const int xr = col ? c : 0;
+  const bool col = row < a.M && row_real(a.mask, row);
+  const int xr = col ? row : 0;
   const uint8_t* wp = tile_row(gu ? a.wu : a.wg, (size_t)e * a.I + n0 + c, nkb, kq);
   const float* swp = (gu ? a.su : a.sg) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * nkb;
   const v4f p = fp8_chain(wp, swp, a.xq + (size_t)xr * a.H + kq * 32, a.xs + (size_t)xr * nkb, col,
                           seg_begin(nkb, seg, kSegGU), seg_begin(nkb, seg + 1, kSegGU));
   if (!col) return;
-  // slot of (row c, expert e): the expert's rows are listed ascending
+  // slot of (row, expert e): the expert's rows are listed ascending
   const int lo = a.offs[u], hi = a.offs[u + 1];
   int slot = -1;
   for (int s = lo; s < hi; ++s)
-    if (a.rows[s] == c) slot = s;
+    if (a.rows[s] == row) slot = s;
   if (slot >= 0)
     store_f4(a.part_gu + (((size_t)seg * a.M * a.K + slot) * 2 + gu) * a.I + n0 + 4 * kq, p);
 }
@@ -180,12 +182,14 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
 // ---------------------------------------------------------------- requantization
 // Split steps: routed h per (slot, 128-column block) for the slots in use,
 // from the gate/up segment partials summed in order, h = silu(G) U.
-// Shared expert down, one K segment of one 16-column tile of H: fp32
-// partials for every real row (t < (H / 16) * kSegSD).
+// Shared expert down, one K segment of one 16-column tile of H for one row
+// half: fp32 partials for the half's real rows (t < (H / 16) * kSegSD *
+// row_halves(M)).
 __device__ __forceinline__ void shared_down_item(const FfnArgs& a, int t, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int seg = t % kSegSD, nt = t / kSegSD;
-  const int row = c;
+  const int nh = row_halves(a.M);
+  const int seg = t % kSegSD, nt = t / kSegSD / nh;
+  const int row = ((t / kSegSD) % nh) * kColRows + c;
   const bool valid = row < a.M && row_real(a.mask, row);
   const uint8_t* wp = tile_row(a.wsd, (size_t)nt * 16 + c, a.Is * 2 / kBlk, kq);
   const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
   const int lane = threadIdx.x & 63;
   if ((int)blockIdx.x < sd_blocks) {
     const int t = (int)blockIdx.x * 4 + wave_id();
-    if (t < (a.H / 16) * kSegSD) shared_down_item(a, t, lane);
+    if (t < (a.H / 16) * kSegSD * row_halves(a.M)) shared_down_item(a, t, lane);
     return;
   }
   const long item = (long)((int)blockIdx.x - sd_blocks) * 4 + wave_id();
@@ -228,25 +232,27 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
 
 // ---------------------------------------------------------------- down (split small steps)
 // Per-segment items: routed D[slot, n] partials for 16 columns of H and one
-// union expert's slots (at most kSmallRows).
+// half (16 slots) of one union expert's slots (at most kSmallRows in all).
 constexpr int kCols = 16;
 
 __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a, int sd_blocks) {
   const int lane = threadIdx.x & 63;
   if ((int)blockIdx.x < sd_blocks) {
     const int t = (int)blockIdx.x * 4 + wave_id();
-    if (t < (a.H / 16) * kSegSD) shared_down_item(a, t, lane);
+    if (t < (a.H / 16) * kSegSD * row_halves(a.M)) shared_down_item(a, t, lane);
     return;
   }
   const int c = lane & 15, kq = lane >> 4;
   const int ntH = a.H / kCols;
-  const int total = a.sched[SCHED_MTILES] * ntH * kSegDN;
+  const int nh = row_halves(a.M);
+  const int total = a.sched[SCHED_MTILES] * ntH * kSegDN * nh;
   const int t = ((int)blockIdx.x - sd_blocks) * 4 + wave_id();
   if (t >= total) return;
-  const int seg = t % kSegDN, it = t / kSegDN;
+  const int seg = t % kSegDN, it = t / kSegDN / nh;
+  const int i = ((t / kSegDN) % nh) * kColRows + c;   // the lane's slot in the expert's list
   const Tile tl = routed_tile(a, it / ntH);
   const int nt = it % ntH;
-  const int slot = c < tl.mcnt ? tl.s0 + c : -1;
+  const int slot = i < tl.mcnt ? tl.s0 + i : -1;
   const int nkb = a.I / kBlk;
   const uint8_t* wp = tile_row(a.wd, (size_t)tl.e * a.H + nt * kCols + c, nkb, kq);
   const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * kCols) / kBlk) * nkb;
@@ -560,15 +566,16 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, const NormArgs* nm) {
     // one slot tile per union expert; the shared expert's gate/up ran in the front launch
     // gate/up also forms the shared h_s; the requantization launch also runs
     // the shared down, in the time it would spend on latency alone
-    const long items = max_union * (a.I / 8) * kSegGU;
+    const int nh = row_halves(a.M);
+    const long items = max_union * (a.I / 8) * kSegGU * nh;
     const int gu_blocks = (int)((items + 3) / 4);
     const int hs_blocks = with_shared ? (int)(((long)a.M * a.Is / 2 + 255) / 256) : 0;
     MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)(hs_blocks + gu_blocks)), dim3(256), 0, s, a, hs_blocks);
     const long post_waves = (long)a.M * a.K * (a.I / kBlk);
     const int post_blocks = (int)((post_waves + 3) / 4);
     MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)post_blocks), dim3(256), 0, s, a, 0);
-    const int sd_blocks = with_shared ? ((a.H / 16) * kSegSD + 3) / 4 : 0;
-    const long dn_items = max_union * (a.H / kCols) * kSegDN;
+    const int sd_blocks = with_shared ? ((a.H / 16) * kSegSD * nh + 3) / 4 : 0;
+    const long dn_items = max_union * (a.H / kCols) * kSegDN * nh;
     MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)(sd_blocks + (dn_items + 3) / 4)), dim3(256), 0, s, a, sd_blocks);
   } else {
     // slot tiles: at most ceil(M*K / kMTile) + (union size), one partial tile per expert

@@ -8,8 +8,12 @@
 namespace moe {
 
 constexpr int kMTile = 128;          // slots (or rows) per tile of the tiled grouped GEMMs
-constexpr int kDecodeMaxRows = 16;  // rows served by the small-step router kernels
-constexpr int kSmallRows = 16;      // rows served by the split small-step expert kernels (one MFMA column each)
+constexpr int kDecodeMaxRows = 32;  // rows served by the small-step router kernels
+constexpr int kSmallRows = 24;      // rows served by the split small-step expert kernels (measured crossover)
+// The split kernels' work items take the step's rows (or an expert's slots)
+// as the 16 MFMA columns, in row halves of kColRows: rows 16 h .. 16 h + 15.
+constexpr int kColRows = 16;
+__host__ __device__ inline int row_halves(int m) { return (m + kColRows - 1) / kColRows; }
 constexpr int kUChunks = 64;        // row chunks of the larger-step union
 // Every GEMM element is the fixed-order sum of its K-segment chains:
 // routed gate/up over kSegGU segments of K = H, shared gate/up over kSegSG,

@@ -12,6 +12,8 @@
 // selection agrees with a float64 evaluation except on near-exact ties.
 #include <string.h>
 
+#include <algorithm>
+
 #include "moe_chains.h"
 
 namespace moe {
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(kMaxExperts) void k_union_scatter(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- small steps
-// For M <= 16 rows.  Logits: one workgroup per expert with one wave per row,
+// For M <= 32 rows.  Logits: one workgroup per expert with one wave per row,
 // the row's chunks streamed through a ring (same per-lane procedure as
 // above); the kernel also stores sigmoid(l) and the biased score c.  Then one
 // workgroup selects every row's top-k by rank and builds the union and the
@@ -379,13 +381,13 @@ __device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int 
 
 __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int r = wave_id();          // one wave per row
-  if (r >= a.M || (a.mask != nullptr && a.mask[r] == 0)) return;
-  logit_row(a, r, blockIdx.x, lane);
+  const int nw = blockDim.x >> 6;
+  for (int r = wave_id(); r < a.M; r += nw)      // one wave per row (and row + nw, ...)
+    if (a.mask == nullptr || a.mask[r] != 0) logit_row(a, r, blockIdx.x, lane);
 }
 
 // The front of a split small step (M <= kSmallRows), one launch:
-//   blocks [0, E)             logits of expert b, wave w: rows w, w + 8
+//   blocks [0, E)             logits of expert b, wave w: rows w, w + 8, ...
 //   blocks [E, E + nq)        x quantization, one (row, 128-block) per wave
 //   blocks [E + nq, ...)      shared expert gate/up, one K segment of the
 //                             gate or up rows of one 16-column tile per wave
@@ -393,24 +395,27 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
 // The shared expert needs no routing, so its weights stream while the router
 // runs.
 // Shared expert gate/up, one K segment of the gate (or the up) rows of one
-// 16-column tile (item t of the segments [seg0, seg0 + nseg); items
-// alternate gate and up of the same columns, and the 16 rows of one packed
-// group make each load read 1 KB of contiguous memory): fp32 partials of g
-// or u for every real row.
+// 16-column tile for one row half (item t of the segments [seg0, seg0 +
+// nseg); items alternate gate and up of the same columns, and the 16 rows of
+// one packed group make each load read 1 KB of contiguous memory): fp32
+// partials of g or u for the half's real rows.  Items per segment:
+// (Is / 8) * row_halves(M).
 __device__ __forceinline__ void shared_gu_item(const FfnArgs& f, int t, int seg0, int nseg, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int seg = seg0 + t % nseg, it = t / nseg;
+  const int nh = row_halves(f.M);
+  const int seg = seg0 + t % nseg, rest = t / nseg;
+  const int row = (rest % nh) * kColRows + c, it = rest / nh;
   const int gu = it & 1, n0 = (it >> 1) * 16;
-  const bool valid = c < f.M && row_real(f.mask, c);
+  const bool valid = row < f.M && row_real(f.mask, row);
   const uint8_t* wp = tile_row(gu ? f.wsu : f.wsg, (size_t)n0 + c, f.H * 2 / kBlk, kq);
-  const uint16_t* bp = f.x + (size_t)(valid ? c : 0) * f.H + kq * 8;
+  const uint16_t* bp = f.x + (size_t)(valid ? row : 0) * f.H + kq * 8;
   const int nst = f.H / 32;
   const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));
-  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + c) * 2 + gu) * f.Is + n0 + 4 * kq, p);
+  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + row) * 2 + gu) * f.Is + n0 + 4 * kq, p);
 }
 
 // Split steps, first launch: blocks [0, E) logits (one block per expert, wave
-// w serving rows w, w + 8); then the x quantization; then the shared expert's gate/up
+// w serving rows w, w + 8, ...); then the x quantization; then the shared expert's gate/up
 // for the first half of its K segments (the second half runs beside the
 // top-k in k_select_union_small).
 __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
@@ -432,11 +437,11 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
     return;
   }
   const int t = (b - r.E - nq) * 8 + wave;
-  if (f.Is == 0 || t >= (f.Is / 8) * (kSegSG / 2)) return;
+  if (f.Is == 0 || t >= (f.Is / 8) * (kSegSG / 2) * row_halves(f.M)) return;
   shared_gu_item(f, t, 0, kSegSG / 2, lane);
 }
 
-// Block 0 (8 waves; wave w serves rows w, w + 8): top-k of every row, then the
+// Block 0 (8 waves; wave w serves rows w, w + 8, ...): top-k of every row, then the
 // union and the row lists in LDS.  With do_sh, blocks >= 1 run the shared
 // expert's gate/up for the second half of its K segments.
 constexpr int kSelWaves = 8;
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs
   if (blockIdx.x > 0) {
     if (!do_sh) return;
     const int t = (blockIdx.x - 1) * kSelWaves + wave;
-    if (t >= (f.Is / 8) * (kSegSG - kSegSG / 2)) return;
+    if (t >= (f.Is / 8) * (kSegSG - kSegSG / 2) * row_halves(f.M)) return;
     shared_gu_item(f, t, kSegSG / 2, kSegSG - kSegSG / 2, lane);
     return;
   }
@@ -578,7 +583,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.M <= kDecodeMaxRows) {
     FfnArgs none;
     memset(&none, 0, sizeof(none));
-    MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * a.M), 0, s, a);
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * std::min(a.M, 16)), 0, s, a);
     MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(64 * kSelWaves), 0, s, a, none, 0);
     return hipSuccess;
   }
@@ -597,8 +602,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 
 hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s) {
   const int nq = (f.M * (f.H / kBlk) + 7) / 8;
-  const int items1 = f.Is > 0 ? (f.Is / 8) * (kSegSG / 2) : 0;
-  const int items2 = f.Is > 0 ? (f.Is / 8) * (kSegSG - kSegSG / 2) : 0;
+  const int items1 = f.Is > 0 ? (f.Is / 8) * (kSegSG / 2) * row_halves(f.M) : 0;
+  const int items2 = f.Is > 0 ? (f.Is / 8) * (kSegSG - kSegSG / 2) * row_halves(f.M) : 0;
   MOE_LAUNCH(KID_FRONT, k_front, dim3(r.E + nq + (items1 + 7) / 8), dim3(512), 0, s, r, f, nq);
   MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1 + (items2 + kSelWaves - 1) / kSelWaves),
              dim3(64 * kSelWaves), 0, s, r, f, f.Is > 0 ? 1 : 0);

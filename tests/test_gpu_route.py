@@ -1,5 +1,5 @@
 """moe_route on its own (both routing paths: the small-step logits +
-select/union kernels for M <= 16 and the large-step logits, top-k and
+select/union kernels for M <= 32 and the large-step logits, top-k and
 chunked-union kernels above) against the oracle's routing, and against the
 routing that moe_layer writes for the same rows (one per-logit procedure)."""
 import numpy as np
@@ -42,7 +42,7 @@ def _route(gl, x_bits, mask):
 
 
 @pytest.mark.parametrize("name", ["tiny", "odd"])
-@pytest.mark.parametrize("m", [1, 6, 16, 17, 90])
+@pytest.mark.parametrize("m", [1, 6, 16, 17, 32, 33, 90])
 def test_route_matches_oracle_and_layer(layers, name, m):
     cfg, gl = layers[name]
     d = cfg.dims

@@ -187,7 +187,26 @@ def test_decode_and_generic_paths_give_identical_rows(tiny):
     assert np.array_equal(g["ids"][where], base["ids"])
 
 
-@pytest.mark.parametrize("m", [1, 3, 16, 17, 37, 200])
+@pytest.mark.parametrize("m", [17, 24])
+def test_two_row_halves_match_tiled(tiny, m):
+    """A split step of 17-24 rows (two row halves per work item) and the same
+    rows inside a 40-row tiled step give identical bits."""
+    cfg, gl, _, _ = tiny
+    x = _rows(cfg, m, 300 + m)
+    mask = np.ones(m, np.uint8)
+    mask[m - 2] = 0
+    x[m - 2] = 0x7FC0
+    half = run_layer(gl, x, mask)
+    big = _rows(cfg, 40, 400 + m)
+    big[:m] = x
+    bmask = np.ones(40, np.uint8)
+    bmask[:m] = mask
+    g = run_layer(gl, big, bmask)
+    assert np.array_equal(g["y"][:m], half["y"])
+    assert np.array_equal(g["ids"][:m], half["ids"])
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 17, 24, 25, 32, 33, 37, 200])
 def test_ragged_row_counts(tiny, m):
     cfg, gl, _, _ = tiny
     x = _rows(cfg, m, 100 + m)
