@@ -144,6 +144,18 @@ __device__ __forceinline__ void form_hs(const FfnArgs& a, long idx) {
 // Blocks [0, hs_blocks) form the shared expert's h_s (its gate/up partials
 // are complete by now; first in the grid so they do not extend the tail);
 // the rest run routed items, one wave each.
+// Slot of (row, expert union index u) in the expert's row list (ascending), or -1.
+__device__ __forceinline__ int slot_of_row(const FfnArgs& a, int u, int row) {
+  const int lo = a.offs[u], hi = a.offs[u + 1];
+  int slot = -1;
+  for (int s = lo; s < hi; ++s)
+    if (a.rows[s] == row) slot = s;
+  return slot;
+}
+
+// NB = row halves of the step (1: rows 0..15; 2: rows 0..31, both halves in
+// one item, sharing each weight fragment).
+template <int NB>
 __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) {
   if ((int)blockIdx.x < hs_blocks) {
     form_hs(a, ((long)blockIdx.x * blockDim.x + threadIdx.x) * 2);
@@ -151,64 +163,79 @@ __global__ __launch_bounds__(256) void k_gateup_split(FfnArgs a, int hs_blocks) 
   }
   const int nkb = a.H / kBlk;
   const int ntI = a.I / 8;                 // (16-column tile, gate | up) pairs per expert
-  const int nh = row_halves(a.M);
-  const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU * nh;
+  const int n_items = a.sched[SCHED_NUNION] * ntI * kSegGU;
   const int t = ((int)blockIdx.x - hs_blocks) * 4 + wave_id();
   if (t >= n_items) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;
   const int seg = t % kSegGU;
-  const int row = ((t / kSegGU) % nh) * kColRows + c;
-  const int item = t / kSegGU / nh;
+  const int item = t / kSegGU;
   const int u = item / ntI, rem = item % ntI;
   const int gu = rem & 1, n0 = (rem >> 1) * 16;
   const int e = a.union_ids[u];
-  const bool col = row < a.M && row_real(a.mask, row);
-  const int xr = col ? row : 0;
   const uint8_t* wp = tile_row(gu ? a.wu : a.wg, (size_t)e * a.I + n0 + c, nkb, kq);
   const float* swp = (gu ? a.su : a.sg) + ((size_t)e * (a.I / kBlk) + n0 / kBlk) * nkb;
-  const v4f p = fp8_chain(wp, swp, a.xq + (size_t)xr * a.H + kq * 32, a.xs + (size_t)xr * nkb, col,
-                          seg_begin(nkb, seg, kSegGU), seg_begin(nkb, seg + 1, kSegGU));
-  if (!col) return;
-  // slot of (row, expert e): the expert's rows are listed ascending
-  const int lo = a.offs[u], hi = a.offs[u + 1];
-  int slot = -1;
-  for (int s = lo; s < hi; ++s)
-    if (a.rows[s] == row) slot = s;
-  if (slot >= 0)
-    store_f4(a.part_gu + (((size_t)seg * a.M * a.K + slot) * 2 + gu) * a.I + n0 + 4 * kq, p);
+  const int kb0 = seg_begin(nkb, seg, kSegGU), kb1 = seg_begin(nkb, seg + 1, kSegGU);
+  const size_t out = ((size_t)seg * a.M * a.K) * 2;
+  const bool col0 = c < a.M && row_real(a.mask, c);
+  const int xr0 = col0 ? c : 0;
+  if (NB == 1) {
+    const v4f p = fp8_chain(wp, swp, a.xq + (size_t)xr0 * a.H + kq * 32, a.xs + (size_t)xr0 * nkb, col0, kb0, kb1);
+    if (!col0) return;
+    const int slot = slot_of_row(a, u, c);
+    if (slot >= 0) store_f4(a.part_gu + (out + (size_t)slot * 2 + gu) * a.I + n0 + 4 * kq, p);
+  } else {
+    const int r1 = kColRows + c;
+    const bool col1 = r1 < a.M && row_real(a.mask, r1);
+    const int xr1 = col1 ? r1 : 0;
+    v4f p0, p1;
+    fp8_chain2(wp, swp, a.xq + (size_t)xr0 * a.H + kq * 32, a.xq + (size_t)xr1 * a.H + kq * 32,
+               a.xs + (size_t)xr0 * nkb, a.xs + (size_t)xr1 * nkb, col0, col1, kb0, kb1, p0, p1);
+    if (col0) {
+      const int slot = slot_of_row(a, u, c);
+      if (slot >= 0) store_f4(a.part_gu + (out + (size_t)slot * 2 + gu) * a.I + n0 + 4 * kq, p0);
+    }
+    if (col1) {
+      const int slot = slot_of_row(a, u, r1);
+      if (slot >= 0) store_f4(a.part_gu + (out + (size_t)slot * 2 + gu) * a.I + n0 + 4 * kq, p1);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- requantization
 // Split steps: routed h per (slot, 128-column block) for the slots in use,
 // from the gate/up segment partials summed in order, h = silu(G) U.
-// Shared expert down, one K segment of one 16-column tile of H for one row
-// half: fp32 partials for the half's real rows (t < (H / 16) * kSegSD *
-// row_halves(M)).
+// Shared expert down, one K segment of one 16-column tile of H: fp32
+// partials for every real row (t < (H / 16) * kSegSD); NB row halves as in
+// k_gateup_split.
+template <int NB>
 __device__ __forceinline__ void shared_down_item(const FfnArgs& a, int t, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int nh = row_halves(a.M);
-  const int seg = t % kSegSD, nt = t / kSegSD / nh;
-  const int row = ((t / kSegSD) % nh) * kColRows + c;
-  const bool valid = row < a.M && row_real(a.mask, row);
+  const int seg = t % kSegSD, nt = t / kSegSD;
   const uint8_t* wp = tile_row(a.wsd, (size_t)nt * 16 + c, a.Is * 2 / kBlk, kq);
-  const uint16_t* bp = a.hsh + (size_t)(valid ? row : 0) * a.Is + kq * 8;
   const int nst = a.Is / 32;
-  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSD), seg_begin(nst, seg + 1, kSegSD));
-  if (valid) store_f4(a.part_s + ((size_t)seg * a.M + row) * a.H + nt * 16 + kq * 4, p);
+  const int s0 = seg_begin(nst, seg, kSegSD), s1 = seg_begin(nst, seg + 1, kSegSD);
+  const bool v0 = c < a.M && row_real(a.mask, c);
+  const uint16_t* bp0 = a.hsh + (size_t)(v0 ? c : 0) * a.Is + kq * 8;
+  float* out = a.part_s + (size_t)seg * a.M * a.H + nt * 16 + kq * 4;
+  if (NB == 1) {
+    const v4f p = bf16_chain(wp, bp0, v0, s0, s1);
+    if (v0) store_f4(out + (size_t)c * a.H, p);
+  } else {
+    const int r1 = kColRows + c;
+    const bool v1 = r1 < a.M && row_real(a.mask, r1);
+    const uint16_t* bp1 = a.hsh + (size_t)(v1 ? r1 : 0) * a.Is + kq * 8;
+    v4f p0, p1;
+    bf16_chain2(wp, bp0, bp1, v0, v1, s0, s1, p0, p1);
+    if (v0) store_f4(out + (size_t)c * a.H, p0);
+    if (v1) store_f4(out + (size_t)r1 * a.H, p1);
+  }
 }
 
-// Blocks [0, sd_blocks) run the shared expert's down (h_s was formed by the
-// gate/up launch; first in the grid, the longer work); the rest requantize
-// routed h, one wave per (slot, 128-column block).
-__global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
+// Routed h requantization, one wave per (slot, 128-column block).
+__global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a) {
   const int lane = threadIdx.x & 63;
-  if ((int)blockIdx.x < sd_blocks) {
-    const int t = (int)blockIdx.x * 4 + wave_id();
-    if (t < (a.H / 16) * kSegSD * row_halves(a.M)) shared_down_item(a, t, lane);
-    return;
-  }
-  const long item = (long)((int)blockIdx.x - sd_blocks) * 4 + wave_id();
+  const long item = (long)blockIdx.x * 4 + wave_id();
   const int nbI = a.I / kBlk;
   const int slot = (int)(item / nbI);
   const int b = (int)(item % nbI);
@@ -235,32 +262,45 @@ __global__ __launch_bounds__(256) void k_post_gateup(FfnArgs a, int sd_blocks) {
 // half (16 slots) of one union expert's slots (at most kSmallRows in all).
 constexpr int kCols = 16;
 
+// NB row halves as in k_gateup_split: an item covers the expert's slots
+// 0..15 (and 16..31 when NB = 2).
+template <int NB>
 __global__ __launch_bounds__(256, 2) void k_down(FfnArgs a, int sd_blocks) {
   const int lane = threadIdx.x & 63;
   if ((int)blockIdx.x < sd_blocks) {
     const int t = (int)blockIdx.x * 4 + wave_id();
-    if (t < (a.H / 16) * kSegSD * row_halves(a.M)) shared_down_item(a, t, lane);
+    if (t < (a.H / 16) * kSegSD) shared_down_item<NB>(a, t, lane);
     return;
   }
   const int c = lane & 15, kq = lane >> 4;
   const int ntH = a.H / kCols;
-  const int nh = row_halves(a.M);
-  const int total = a.sched[SCHED_MTILES] * ntH * kSegDN * nh;
+  const int total = a.sched[SCHED_MTILES] * ntH * kSegDN;
   const int t = ((int)blockIdx.x - sd_blocks) * 4 + wave_id();
   if (t >= total) return;
-  const int seg = t % kSegDN, it = t / kSegDN / nh;
-  const int i = ((t / kSegDN) % nh) * kColRows + c;   // the lane's slot in the expert's list
+  const int seg = t % kSegDN, it = t / kSegDN;
   const Tile tl = routed_tile(a, it / ntH);
   const int nt = it % ntH;
-  const int slot = i < tl.mcnt ? tl.s0 + i : -1;
   const int nkb = a.I / kBlk;
   const uint8_t* wp = tile_row(a.wd, (size_t)tl.e * a.H + nt * kCols + c, nkb, kq);
   const float* swp = a.sd + ((size_t)tl.e * (a.H / kBlk) + (nt * kCols) / kBlk) * nkb;
-  const uint8_t* bp = a.hq + (size_t)(slot < 0 ? 0 : slot) * a.I + kq * 32;
-  const float* shp = a.hs + (size_t)(slot < 0 ? 0 : slot) * nkb;
-  const v4f p = fp8_chain(wp, swp, bp, shp, slot >= 0, seg_begin(nkb, seg, kSegDN),
-                                 seg_begin(nkb, seg + 1, kSegDN));
-  if (slot >= 0) store_f4(a.part_d + ((size_t)seg * a.M * a.K + slot) * a.H + nt * kCols + kq * 4, p);
+  const int kb0 = seg_begin(nkb, seg, kSegDN), kb1 = seg_begin(nkb, seg + 1, kSegDN);
+  float* out = a.part_d + (size_t)seg * a.M * a.K * a.H + nt * kCols + kq * 4;
+  const int slot0 = c < tl.mcnt ? tl.s0 + c : -1;
+  const uint8_t* bp0 = a.hq + (size_t)(slot0 < 0 ? 0 : slot0) * a.I + kq * 32;
+  const float* shp0 = a.hs + (size_t)(slot0 < 0 ? 0 : slot0) * nkb;
+  if (NB == 1) {
+    const v4f p = fp8_chain(wp, swp, bp0, shp0, slot0 >= 0, kb0, kb1);
+    if (slot0 >= 0) store_f4(out + (size_t)slot0 * a.H, p);
+  } else {
+    const int i1 = kColRows + c;
+    const int slot1 = i1 < tl.mcnt ? tl.s0 + i1 : -1;
+    const uint8_t* bp1 = a.hq + (size_t)(slot1 < 0 ? 0 : slot1) * a.I + kq * 32;
+    const float* shp1 = a.hs + (size_t)(slot1 < 0 ? 0 : slot1) * nkb;
+    v4f p0, p1;
+    fp8_chain2(wp, swp, bp0, bp1, shp0, shp1, slot0 >= 0, slot1 >= 0, kb0, kb1, p0, p1);
+    if (slot0 >= 0) store_f4(out + (size_t)slot0 * a.H, p0);
+    if (slot1 >= 0) store_f4(out + (size_t)slot1 * a.H, p1);
+  }
 }
 
 // ---------------------------------------------------------------- combine
@@ -564,19 +604,28 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, const NormArgs* nm) {
   const long max_union = std::min<long>(a.E, (long)a.M * a.K);
   if (a.split) {
     // one slot tile per union expert; the shared expert's gate/up ran in the front launch
-    // gate/up also forms the shared h_s; the requantization launch also runs
-    // the shared down, in the time it would spend on latency alone
+    // gate/up also forms the shared h_s; the down launch also runs the shared down
     const int nh = row_halves(a.M);
-    const long items = max_union * (a.I / 8) * kSegGU * nh;
+    const long items = max_union * (a.I / 8) * kSegGU;
     const int gu_blocks = (int)((items + 3) / 4);
     const int hs_blocks = with_shared ? (int)(((long)a.M * a.Is / 2 + 255) / 256) : 0;
-    MOE_LAUNCH(KID_GATEUP, k_gateup_split, dim3((unsigned)(hs_blocks + gu_blocks)), dim3(256), 0, s, a, hs_blocks);
+    const dim3 gu_grid((unsigned)(hs_blocks + gu_blocks));
+    if (nh == 1) {
+      MOE_LAUNCH(KID_GATEUP, k_gateup_split<1>, gu_grid, dim3(256), 0, s, a, hs_blocks);
+    } else {
+      MOE_LAUNCH(KID_GATEUP, k_gateup_split<2>, gu_grid, dim3(256), 0, s, a, hs_blocks);
+    }
     const long post_waves = (long)a.M * a.K * (a.I / kBlk);
     const int post_blocks = (int)((post_waves + 3) / 4);
-    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)post_blocks), dim3(256), 0, s, a, 0);
-    const int sd_blocks = with_shared ? ((a.H / 16) * kSegSD * nh + 3) / 4 : 0;
-    const long dn_items = max_union * (a.H / kCols) * kSegDN * nh;
-    MOE_LAUNCH(KID_DOWN, k_down, dim3((unsigned)(sd_blocks + (dn_items + 3) / 4)), dim3(256), 0, s, a, sd_blocks);
+    MOE_LAUNCH(KID_POST_GATEUP, k_post_gateup, dim3((unsigned)post_blocks), dim3(256), 0, s, a);
+    const int sd_blocks = with_shared ? ((a.H / 16) * kSegSD + 3) / 4 : 0;
+    const long dn_items = max_union * (a.H / kCols) * kSegDN;
+    const dim3 dn_grid((unsigned)(sd_blocks + (dn_items + 3) / 4));
+    if (nh == 1) {
+      MOE_LAUNCH(KID_DOWN, k_down<1>, dn_grid, dim3(256), 0, s, a, sd_blocks);
+    } else {
+      MOE_LAUNCH(KID_DOWN, k_down<2>, dn_grid, dim3(256), 0, s, a, sd_blocks);
+    }
   } else {
     // slot tiles: at most ceil(M*K / kMTile) + (union size), one partial tile per expert
     const long mtiles_max = ((long)a.M * a.K + kMTile - 1) / kMTile + max_union;

@@ -146,6 +146,60 @@ __device__ __forceinline__ v4f fp8_chain(const uint8_t* wp, const float* swp, co
   return acc;
 }
 
+// The same chain for two B tiles (two row halves) sharing each A fragment:
+// acc0 over B rows bp0 (valid v0), acc1 over bp1 (v1).  Each accumulator
+// takes exactly the steps fp8_chain gives it, so the values are the same.
+__device__ __forceinline__ void fp8_chain2(const uint8_t* wp, const float* swp, const uint8_t* bp0,
+                                           const uint8_t* bp1, const float* sxp0, const float* sxp1, bool v0,
+                                           bool v1, int kb0, int kb1, v4f& acc0, v4f& acc1) {
+  acc0 = v4f{0.f, 0.f, 0.f, 0.f};
+  acc1 = acc0;
+  if (kb0 >= kb1) return;
+  const int last = kb1 - 1;
+  const int keep0 = v0 ? -1 : 0, keep1 = v1 ? -1 : 0;
+  v8i wb[kRing], xa[kRing], xc[kRing];
+  float swb[kRing], sa[kRing], sc[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    const int kb = min(kb0 + i, last);
+    wb[i] = load_frag(wp + (size_t)kb * kTile);
+    swb[i] = swp[kb];
+    xa[i] = load32(bp0 + kb * kBlk);
+    sa[i] = sxp0[kb];
+    xc[i] = load32(bp1 + kb * kBlk);
+    sc[i] = sxp1[kb];
+  }
+  auto step = [&](int i) {
+    const v4f p0 = mfma_fp8_k128(wb[i], mask8(xa[i], keep0));
+    scale_acc(acc0, p0, v0 ? sa[i] : 0.0f, swb[i]);
+    const v4f p1 = mfma_fp8_k128(wb[i], mask8(xc[i], keep1));
+    scale_acc(acc1, p1, v1 ? sc[i] : 0.0f, swb[i]);
+  };
+  auto refill = [&](int i, int nk) {
+    wb[i] = load_frag(wp + (size_t)nk * kTile);
+    swb[i] = swp[nk];
+    xa[i] = load32(bp0 + nk * kBlk);
+    sa[i] = sxp0[nk];
+    xc[i] = load32(bp1 + nk * kBlk);
+    sc[i] = sxp1[nk];
+  };
+  int k0 = kb0;
+  for (; k0 + 2 * kRing <= kb1; k0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      step(i);
+      refill(i, k0 + i + kRing);
+    }
+  }
+  for (; k0 < kb1; k0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      if (k0 + i < kb1) step(i);
+      if (k0 + i + kRing < kb1) refill(i, k0 + i + kRing);
+    }
+  }
+}
+
 // bf16 chain over K-steps [s0, s1) (32 deep each) for one 16x16 tile; loads
 // as in fp8_chain.  wp = the lane's packed tile_row address at stage 0 (step
 // st is in stage st / 2, half st % 2); bp = the lane's row-major B row.
@@ -188,6 +242,53 @@ __device__ __forceinline__ v4f bf16_chain(const uint8_t* wp, const uint16_t* bp,
     }
   }
   return settle_bf16(acc);
+}
+
+// bf16_chain for two B tiles (two row halves) sharing each A fragment; each
+// accumulator takes exactly the steps bf16_chain gives it.
+__device__ __forceinline__ void bf16_chain2(const uint8_t* wp, const uint16_t* bp0, const uint16_t* bp1, bool v0,
+                                            bool v1, int s0, int s1, v4f& acc0, v4f& acc1) {
+  acc0 = v4f{0.f, 0.f, 0.f, 0.f};
+  acc1 = acc0;
+  if (s0 >= s1) return;
+  const int last = s1 - 1;
+  const int keep0 = v0 ? -1 : 0, keep1 = v1 ? -1 : 0;
+  v4i wb[kRingBf], xa[kRingBf], xc[kRingBf];
+#pragma unroll
+  for (int i = 0; i < kRingBf; ++i) {
+    const int st = min(s0 + i, last);
+    wb[i] = load_step(wp, st);
+    xa[i] = load16(bp0 + st * 32);
+    xc[i] = load16(bp1 + st * 32);
+  }
+  int k0 = s0;
+  for (; k0 + 2 * kRingBf <= s1; k0 += kRingBf) {
+#pragma unroll
+    for (int i = 0; i < kRingBf; ++i) {
+      acc0 = mfma_bf16_k32(wb[i], mask4(xa[i], keep0), acc0);
+      acc1 = mfma_bf16_k32(wb[i], mask4(xc[i], keep1), acc1);
+      wb[i] = load_step(wp, k0 + i + kRingBf);
+      xa[i] = load16(bp0 + (k0 + i + kRingBf) * 32);
+      xc[i] = load16(bp1 + (k0 + i + kRingBf) * 32);
+    }
+  }
+  for (; k0 < s1; k0 += kRingBf) {
+#pragma unroll
+    for (int i = 0; i < kRingBf; ++i) {
+      if (k0 + i < s1) {
+        acc0 = mfma_bf16_k32(wb[i], mask4(xa[i], keep0), acc0);
+        acc1 = mfma_bf16_k32(wb[i], mask4(xc[i], keep1), acc1);
+      }
+      const int nx = k0 + i + kRingBf;
+      if (nx < s1) {
+        wb[i] = load_step(wp, nx);
+        xa[i] = load16(bp0 + nx * 32);
+        xc[i] = load16(bp1 + nx * 32);
+      }
+    }
+  }
+  acc0 = settle_bf16(acc0);
+  acc1 = settle_bf16(acc1);
 }
 
 // ---------------------------------------------------------------- slot tiles

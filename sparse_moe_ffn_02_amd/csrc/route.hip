@@ -395,29 +395,41 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
 // The shared expert needs no routing, so its weights stream while the router
 // runs.
 // Shared expert gate/up, one K segment of the gate (or the up) rows of one
-// 16-column tile for one row half (item t of the segments [seg0, seg0 +
-// nseg); items alternate gate and up of the same columns, and the 16 rows of
-// one packed group make each load read 1 KB of contiguous memory): fp32
-// partials of g or u for the half's real rows.  Items per segment:
-// (Is / 8) * row_halves(M).
+// 16-column tile (item t of the segments [seg0, seg0 + nseg); items
+// alternate gate and up of the same columns, and the 16 rows of one packed
+// group make each load read 1 KB of contiguous memory): fp32 partials of g
+// or u for every real row.  NB row halves: rows 0..15 (and 16..31 when
+// NB = 2, sharing each weight fragment).
+template <int NB>
 __device__ __forceinline__ void shared_gu_item(const FfnArgs& f, int t, int seg0, int nseg, int lane) {
   const int c = lane & 15, kq = lane >> 4;
-  const int nh = row_halves(f.M);
-  const int seg = seg0 + t % nseg, rest = t / nseg;
-  const int row = (rest % nh) * kColRows + c, it = rest / nh;
+  const int seg = seg0 + t % nseg, it = t / nseg;
   const int gu = it & 1, n0 = (it >> 1) * 16;
-  const bool valid = row < f.M && row_real(f.mask, row);
   const uint8_t* wp = tile_row(gu ? f.wsu : f.wsg, (size_t)n0 + c, f.H * 2 / kBlk, kq);
-  const uint16_t* bp = f.x + (size_t)(valid ? row : 0) * f.H + kq * 8;
   const int nst = f.H / 32;
-  const v4f p = bf16_chain(wp, bp, valid, seg_begin(nst, seg, kSegSG), seg_begin(nst, seg + 1, kSegSG));
-  if (valid) store_f4(f.part_sh + (((size_t)seg * f.M + row) * 2 + gu) * f.Is + n0 + 4 * kq, p);
+  const int s0 = seg_begin(nst, seg, kSegSG), s1 = seg_begin(nst, seg + 1, kSegSG);
+  float* out = f.part_sh + ((size_t)seg * f.M * 2 + gu) * f.Is + n0 + 4 * kq;
+  const bool v0 = c < f.M && row_real(f.mask, c);
+  const uint16_t* bp0 = f.x + (size_t)(v0 ? c : 0) * f.H + kq * 8;
+  if (NB == 1) {
+    const v4f p = bf16_chain(wp, bp0, v0, s0, s1);
+    if (v0) store_f4(out + (size_t)c * 2 * f.Is, p);
+  } else {
+    const int r1 = kColRows + c;
+    const bool v1 = r1 < f.M && row_real(f.mask, r1);
+    const uint16_t* bp1 = f.x + (size_t)(v1 ? r1 : 0) * f.H + kq * 8;
+    v4f p0, p1;
+    bf16_chain2(wp, bp0, bp1, v0, v1, s0, s1, p0, p1);
+    if (v0) store_f4(out + (size_t)c * 2 * f.Is, p0);
+    if (v1) store_f4(out + (size_t)r1 * 2 * f.Is, p1);
+  }
 }
 
 // Split steps, first launch: blocks [0, E) logits (one block per expert, wave
 // w serving rows w, w + 8, ...); then the x quantization; then the shared expert's gate/up
 // for the first half of its K segments (the second half runs beside the
 // top-k in k_select_union_small).
+template <int NB>
 __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int b = blockIdx.x;
@@ -437,8 +449,8 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
     return;
   }
   const int t = (b - r.E - nq) * 8 + wave;
-  if (f.Is == 0 || t >= (f.Is / 8) * (kSegSG / 2) * row_halves(f.M)) return;
-  shared_gu_item(f, t, 0, kSegSG / 2, lane);
+  if (f.Is == 0 || t >= (f.Is / 8) * (kSegSG / 2)) return;
+  shared_gu_item<NB>(f, t, 0, kSegSG / 2, lane);
 }
 
 // Block 0 (8 waves; wave w serves rows w, w + 8, ...): top-k of every row, then the
@@ -446,6 +458,7 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
 // expert's gate/up for the second half of its K segments.
 constexpr int kSelWaves = 8;
 
+template <int NB>
 __global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs a, FfnArgs f, int do_sh) {
   __shared__ double ssig[kDecodeMaxRows][kMaxTopK];
   __shared__ int sid[kDecodeMaxRows][kMaxTopK];
@@ -456,8 +469,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs
   if (blockIdx.x > 0) {
     if (!do_sh) return;
     const int t = (blockIdx.x - 1) * kSelWaves + wave;
-    if (t >= (f.Is / 8) * (kSegSG - kSegSG / 2) * row_halves(f.M)) return;
-    shared_gu_item(f, t, kSegSG / 2, kSegSG - kSegSG / 2, lane);
+    if (t >= (f.Is / 8) * (kSegSG - kSegSG / 2)) return;
+    shared_gu_item<NB>(f, t, kSegSG / 2, kSegSG - kSegSG / 2, lane);
     return;
   }
   const int nwords = (a.E + 31) / 32;
@@ -584,7 +597,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     FfnArgs none;
     memset(&none, 0, sizeof(none));
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * std::min(a.M, 16)), 0, s, a);
-    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1), dim3(64 * kSelWaves), 0, s, a, none, 0);
+    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small<1>, dim3(1), dim3(64 * kSelWaves), 0, s, a, none, 0);
     return hipSuccess;
   }
   {
@@ -602,11 +615,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 
 hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s) {
   const int nq = (f.M * (f.H / kBlk) + 7) / 8;
-  const int items1 = f.Is > 0 ? (f.Is / 8) * (kSegSG / 2) * row_halves(f.M) : 0;
-  const int items2 = f.Is > 0 ? (f.Is / 8) * (kSegSG - kSegSG / 2) * row_halves(f.M) : 0;
-  MOE_LAUNCH(KID_FRONT, k_front, dim3(r.E + nq + (items1 + 7) / 8), dim3(512), 0, s, r, f, nq);
-  MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small, dim3(1 + (items2 + kSelWaves - 1) / kSelWaves),
-             dim3(64 * kSelWaves), 0, s, r, f, f.Is > 0 ? 1 : 0);
+  const int items1 = f.Is > 0 ? (f.Is / 8) * (kSegSG / 2) : 0;
+  const int items2 = f.Is > 0 ? (f.Is / 8) * (kSegSG - kSegSG / 2) : 0;
+  const dim3 fg((unsigned)(r.E + nq + (items1 + 7) / 8)), sg((unsigned)(1 + (items2 + kSelWaves - 1) / kSelWaves));
+  const int do_sh = f.Is > 0 ? 1 : 0;
+  if (row_halves(f.M) == 1) {
+    MOE_LAUNCH(KID_FRONT, k_front<1>, fg, dim3(512), 0, s, r, f, nq);
+    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small<1>, sg, dim3(64 * kSelWaves), 0, s, r, f, do_sh);
+  } else {
+    MOE_LAUNCH(KID_FRONT, k_front<2>, fg, dim3(512), 0, s, r, f, nq);
+    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small<2>, sg, dim3(64 * kSelWaves), 0, s, r, f, do_sh);
+  }
   return hipSuccess;
 }
 

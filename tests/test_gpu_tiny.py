@@ -189,7 +189,7 @@ def test_decode_and_generic_paths_give_identical_rows(tiny):
 
 @pytest.mark.parametrize("m", [17, 24])
 def test_two_row_halves_match_tiled(tiny, m):
-    """A split step of 17-24 rows (two row halves per work item) and the same
+    """A split step of 17-24 rows (both row halves in each work item) and the same
     rows inside a 40-row tiled step give identical bits."""
     cfg, gl, _, _ = tiny
     x = _rows(cfg, m, 300 + m)
