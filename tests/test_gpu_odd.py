@@ -4,6 +4,8 @@ part-way), 40 experts (not a multiple of 64: top-k lanes and union words
 partly empty), top-6, inter 384 (three 128-blocks), a one-block shared
 expert.  Both execution paths: an 8-row step (split) and a 150-row step
 (tiled) that carries the same 8 rows first."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -62,3 +64,29 @@ def test_odd_tiled_step_and_row_identity(odd):
     small = run_layer(gl, x, mask)
     assert np.array_equal(g["y"][:8], small["y"])
     assert np.array_equal(g["ids"][:8], small["ids"])
+
+
+@pytest.fixture(scope="module")
+def narrow():
+    """The smallest legal hidden size, 128: one K-block, so the first of the
+    two gate/up K segments is empty, and a one-block shared expert."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load()
+    base = synth.CONFIGS["odd"]
+    cfg = dataclasses.replace(base, dims=dataclasses.replace(base.dims, hidden=128), seed=1007)
+    gl = GpuLayer(synth.make_layer(cfg, threads=4))
+    return cfg, gl
+
+
+@pytest.mark.parametrize("m", [8, 20, 60])        # split, split with two row halves, tiled
+def test_narrow_hidden(narrow, m):
+    cfg, gl = narrow
+    x, mask = synth.activations(synth.with_rows(cfg, m))
+    mask = mask.copy()
+    x = x.copy()
+    mask[m // 2] = 0
+    x[m // 2] = 0x7FC0
+    say(f"hidden 128 layer M={m}")
+    g, err, bad, n = _check(gl, x, mask)
+    say(f"hidden 128 M={m}: max row rel err {err:.3e}, h code flips {bad}/{n}")
