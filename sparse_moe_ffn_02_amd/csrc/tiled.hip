@@ -169,8 +169,10 @@ __device__ __forceinline__ void lds_frag_pair(const uint8_t* lb, const float* ls
   }
 }
 
-// One K stage on LDS buffer `buf` with A fragments `a`.
-template <bool kFp8>
+// One K stage on LDS buffer `buf` with A fragments `a`.  fp8: only slot
+// tiles 0 .. NL - 1 are computed; the caller picks NL >= the tile's slot
+// tiles holding real rows (the rest hold zero codes and are never stored).
+template <bool kFp8, int NL>
 __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const AStage& as, int st, Acc& acc, Acc& tot,
                                            SegState& g) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
@@ -184,8 +186,8 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
     float sx[2], sxn[2];
     lds_frag_pair(L.b[buf], L.s[buf], 0, c, q, xb, sx);
 #pragma unroll
-    for (int b = 0; b < kNB; b += 2) {
-      if (b + 2 < kNB) lds_frag_pair(L.b[buf], L.s[buf], b + 2, c, q, xn, sxn);
+    for (int b = 0; b < NL; b += 2) {
+      if (b + 2 < NL) lds_frag_pair(L.b[buf], L.s[buf], b + 2, c, q, xn, sxn);
       v4f p0 = mfma_fp8_raw(a[0], xb[0]), p1 = mfma_fp8_raw(a[1], xb[0]);
       v4f p2 = mfma_fp8_raw(a[0], xb[1]), p3 = mfma_fp8_raw(a[1], xb[1]);
       settle4(p0, p1, p2, p3);
@@ -194,7 +196,7 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
       scale_acc(acc[0][b + 1], p2, sx[1], sw0);
       scale_acc(acc[1][b + 1], p3, sx[1], sw1);
       asm volatile("" : "+v"(acc[0][b]), "+v"(acc[1][b]), "+v"(acc[0][b + 1]), "+v"(acc[1][b + 1]));
-      if (b + 2 < kNB) {
+      if (b + 2 < NL) {
         xb[0] = xn[0];
         xb[1] = xn[1];
         sx[0] = sxn[0];
@@ -231,9 +233,10 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
 // block scales are loaded kRingA stages ahead into registers (3 where the
 // registers allow it, else 2); activation rows two stages ahead into
 // registers, then into the LDS double buffer one stage ahead.
-template <bool kFp8, int kRingA>
+template <bool kFp8, int kRingA, int NL = kNB>
 __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
   static_assert(kRingA == 2 || kRingA == 3, "weight ring of 2 or 3 stages");
+  static_assert(NL % 2 == 0 && NL >= 2 && NL <= kNB && (kFp8 || NL == kNB), "slot tiles in pairs");
   Acc acc;
 #pragma unroll
   for (int t = 0; t < kNA; ++t)
@@ -271,7 +274,7 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
   {                                                            \
     const int st = st0 + (D);                                  \
     if (st >= n) break;                                        \
-    tile_stage<kFp8>(L, (U), AR, st, acc, tot, g);             \
+    tile_stage<kFp8, NL>(L, (U), AR, st, acc, tot, g);         \
     load_a<kFp8>(AR, in, min(st + kRingA, last));              \
     store_b<kFp8>(L, (U) ^ 1, BN, in);                         \
     load_b<kFp8>(BN, in, min(st + 3, last));                   \
@@ -368,8 +371,11 @@ __device__ __forceinline__ void wide_store_b(uint8_t* smem, int buf, const WB& r
   }
 }
 
-// One K-block on stage buffer `buf`: 32 MFMAs, each partial scaled into its
-// chain as in every other kernel.
+// One K-block on stage buffer `buf`: 4 MFMAs for each of slot tiles
+// 0 .. NL - 1 (32 for a full tile), each partial scaled into its chain as in
+// every other kernel.  The caller picks NL >= the tile's slot tiles holding
+// real rows (the rest hold zero codes and are never stored).
+template <int NL>
 __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const WStage& as, WAcc& acc) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const uint8_t* lb = smem + buf * kWBuf;
@@ -386,8 +392,8 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
   float sx, sxn;
   frag(0, xb, sx);
 #pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    if (b + 1 < kNB) frag(b + 1, xn, sxn);
+  for (int b = 0; b < NL; ++b) {
+    if (b + 1 < NL) frag(b + 1, xn, sxn);
     v4f p0 = mfma_fp8_raw(as.v[0], xb), p1 = mfma_fp8_raw(as.v[1], xb);
     v4f p2 = mfma_fp8_raw(as.v[2], xb), p3 = mfma_fp8_raw(as.v[3], xb);
     settle4(p0, p1, p2, p3);
@@ -398,7 +404,7 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
     // pin the chain updates here: left free, the compiler sinks them below
     // later MFMAs and keeps every partial of the K-block live at once
     asm volatile("" : "+v"(acc[0][b]), "+v"(acc[1][b]), "+v"(acc[2][b]), "+v"(acc[3][b]));
-    if (b + 1 < kNB) {
+    if (b + 1 < NL) {
       xb = xn;
       sx = sxn;
     }
@@ -411,8 +417,13 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
 // activation rows one K-block ahead into registers, then into the LDS double
 // buffer.  Loads past the last K-block reload it (valid, unused), so every
 // step issues the same loads with no branch around them.
+template <int NL>
 __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc& acc) {
   const int n = in.nkb, last = n - 1;
+  // keeps the K loop's first loads below the caller's branch between
+  // instantiations: hoisted above it (they are the same loads in each), they
+  // stretch live ranges across every instantiation and the kernel spills
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int t = 0; t < kWA; ++t)
 #pragma unroll
@@ -427,7 +438,7 @@ __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc&
   __syncthreads();
 #define MOE_WIDE_STEP(S, D, AR)                         \
   {                                                     \
-    wide_stage(smem, (D), AR, acc);                     \
+    wide_stage<NL>(smem, (D), AR, acc);                 \
     wide_load_a(AR, in, min((S) + 2, last));            \
     wide_store_b(smem, (D) ^ 1, br, in);                \
     wide_load_b(br, in, min((S) + 2, last));            \
@@ -509,7 +520,14 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   }
   in.nstage = nkb;
   in.nseg = kSegGU;
-  tile_gemm<true, 2>(in, L, tot);
+  // the slot tiles holding real rows, rounded up to 2, 4 or 8
+  const int live = (tl.mcnt + 15) / 16;
+  if (live <= 2)
+    tile_gemm<true, 2, 2>(in, L, tot);
+  else if (live <= 4)
+    tile_gemm<true, 2, 4>(in, L, tot);
+  else
+    tile_gemm<true, 2, kNB>(in, L, tot);
   // h = silu(G) U in place of G; 1x128 requantization over the tile's 128 columns
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
@@ -556,6 +574,24 @@ constexpr int kDnCols = 32 * kWaves;
 static_assert(kSegDN == 1, "the routed down tiles run one K segment per wave");
 constexpr int kDnColsW = 16 * kWA * kWaves;
 constexpr int kDnLds = kWLds > (int)sizeof(TileLds) ? kWLds : (int)sizeof(TileLds);
+
+// One routed wide tile over its first NL slot tiles: the K loop, then the
+// real slots' D rows (waves past H store nothing).
+template <int NL>
+__device__ __forceinline__ void down_wide_tile(const FfnArgs& a, const WideIn& in, uint8_t* smem, const Tile& tl,
+                                               int n0) {
+  WAcc acc;
+  wide_gemm<NL>(in, smem, acc);
+  if (n0 >= a.H) return;
+  const int c = threadIdx.x & 15, q = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int b = 0; b < NL; ++b) {
+    const int i = 16 * b + c;
+    if (i >= tl.mcnt) continue;
+#pragma unroll
+    for (int t = 0; t < kWA; ++t) store_f4(a.D + (size_t)(tl.s0 + i) * a.H + n0 + 16 * t + 4 * q, acc[t][b]);
+  }
+}
 
 __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   __shared__ __align__(16) uint8_t smem[kDnLds];
@@ -622,16 +658,16 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   in.sbase = a.hs;
   in.soff = (uint32_t)((size_t)(tl.s0 + (in.bsok ? tid : 0)) * nkb);
   in.nkb = nkb;
-  WAcc acc;
-  wide_gemm(in, smem, acc);
-  if (n0 >= a.H) return;
-#pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    const int i = 16 * b + c;
-    if (i >= tl.mcnt) continue;
-#pragma unroll
-    for (int t = 0; t < kWA; ++t) store_f4(a.D + (size_t)(tl.s0 + i) * a.H + n0 + 16 * t + 4 * q, acc[t][b]);
-  }
+  // the slot tiles holding real rows, rounded up to 1, 2, 4 or 8
+  const int live = (tl.mcnt + 15) / 16;
+  if (live <= 1)
+    down_wide_tile<1>(a, in, smem, tl, n0);
+  else if (live <= 2)
+    down_wide_tile<2>(a, in, smem, tl, n0);
+  else if (live <= 4)
+    down_wide_tile<4>(a, in, smem, tl, n0);
+  else
+    down_wide_tile<kNB>(a, in, smem, tl, n0);
 }
 
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s) {
