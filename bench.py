@@ -411,7 +411,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="only the prefill part (profiling)")
     ap.add_argument("--prefill-layers", type=int, default=4, help="stacked layers of the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweeps", action="store_true", help="skip the row-count and TP8-rank sweeps")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the row-count and TP8-rank sweeps and the DP8 and 512-token legs")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -581,50 +582,51 @@ def main():
                              "timing": "hipGraph replay, weights rotated as above"}
 
     # ---------------- the other decode and chunk workloads on the same layer
-    # DP8 step: 8 independent rows, pads at slots 2, 5, 7 (a larger union)
-    dcfg = synth.CONFIGS["dp8"]
-    xd_np, md_np = synth.activations(dcfg)
-    xd = torch.from_numpy(xd_np.view(np.int16)).cuda()
-    mkd = torch.from_numpy(md_np).cuda()
+    if not args.no_sweeps:
+        # DP8 step: 8 independent rows, pads at slots 2, 5, 7 (a larger union)
+        dcfg = synth.CONFIGS["dp8"]
+        xd_np, md_np = synth.activations(dcfg)
+        xd = torch.from_numpy(xd_np.view(np.int16)).cuda()
+        mkd = torch.from_numpy(md_np).cuda()
 
-    def step_dp8(i):
-        r = reps[i % len(reps)]
-        moe.layer(md, xd, mkd, r["router_w"], r["bias"], r["experts"], r["shared"], y, rt, ws)
+        def step_dp8(i):
+            r = reps[i % len(reps)]
+            moe.layer(md, xd, mkd, r["router_w"], r["bias"], r["experts"], r["shared"], y, rt, ws)
 
-    us_dp8 = graph_replay_us(torch, step_dp8, len(reps), args.steps, args.warmup, rt_lib, stream)[0]
-    nu_dp8 = int(rt.n_union.item())
-    rb8, fb8 = decode_bytes(nu_dp8, d, M)
-    result["dp8"] = {"workload": "DP8-style decode step: 8 independent rows (pads at slots 2, 5, 7), same layer",
-                     "us": round(us_dp8, 2), "union_experts": nu_dp8, "bytes": rb8 + fb8,
-                     "gbs": round((rb8 + fb8) / (us_dp8 * 1e-6) / 1e9, 1),
-                     "hbm_frac": round((rb8 + fb8) / (us_dp8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"[bench] dp8: {us_dp8:.1f} us, |U|={nu_dp8}, {(rb8 + fb8) / (us_dp8 * 1e-6) / 1e9:.0f} GB/s")
-    # 512-token chunk with the Zipf-skewed router bias
-    pcfg5 = synth.CONFIGS["prefill512"]
-    xp_np, mp_np = synth.activations(pcfg5)
-    xp5 = torch.from_numpy(xp_np.view(np.int16)).cuda()
-    mp5 = torch.from_numpy(mp_np).cuda()
-    zb = torch.from_numpy(np.ascontiguousarray(synth.router_bias(pcfg5), dtype=np.float32)).cuda()
-    m5 = pcfg5.rows
-    ws5 = moe.workspace(md, m5)
-    y5 = torch.empty((m5, d.hidden), dtype=torch.int16, device="cuda")
-    rt5 = moe.Routing.empty(md, m5)
+        us_dp8 = graph_replay_us(torch, step_dp8, len(reps), args.steps, args.warmup, rt_lib, stream)[0]
+        nu_dp8 = int(rt.n_union.item())
+        rb8, fb8 = decode_bytes(nu_dp8, d, M)
+        result["dp8"] = {"workload": "DP8-style decode step: 8 independent rows (pads at slots 2, 5, 7), same layer",
+                         "us": round(us_dp8, 2), "union_experts": nu_dp8, "bytes": rb8 + fb8,
+                         "gbs": round((rb8 + fb8) / (us_dp8 * 1e-6) / 1e9, 1),
+                         "hbm_frac": round((rb8 + fb8) / (us_dp8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] dp8: {us_dp8:.1f} us, |U|={nu_dp8}, {(rb8 + fb8) / (us_dp8 * 1e-6) / 1e9:.0f} GB/s")
+        # 512-token chunk with the Zipf-skewed router bias
+        pcfg5 = synth.CONFIGS["prefill512"]
+        xp_np, mp_np = synth.activations(pcfg5)
+        xp5 = torch.from_numpy(xp_np.view(np.int16)).cuda()
+        mp5 = torch.from_numpy(mp_np).cuda()
+        zb = torch.from_numpy(np.ascontiguousarray(synth.router_bias(pcfg5), dtype=np.float32)).cuda()
+        m5 = pcfg5.rows
+        ws5 = moe.workspace(md, m5)
+        y5 = torch.empty((m5, d.hidden), dtype=torch.int16, device="cuda")
+        rt5 = moe.Routing.empty(md, m5)
 
-    def step_p512(i):
-        r = reps[i % len(reps)]
-        moe.layer(md, xp5, mp5, r["router_w"], zb, r["experts"], r["shared"], y5, rt5, ws5)
+        def step_p512(i):
+            r = reps[i % len(reps)]
+            moe.layer(md, xp5, mp5, r["router_w"], zb, r["experts"], r["shared"], y5, rt5, ws5)
 
-    us_p5 = graph_replay_us(torch, step_p512, len(reps), min(args.steps, 50), min(args.warmup, 5), rt_lib, stream)[0]
-    nu5 = int(rt5.n_union.item())
-    sl5 = int(rt5.offs[nu5].item())
-    rb5, fb5 = decode_bytes(nu5, d, m5)
-    f8, f16, fr = layer_flops(d, m5, sl5)
-    result["prefill512"] = {"workload": "512-token chunk, Zipf(1.1) router bias, same layer",
-                            "us": round(us_p5, 2), "union_experts": nu5,
-                            "tflops_total": round((f8 + f16 + fr) / (us_p5 * 1e-6) / 1e12, 2),
-                            "hbm_frac": round((rb5 + fb5) / (us_p5 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"[bench] prefill512: {us_p5:.1f} us, |U|={nu5}, {(rb5 + fb5) / (us_p5 * 1e-6) / 1e9:.0f} GB/s")
-    del ws5, y5
+        us_p5 = graph_replay_us(torch, step_p512, len(reps), min(args.steps, 50), min(args.warmup, 5), rt_lib, stream)[0]
+        nu5 = int(rt5.n_union.item())
+        sl5 = int(rt5.offs[nu5].item())
+        rb5, fb5 = decode_bytes(nu5, d, m5)
+        f8, f16, fr = layer_flops(d, m5, sl5)
+        result["prefill512"] = {"workload": "512-token chunk, Zipf(1.1) router bias, same layer",
+                                "us": round(us_p5, 2), "union_experts": nu5,
+                                "tflops_total": round((f8 + f16 + fr) / (us_p5 * 1e-6) / 1e12, 2),
+                                "hbm_frac": round((rb5 + fb5) / (us_p5 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] prefill512: {us_p5:.1f} us, |U|={nu5}, {(rb5 + fb5) / (us_p5 * 1e-6) / 1e9:.0f} GB/s")
+        del ws5, y5
 
     # ---------------- CPU oracle baseline on the same decode step
     if not args.no_cpu_baseline:
