@@ -266,3 +266,36 @@ def test_workspace_reuse_across_sizes(tiny):
     a = run_layer(gl, x, mask, ws_rows=300)
     b = run_layer(gl, x, mask)
     assert np.array_equal(a["y"], b["y"])
+
+
+@pytest.mark.parametrize("m", [16, 17, 25, 32, 33, 48, 64, 65, 66, 128, 129, 200])
+def test_forced_routing_tile_fill(tiny, m):
+    """Every real row picks the same four experts (correction bias +100 on
+    them), so each holds exactly the real-row count of slots: counts of
+    16 k and 16 k + 1 put the last 16-slot group of a 128-slot tile just
+    full or just started (the tiled kernels compute only the groups that
+    hold real rows), 128 and 129 fill one tile and start a second.  Parity
+    against the oracle, and the first 8 rows equal the 8-row split step on
+    those rows bit for bit."""
+    cfg, gl, _, _ = tiny
+    bias = gl.host.bias.astype(np.float32).copy()
+    bias[[1, 6, 11, 14]] += 100.0
+    gf = gl.with_bias(bias)
+    x = _rows(cfg, m, 500 + m)
+    mask = np.ones(m, np.uint8)
+    if m == 66:                               # one pad: 65 slots per expert
+        mask[40] = 0
+        x[40] = 0x7FC0
+    say(f"tiny forced routing M={m}")
+    g = run_layer(gf, x, mask)
+    o = run_oracle(gf, x, mask)
+    assert_routing_equal(g, o.routing, mask)
+    assert list(o.routing.union_ids) == [1, 6, 11, 14]
+    assert np.all(np.diff(o.routing.offs) == int(mask.sum()))
+    real = mask != 0
+    assert np.array_equal(g["x_codes"][real], o.x_codes[real])
+    compare_h_codes(g["h_codes"], g["h_scales"], o, gf)
+    assert_y_close(g["y"], o)
+    assert not g["y"][~real].any()
+    small = run_layer(gf, x[:8], mask[:8])
+    assert np.array_equal(g["y"][:8], small["y"])
