@@ -386,9 +386,11 @@ __global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
     if (a.mask == nullptr || a.mask[r] != 0) logit_row(a, r, blockIdx.x, lane);
 }
 
-// The front of a split small step (M <= kSmallRows), one launch:
-//   blocks [0, E)             logits of expert b, wave w: rows w, w + 8, ...
-//   blocks [E, E + nq)        x quantization, one (row, 128-block) per wave
+// The front of a split small step (M <= kSmallRows), one launch of
+// kFrontWaves-wave workgroups:
+//   blocks [0, E nlg)         logits of expert b % E, wave w: row 8 (b / E) + w
+//                             (nlg = ceil(M / 8) row groups: one round for any M)
+//   blocks [E nlg, E nlg + nq) x quantization, one (row, 128-block) per wave
 //   blocks [E + nq, ...)      shared expert gate/up, one K segment of the
 //                             gate or up rows of one 16-column tile per wave
 //                             (fp32 partials)
@@ -425,21 +427,27 @@ __device__ __forceinline__ void shared_gu_item(const FfnArgs& f, int t, int seg0
   }
 }
 
-// Split steps, first launch: blocks [0, E) logits (one block per expert, wave
-// w serving rows w, w + 8, ...); then the x quantization; then the shared expert's gate/up
-// for the first half of its K segments (the second half runs beside the
-// top-k in k_select_union_small).
+// Split steps, first launch: blocks [0, E nlg) logits (one block per expert
+// and group of kFrontWaves rows, one row per wave); then the x quantization;
+// then the shared expert's gate/up for the first half of its K segments (the
+// second half runs beside the top-k in k_select_union_small).  Workgroups
+// stay at 8 waves so that the logit blocks leave room on their CUs for the
+// streaming shared-expert blocks.
+constexpr int kFrontWaves = 8;
+
 template <int NB>
-__global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
+__global__ __launch_bounds__(64 * kFrontWaves) void k_front(RouteArgs r, FfnArgs f, int nq) {
   const int lane = threadIdx.x & 63, wave = wave_id();
+  const int nlg = (r.M + kFrontWaves - 1) / kFrontWaves;
+  const int nl = r.E * nlg;
   const int b = blockIdx.x;
-  if (b < r.E) {
-    for (int row = wave; row < r.M; row += 8)
-      if (r.mask == nullptr || r.mask[row] != 0) logit_row(r, row, b, lane);
+  if (b < nl) {
+    const int row = (b / r.E) * kFrontWaves + wave;
+    if (row < r.M && (r.mask == nullptr || r.mask[row] != 0)) logit_row(r, row, b % r.E, lane);
     return;
   }
-  if (b < r.E + nq) {
-    const int item = (b - r.E) * 8 + wave;
+  if (b < nl + nq) {
+    const int item = (b - nl) * kFrontWaves + wave;
     const int nb = f.H / kBlk;
     const int row = item / nb, blk = item % nb;
     if (row >= f.M || !row_real(f.mask, row)) return;
@@ -448,18 +456,17 @@ __global__ __launch_bounds__(512) void k_front(RouteArgs r, FfnArgs f, int nq) {
                lane);
     return;
   }
-  const int t = (b - r.E - nq) * 8 + wave;
+  const int t = (b - nl - nq) * kFrontWaves + wave;
   if (f.Is == 0 || t >= (f.Is / 8) * (kSegSG / 2)) return;
   shared_gu_item<NB>(f, t, 0, kSegSG / 2, lane);
 }
 
-// Block 0 (8 waves; wave w serves rows w, w + 8, ...): top-k of every row, then the
-// union and the row lists in LDS.  With do_sh, blocks >= 1 run the shared
-// expert's gate/up for the second half of its K segments.
-constexpr int kSelWaves = 8;
-
-template <int NB>
-__global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs a, FfnArgs f, int do_sh) {
+// Block 0 (SW waves; wave w serves rows w, w + SW, ...): top-k of every row,
+// then the union and the row lists in LDS.  With do_sh, blocks >= 1 run the
+// shared expert's gate/up for the second half of its K segments.  Steps of
+// up to 8 rows use 8-wave workgroups, larger ones 16 (fewer rounds of rows).
+template <int NB, int SW>
+__global__ __launch_bounds__(64 * SW) void k_select_union_small(RouteArgs a, FfnArgs f, int do_sh) {
   __shared__ double ssig[kDecodeMaxRows][kMaxTopK];
   __shared__ int sid[kDecodeMaxRows][kMaxTopK];
   __shared__ uint32_t sbits[kDecodeMaxRows][8];
@@ -468,14 +475,14 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs
   const int wave = wave_id();
   if (blockIdx.x > 0) {
     if (!do_sh) return;
-    const int t = (blockIdx.x - 1) * kSelWaves + wave;
+    const int t = (blockIdx.x - 1) * SW + wave;
     if (t >= (f.Is / 8) * (kSegSG - kSegSG / 2)) return;
     shared_gu_item<NB>(f, t, kSegSG / 2, kSegSG - kSegSG / 2, lane);
     return;
   }
   const int nwords = (a.E + 31) / 32;
   // Phase A (row r): top-k, ids in ascending order, row bitmaps.
-  for (int r = wave; r < a.M; r += kSelWaves) {
+  for (int r = wave; r < a.M; r += SW) {
     const bool real = a.mask == nullptr || a.mask[r] != 0;
     if (real) {
       double c[4], sg[4];
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs
   // Phase B (last wave; lane l owns experts 4 l .. 4 l + 3): per-expert row
   // counts, then one exclusive scan of a packed word gives each expert's
   // first slot (bits 0-12), union index (bits 13-21) and first tile (22-31).
-  if (wave == kSelWaves - 1) {
+  if (wave == SW - 1) {
     uint32_t cnt[4], pk[4], run = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -572,7 +579,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_union_small(RouteArgs
   // Phase C (row r, lane j = pick j): combine weight and slot.  An expert's
   // slots list its rows ascending, so row r's slot is the expert's first slot
   // plus the number of earlier rows that picked it.
-  for (int r = wave; r < a.M; r += kSelWaves) {
+  for (int r = wave; r < a.M; r += SW) {
     const bool real = a.mask == nullptr || a.mask[r] != 0;
     if (!real || lane >= a.K) continue;
     double tot = 0.0;
@@ -597,7 +604,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     FfnArgs none;
     memset(&none, 0, sizeof(none));
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * std::min(a.M, 16)), 0, s, a);
-    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small<1>, dim3(1), dim3(64 * kSelWaves), 0, s, a, none, 0);
+    if (a.M <= 8) {
+      MOE_LAUNCH(KID_ROUTE_SMALL, (k_select_union_small<1, 8>), dim3(1), dim3(64 * 8), 0, s, a, none, 0);
+    } else {
+      MOE_LAUNCH(KID_ROUTE_SMALL, (k_select_union_small<1, 16>), dim3(1), dim3(64 * 16), 0, s, a, none, 0);
+    }
     return hipSuccess;
   }
   {
@@ -614,17 +625,22 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_front_split(const RouteArgs& r, const FfnArgs& f, hipStream_t s) {
-  const int nq = (f.M * (f.H / kBlk) + 7) / 8;
+  const int nq = (f.M * (f.H / kBlk) + kFrontWaves - 1) / kFrontWaves;
+  const int nlg = (f.M + kFrontWaves - 1) / kFrontWaves;
   const int items1 = f.Is > 0 ? (f.Is / 8) * (kSegSG / 2) : 0;
   const int items2 = f.Is > 0 ? (f.Is / 8) * (kSegSG - kSegSG / 2) : 0;
-  const dim3 fg((unsigned)(r.E + nq + (items1 + 7) / 8)), sg((unsigned)(1 + (items2 + kSelWaves - 1) / kSelWaves));
+  const dim3 fg((unsigned)(r.E * nlg + nq + (items1 + kFrontWaves - 1) / kFrontWaves));
+  const dim3 sg8((unsigned)(1 + (items2 + 7) / 8)), sg16((unsigned)(1 + (items2 + 15) / 16));
   const int do_sh = f.Is > 0 ? 1 : 0;
-  if (row_halves(f.M) == 1) {
-    MOE_LAUNCH(KID_FRONT, k_front<1>, fg, dim3(512), 0, s, r, f, nq);
-    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small<1>, sg, dim3(64 * kSelWaves), 0, s, r, f, do_sh);
+  if (f.M <= 8) {
+    MOE_LAUNCH(KID_FRONT, k_front<1>, fg, dim3(64 * kFrontWaves), 0, s, r, f, nq);
+    MOE_LAUNCH(KID_ROUTE_SMALL, (k_select_union_small<1, 8>), sg8, dim3(64 * 8), 0, s, r, f, do_sh);
+  } else if (row_halves(f.M) == 1) {
+    MOE_LAUNCH(KID_FRONT, k_front<1>, fg, dim3(64 * kFrontWaves), 0, s, r, f, nq);
+    MOE_LAUNCH(KID_ROUTE_SMALL, (k_select_union_small<1, 16>), sg16, dim3(64 * 16), 0, s, r, f, do_sh);
   } else {
-    MOE_LAUNCH(KID_FRONT, k_front<2>, fg, dim3(512), 0, s, r, f, nq);
-    MOE_LAUNCH(KID_ROUTE_SMALL, k_select_union_small<2>, sg, dim3(64 * kSelWaves), 0, s, r, f, do_sh);
+    MOE_LAUNCH(KID_FRONT, k_front<2>, fg, dim3(64 * kFrontWaves), 0, s, r, f, nq);
+    MOE_LAUNCH(KID_ROUTE_SMALL, (k_select_union_small<2, 16>), sg16, dim3(64 * 16), 0, s, r, f, do_sh);
   }
   return hipSuccess;
 }
