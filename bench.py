@@ -275,7 +275,7 @@ def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
     plus drafts, the same recipe at every count): the small-step path serves
     up to moe.SMALL_ROWS rows, the tiled path above."""
     out = []
-    for m in (1, 2, 4, 8, 9, 12, 16, 17, 24, 32, 33, 48, 64):
+    for m in (1, 2, 4, 8, 9, 12, 16, 17, 24, 32, 33, 48, 64, 128, 256):
         cfg = synth.with_rows(synth.CONFIGS["span8"], m)
         x_np, mask_np = synth.activations(cfg)
         x = torch.from_numpy(x_np.view(np.int16)).cuda()

@@ -344,8 +344,8 @@ __device__ __forceinline__ double dot_chunk(const uint4& xv, const uint4& wv, do
   return acc;
 }
 
-// logit of (row r, expert e) for the calling wave; stores sigmoid and score
-__device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int lane) {
+// logit l of (row r, expert e) for the calling wave (every lane gets it)
+__device__ __forceinline__ double logit_dot(const RouteArgs& a, int r, int e, int lane) {
   const uint16_t* wrow = a.wr + (size_t)e * a.H + 8 * lane;
   const uint16_t* xrow = a.x + (size_t)r * a.H + 8 * lane;
   const int nch = (a.H + 511) / 512;
@@ -370,7 +370,13 @@ __device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int 
       }
     }
   }
-  const double l = wave_sum_f64(acc);
+  return wave_sum_f64(acc);
+}
+
+// logit of (row r, expert e) for the calling wave; stores the biased score c
+// in logits and sigmoid(l) in sig (the form the small-step selection reads)
+__device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int lane) {
+  const double l = logit_dot(a, r, e, lane);
   if (lane == 0) {
     double sig, c;
     route_score(l, a.bias[e], sig, c);
@@ -379,11 +385,28 @@ __device__ __forceinline__ void logit_row(const RouteArgs& a, int r, int e, int 
   }
 }
 
-__global__ __launch_bounds__(1024) void k_logits_small(RouteArgs a) {
+// Logits of steps up to kGroupedLogitRows rows: one 8-wave block per
+// (expert b % E, group of 8 rows b / E), one logit per wave, so a step of a
+// few dozen rows still spreads over thousands of waves; the router row is
+// re-read by each row group from L2.  Its time grows with the rows (≈ 20 µs
+// at 64 rows, 83 µs at 256 for 256 experts, hidden 6144) while
+// k_router_logits stays near 43 µs up to 256 rows: they meet near 128.  kRaw: store the raw logit l, as
+// k_router_logits does, for k_route_select; else the score c and sigmoid(l)
+// for k_select_union_small.
+constexpr int kGroupedLogitRows = 128;
+
+template <bool kRaw>
+__global__ __launch_bounds__(512) void k_logits_grouped(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
-  for (int r = wave_id(); r < a.M; r += nw)      // one wave per row (and row + nw, ...)
-    if (a.mask == nullptr || a.mask[r] != 0) logit_row(a, r, blockIdx.x, lane);
+  const int e = blockIdx.x % a.E;
+  const int r = (blockIdx.x / a.E) * 8 + wave_id();
+  if (r >= a.M || (a.mask != nullptr && a.mask[r] == 0)) return;
+  if (kRaw) {
+    const double l = logit_dot(a, r, e, lane);
+    if (lane == 0) a.logits[(size_t)r * a.E + e] = l;
+  } else {
+    logit_row(a, r, e, lane);
+  }
 }
 
 // The front of a split small step (M <= kSmallRows), one launch of
@@ -603,7 +626,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.M <= kDecodeMaxRows) {
     FfnArgs none;
     memset(&none, 0, sizeof(none));
-    MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_small, dim3(a.E), dim3(64 * std::min(a.M, 16)), 0, s, a);
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_grouped<false>, dim3((unsigned)(a.E * ((a.M + 7) / 8))), dim3(512), 0, s, a);
     if (a.M <= 8) {
       MOE_LAUNCH(KID_ROUTE_SMALL, (k_select_union_small<1, 8>), dim3(1), dim3(64 * 8), 0, s, a, none, 0);
     } else {
@@ -611,7 +634,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     }
     return hipSuccess;
   }
-  {
+  if (a.M <= kGroupedLogitRows) {
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_grouped<true>, dim3((unsigned)(a.E * ((a.M + 7) / 8))), dim3(512), 0, s, a);
+  } else {
     const long groups8 = ((a.M + 7) / 8 + 7) / 8 * 8;     // row groups, padded to a multiple of 8
     constexpr int kEpw = 8;                                 // experts per wave (32 per workgroup)
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<kEpw>, dim3((unsigned)(groups8 * ((a.E + 4 * kEpw - 1) / (4 * kEpw)))),
