@@ -8,7 +8,7 @@
 namespace moe {
 
 constexpr int kMTile = 128;          // slots (or rows) per tile of the tiled grouped GEMMs
-constexpr int kDecodeMaxRows = 32;  // rows served by the small-step router kernels
+constexpr int kDecodeMaxRows = 32;  // LDS capacity (rows) of the small-step selection kernel
 constexpr int kSmallRows = 24;      // rows served by the split small-step expert kernels (measured crossover)
 // The split kernels' work items take the step's rows (or an expert's slots)
 // as the 16 MFMA columns, in row halves of kColRows: rows 16 h .. 16 h + 15.
