@@ -299,3 +299,27 @@ def test_forced_routing_tile_fill(tiny, m):
     assert not g["y"][~real].any()
     small = run_layer(gf, x[:8], mask[:8])
     assert np.array_equal(g["y"][:8], small["y"])
+
+
+def test_logit_kernels_give_identical_routing(tiny):
+    """The same 100 rows as a 100-row step (float64 logits one wave per logit)
+    and as the first rows of a 200-row step (8-row x 8-expert logit waves):
+    the logits take one lane order and butterfly in both, so the ids, the
+    float32 combine weights and the y rows are equal bit for bit."""
+    cfg, gl, _, _ = tiny
+    x = _rows(cfg, 100, 901)
+    mask = np.ones(100, np.uint8)
+    mask[37] = 0
+    x[37] = 0x7FC0
+    say("tiny logit kernels: 100 vs 200 rows")
+    a = run_layer(gl, x, mask)
+    big = _rows(cfg, 200, 902)
+    big[:100] = x
+    bmask = np.ones(200, np.uint8)
+    bmask[:100] = mask
+    b = run_layer(gl, big, bmask)
+    assert np.array_equal(a["ids"], b["ids"][:100])
+    assert np.array_equal(a["w"].view(np.uint32), b["w"][:100].view(np.uint32))
+    assert np.array_equal(a["y"], b["y"][:100])
+    o = run_oracle(gl, x, mask)
+    assert_routing_equal(a, o.routing, mask)
