@@ -169,9 +169,9 @@ __device__ __forceinline__ void lds_frag_pair(const uint8_t* lb, const float* ls
   }
 }
 
-// One K stage on LDS buffer `buf` with A fragments `a`.  fp8: only slot
-// tiles 0 .. NL - 1 are computed; the caller picks NL >= the tile's slot
-// tiles holding real rows (the rest hold zero codes and are never stored).
+// One K stage on LDS buffer `buf` with A fragments `a`.  Only slot tiles
+// 0 .. NL - 1 are computed; the caller picks NL >= the tile's slot tiles
+// holding rows (the rest hold zeros and are never stored).
 template <bool kFp8, int NL>
 __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const AStage& as, int st, Acc& acc, Acc& tot,
                                            SegState& g) {
@@ -211,9 +211,9 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
       // the next slot tile's fragment is read while this tile's MFMAs run
       uint4 xv = ld16(&L.b[buf][c * kLdsRow + j * 64 + q * 16]);
 #pragma unroll
-      for (int b = 0; b < kNB; ++b) {
+      for (int b = 0; b < NL; ++b) {
         uint4 xnv = xv;
-        if (b + 1 < kNB) xnv = ld16(&L.b[buf][(16 * (b + 1) + c) * kLdsRow + j * 64 + q * 16]);
+        if (b + 1 < NL) xnv = ld16(&L.b[buf][(16 * (b + 1) + c) * kLdsRow + j * 64 + q * 16]);
         const v4i xb = {(int)xv.x, (int)xv.y, (int)xv.z, (int)xv.w};
 #pragma unroll
         for (int t = 0; t < kNA; ++t) {
@@ -236,7 +236,10 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
 template <bool kFp8, int kRingA, int NL = kNB>
 __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
   static_assert(kRingA == 2 || kRingA == 3, "weight ring of 2 or 3 stages");
-  static_assert(NL % 2 == 0 && NL >= 2 && NL <= kNB && (kFp8 || NL == kNB), "slot tiles in pairs");
+  static_assert(NL % 2 == 0 && NL >= 2 && NL <= kNB, "slot tiles in pairs");
+  // keeps the first loads below the caller's branch between instantiations
+  // (hoisted above it they stretch live ranges across all of them)
+  asm volatile("" ::: "memory");
   Acc acc;
 #pragma unroll
   for (int t = 0; t < kNA; ++t)
@@ -455,6 +458,40 @@ __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc&
 }
 
 // ---------------------------------------------------------------- gate/up
+// One shared-expert gate/up tile (row tile mt, 128-column tile nt) over its
+// first NL 16-row groups: h_s = silu(G) U, rounded to bf16, for the real
+// rows.  Wave w holds the gate (A tile 0) and up (A tile 1) rows of h
+// columns n0 + 16 w .. + 15.
+template <int NL>
+__device__ __forceinline__ void shared_gateup_tile(const FfnArgs& a, TileLds& L, int mt, int nt) {
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int n0 = nt * kBlk + 16 * w;                 // wave's first h column
+  TileIn in;
+  in.a[0] = tile_row(a.wsg, (size_t)n0 + c, a.H * 2 / kBlk, q);
+  in.a[1] = tile_row(a.wsu, (size_t)n0 + c, a.H * 2 / kBlk, q);
+  in.sw[0] = in.sw[1] = nullptr;
+#pragma unroll
+  for (int i = 0; i < kBVec; ++i) {
+    const int brow = mt * kTM + tid / 8 + kBRowStep * i;
+    in.bok[i] = brow < a.M && row_real(a.mask, brow);
+    in.b[i] = reinterpret_cast<const uint8_t*>(a.x + (size_t)(in.bok[i] ? brow : 0) * a.H) + (tid % 8) * 16;
+  }
+  in.bs = nullptr;
+  in.bsok = false;
+  in.nstage = a.H * 2 / kStageBytes;
+  in.nseg = kSegSG;
+  Acc tot;
+  tile_gemm<false, 3, NL>(in, L, tot);
+#pragma unroll
+  for (int b = 0; b < NL; ++b) {
+    const int row = mt * kTM + 16 * b + c;
+    if (row >= a.M || !row_real(a.mask, row)) continue;
+    const v4f h = {silu_mul(tot[0][b][0], tot[1][b][0]), silu_mul(tot[0][b][1], tot[1][b][1]),
+                   silu_mul(tot[0][b][2], tot[1][b][2]), silu_mul(tot[0][b][3], tot[1][b][3])};
+    store_bf16x4(a.hsh + (size_t)row * a.Is + n0 + 4 * q, h);
+  }
+}
+
 // Blocks [0, n_sh): shared-expert tiles (row tile, 128-column tile); then
 // routed tiles (slot tile of one expert, 128-column tile).  Wave w holds the
 // gate (A tile 0) and up (A tile 1) rows of h columns n0 + 16 w .. + 15.
@@ -470,30 +507,14 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   Acc tot;
   if (bid < n_sh) {
     const int mt = bid / ntS, nt = bid % ntS;
-    const int n0 = nt * kBlk + 16 * w;                 // wave's first h column
-    TileIn in;
-    in.a[0] = tile_row(a.wsg, (size_t)n0 + c, a.H * 2 / kBlk, q);
-    in.a[1] = tile_row(a.wsu, (size_t)n0 + c, a.H * 2 / kBlk, q);
-    in.sw[0] = in.sw[1] = nullptr;
-#pragma unroll
-    for (int i = 0; i < kBVec; ++i) {
-      const int brow = mt * kTM + tid / 8 + kBRowStep * i;
-      in.bok[i] = brow < a.M && row_real(a.mask, brow);
-      in.b[i] = reinterpret_cast<const uint8_t*>(a.x + (size_t)(in.bok[i] ? brow : 0) * a.H) + (tid % 8) * 16;
-    }
-    in.bs = nullptr;
-    in.bsok = false;
-    in.nstage = a.H * 2 / kStageBytes;
-    in.nseg = kSegSG;
-    tile_gemm<false, 3>(in, L, tot);
-#pragma unroll
-    for (int b = 0; b < kNB; ++b) {
-      const int row = mt * kTM + 16 * b + c;
-      if (row >= a.M || !row_real(a.mask, row)) continue;
-      const v4f h = {silu_mul(tot[0][b][0], tot[1][b][0]), silu_mul(tot[0][b][1], tot[1][b][1]),
-                     silu_mul(tot[0][b][2], tot[1][b][2]), silu_mul(tot[0][b][3], tot[1][b][3])};
-      store_bf16x4(a.hsh + (size_t)row * a.Is + n0 + 4 * q, h);
-    }
+    // the row tile's 16-row groups holding rows, rounded up to 2, 4 or 8
+    const int live = (min(kTM, a.M - mt * kTM) + 15) / 16;
+    if (live <= 2)
+      shared_gateup_tile<2>(a, L, mt, nt);
+    else if (live <= 4)
+      shared_gateup_tile<4>(a, L, mt, nt);
+    else
+      shared_gateup_tile<kNB>(a, L, mt, nt);
     return;
   }
   const int rb = bid - n_sh;
@@ -575,6 +596,43 @@ static_assert(kSegDN == 1, "the routed down tiles run one K segment per wave");
 constexpr int kDnColsW = 16 * kWA * kWaves;
 constexpr int kDnLds = kWLds > (int)sizeof(TileLds) ? kWLds : (int)sizeof(TileLds);
 
+// One shared-expert down tile (row tile mt, kDnCols-column tile nt) over its
+// first NL 16-row groups: S = h_s Wsd^T in fp32 for the real rows.  Wave w
+// holds output columns n0 + 32 w .. + 31 (A tiles 0 and 1); waves past H
+// compute on in-range rows and store nothing.
+template <int NL>
+__device__ __forceinline__ void shared_down_tile(const FfnArgs& a, TileLds& L, int mt, int nt) {
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int n0 = nt * kDnCols + 32 * w;
+  TileIn in;
+  const int nr = n0 < a.H ? n0 : a.H - 32;
+#pragma unroll
+  for (int t = 0; t < kNA; ++t) {
+    in.a[t] = tile_row(a.wsd, (size_t)nr + 16 * t + c, a.Is * 2 / kBlk, q);
+    in.sw[t] = nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < kBVec; ++i) {
+    const int brow = mt * kTM + tid / 8 + kBRowStep * i;
+    in.bok[i] = brow < a.M && row_real(a.mask, brow);
+    in.b[i] = reinterpret_cast<const uint8_t*>(a.hsh + (size_t)(in.bok[i] ? brow : 0) * a.Is) + (tid % 8) * 16;
+  }
+  in.bs = nullptr;
+  in.bsok = false;
+  in.nstage = a.Is * 2 / kStageBytes;
+  in.nseg = kSegSD;
+  Acc tot;
+  tile_gemm<false, 2, NL>(in, L, tot);
+  if (n0 >= a.H) return;
+#pragma unroll
+  for (int b = 0; b < NL; ++b) {
+    const int row = mt * kTM + 16 * b + c;
+    if (row >= a.M || !row_real(a.mask, row)) continue;
+#pragma unroll
+    for (int t = 0; t < kNA; ++t) store_f4(a.S + (size_t)row * a.H + n0 + 16 * t + 4 * q, tot[t][b]);
+  }
+}
+
 // One routed wide tile over its first NL slot tiles: the K loop, then the
 // real slots' D rows (waves past H store nothing).
 template <int NL>
@@ -606,34 +664,14 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   Acc tot;
   if (bid < n_sh) {
     const int mt = bid / ntH, nt = bid % ntH;
-    const int n0 = nt * kDnCols + 32 * w;
-    TileIn in;
-    // waves past H compute on in-range rows and store nothing
-    const int nr = n0 < a.H ? n0 : a.H - 32;
-#pragma unroll
-    for (int t = 0; t < kNA; ++t) {
-      in.a[t] = tile_row(a.wsd, (size_t)nr + 16 * t + c, a.Is * 2 / kBlk, q);
-      in.sw[t] = nullptr;
-    }
-#pragma unroll
-    for (int i = 0; i < kBVec; ++i) {
-      const int brow = mt * kTM + tid / 8 + kBRowStep * i;
-      in.bok[i] = brow < a.M && row_real(a.mask, brow);
-      in.b[i] = reinterpret_cast<const uint8_t*>(a.hsh + (size_t)(in.bok[i] ? brow : 0) * a.Is) + (tid % 8) * 16;
-    }
-    in.bs = nullptr;
-    in.bsok = false;
-    in.nstage = a.Is * 2 / kStageBytes;
-    in.nseg = kSegSD;
-    tile_gemm<false, 2>(in, L, tot);
-    if (n0 >= a.H) return;
-#pragma unroll
-    for (int b = 0; b < kNB; ++b) {
-      const int row = mt * kTM + 16 * b + c;
-      if (row >= a.M || !row_real(a.mask, row)) continue;
-#pragma unroll
-      for (int t = 0; t < kNA; ++t) store_f4(a.S + (size_t)row * a.H + n0 + 16 * t + 4 * q, tot[t][b]);
-    }
+    // the row tile's 16-row groups holding rows, rounded up to 2, 4 or 8
+    const int live = (min(kTM, a.M - mt * kTM) + 15) / 16;
+    if (live <= 2)
+      shared_down_tile<2>(a, L, mt, nt);
+    else if (live <= 4)
+      shared_down_tile<4>(a, L, mt, nt);
+    else
+      shared_down_tile<kNB>(a, L, mt, nt);
     return;
   }
   const int rb = bid - n_sh;
