@@ -273,7 +273,7 @@ def graph_chain_us(torch, step, n_calls, steps, warmup, rt_lib, stream):
 def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
     """Layer time against the row count on the span-8 layer (one committed row
     plus drafts, the same recipe at every count): the small-step path serves
-    up to moe.SMALL_ROWS rows, the tiled path above."""
+    up to moe.split_rows(inter) rows, the tiled path above."""
     out = []
     for m in (1, 2, 4, 8, 9, 12, 16, 17, 24, 32, 33, 48, 64, 128, 256):
         cfg = synth.with_rows(synth.CONFIGS["span8"], m)
@@ -291,7 +291,7 @@ def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
         us, p10, p50, p90 = graph_replay_us(torch, step, len(reps), steps, warmup, rt_lib, stream)
         nu = int(rt.n_union.item())
         rb, fb = decode_bytes(nu, d, m)
-        out.append({"rows": m, "path": "split" if m <= moe.SMALL_ROWS else "tiled", "union_experts": nu,
+        out.append({"rows": m, "path": "split" if m <= moe.split_rows(d.inter) else "tiled", "union_experts": nu,
                     "us": round(us, 2),
                     "us_p10": round(p10, 2), "us_p90": round(p90, 2),
                     "gbs": round((rb + fb) / (us * 1e-6) / 1e9, 1)})

@@ -179,8 +179,9 @@ int moe_add_rmsnorm(int32_t M, int32_t H, const uint16_t* y, const uint8_t* row_
                     const uint16_t* gamma, float eps, uint16_t* residual_out, uint16_t* out, void* stream);
 
 /* moe_layer with the combine running the residual add + RMSNorm above in the
- * same pass (one launch instead of two, y never re-read), except for steps of
- * at most 24 rows, where the element-wise combine and the row epilogue run
+ * same pass (one launch instead of two, y never re-read), except for the
+ * small steps (at most 16 rows, or 24 when dims->inter <= 512), where the
+ * element-wise combine and the row epilogue run
  * as two launches (more workgroups; the same bits).  y (the layer output,
  * bf16 [M, H]) is also stored unless y is NULL; residual_out and out as in
  * moe_add_rmsnorm with H = dims->hidden. */

@@ -19,7 +19,14 @@ LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = range(5)
 MAX_ROWS, MAX_EXPERTS, MAX_TOPK, MAX_INTER = 16384, 256, 16, 8192
-SMALL_ROWS = 24      # steps of up to this many rows take the split small-step kernels
+SMALL_ROWS = 24      # steps of up to this many rows take the split small-step kernels (inter <= 512)
+SMALL_ROWS_WIDE = 16 # the same for wider experts (inter > 512)
+NARROW_INTER = 512
+
+
+def split_rows(inter: int) -> int:
+    """Most rows of a step that takes the split small-step kernels."""
+    return SMALL_ROWS if inter <= NARROW_INTER else SMALL_ROWS_WIDE
 
 
 class MoeError(RuntimeError):

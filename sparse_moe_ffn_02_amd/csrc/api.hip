@@ -43,7 +43,7 @@ Layout make_layout(const moe_dims& d, int M) {
   L.hsh = take(m * Is * sizeof(uint16_t));
   L.S = take(m * H * sizeof(float));
   L.D = take(m * K * H * sizeof(float));
-  L.split = use_split(M, d.hidden);
+  L.split = use_split(M, d.hidden, d.inter);
   const size_t sp = L.split ? 1 : 0;
   L.part_gu = take(sp * kSegGU * m * K * 2 * I * sizeof(float));
   L.part_sh = take(sp * kSegSG * m * 2 * Is * sizeof(float));
@@ -235,7 +235,8 @@ size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_rows) {
   // small steps keep per-segment partials, so the largest layout for M <=
   // max_rows is either at max_rows or at the largest split row count
   size_t need = make_layout(*dims, max_rows).total;
-  const int split_m = max_rows < kSmallRows ? max_rows : kSmallRows;
+  const int cap = split_rows(dims->inter);
+  const int split_m = max_rows < cap ? max_rows : cap;
   need = std::max(need, make_layout(*dims, split_m).total);
   return need;
 }

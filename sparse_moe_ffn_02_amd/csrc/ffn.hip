@@ -597,7 +597,7 @@ hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8
   return hipSuccess;
 }
 
-bool use_split(int M, int H) { return M <= kSmallRows && H > 0; }
+bool use_split(int M, int H, int I) { return M <= split_rows(I) && H > 0; }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s, const NormArgs* nm) {
   const int with_shared = a.Is > 0 ? 1 : 0;

@@ -9,7 +9,13 @@ namespace moe {
 
 constexpr int kMTile = 128;          // slots (or rows) per tile of the tiled grouped GEMMs
 constexpr int kDecodeMaxRows = 32;  // LDS capacity (rows) of the small-step selection kernel
-constexpr int kSmallRows = 24;      // rows served by the split small-step expert kernels (measured crossover)
+constexpr int kSmallRows = 24;      // most rows of a split small step (experts of inter <= kNarrowInter)
+constexpr int kSmallRowsWide = 16;  // most rows of a split small step for wider experts
+constexpr int kNarrowInter = 512;
+// Rows up to which the split small-step kernels beat the tiled ones (measured
+// crossover): wide experts (inter 2048) reach the tiled kernels' speed from
+// 17 rows, narrow ones (a TP8 shard's inter 256) keep the split path to 24.
+inline int split_rows(int inter) { return inter <= kNarrowInter ? kSmallRows : kSmallRowsWide; }
 // The split kernels' work items take the step's rows (or an expert's slots)
 // as the 16 MFMA columns, in row halves of kColRows: rows 16 h .. 16 h + 15.
 constexpr int kColRows = 16;
@@ -124,7 +130,7 @@ hipError_t launch_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int M, int
                               hipStream_t s);
 // steps that do not take the split path: tiled gate/up (+ SiLU, requant) and down
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s);
-bool use_split(int M, int H);   // M <= kSmallRows
+bool use_split(int M, int H, int I);   // M <= split_rows(I)
 hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int is_bf16, hipStream_t s);
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);
