@@ -69,7 +69,9 @@ class HipEvents:
 
 # ----------------------------------------------------------------------------- device layers
 def device_layer(cfg, layer, torch, moe, replicas=1):
-    """Stream a seeded layer to the GPU expert by expert; `replicas` copies."""
+    """Stream a seeded layer to the GPU expert by expert; `replicas` copies.
+    Every replica holds its own copy of every weight (routed, shared, router),
+    so a call on one replica never finds another's weights in a cache."""
     import synth
     d = cfg.dims
     E, I, H = d.n_experts, d.inter, d.hidden
@@ -103,14 +105,18 @@ def device_layer(cfg, layer, torch, moe, replicas=1):
             r[k].copy_(r0[k])
     sh = synth.shared_expert(cfg, layer)
     t16 = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)
-    shared = moe.pack_shared(moe.Shared(t16(sh["gate"]), t16(sh["up"]), t16(sh["down"])))
+    shared0 = moe.pack_shared(moe.Shared(t16(sh["gate"]), t16(sh["up"]), t16(sh["down"])))
+    router0 = t16(synth.router_weight(cfg, layer))
+    bias0 = torch.from_numpy(synth.router_bias(cfg, layer)).to(dev)
     out = []
-    for r in reps:
+    for i, r in enumerate(reps):
+        shared = shared0 if i == 0 else moe.Shared(shared0.w_gate.clone(), shared0.w_up.clone(),
+                                                   shared0.w_down.clone(), moe.WEIGHTS_PACKED)
         out.append(dict(
-            experts=moe.Experts(r["wg"], r["wu"], r["wd"], r["sg"], r["su"], r["sd"]),
+            experts=moe.Experts(r["wg"], r["wu"], r["wd"], r["sg"], r["su"], r["sd"], moe.WEIGHTS_PACKED),
             shared=shared,
-            router_w=t16(synth.router_weight(cfg, layer)),
-            bias=torch.from_numpy(synth.router_bias(cfg, layer)).to(dev)))
+            router_w=router0 if i == 0 else router0.clone(),
+            bias=bias0 if i == 0 else bias0.clone()))
     torch.cuda.synchronize()
     return out
 
@@ -242,8 +248,9 @@ def graph_replay_us(torch, step, n_graphs, steps, warmup, rt_lib, stream):
 def graph_chain_us(torch, step, n_calls, steps, warmup, rt_lib, stream):
     """One graph holding n_calls consecutive steps (step(0) .. step(n_calls - 1),
     the weight replicas in rotation), as a decode graph over consecutive
-    layers holds them, replayed back to back.  Returns the mean us per step over at least
-    `steps` steps."""
+    layers holds them, replayed back to back.  Returns the mean us per step
+    over at least `steps` steps, and the p10/p50/p90 over single replays
+    (each bracketed by its own events) of the us per step inside one replay."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -257,17 +264,46 @@ def graph_chain_us(torch, step, n_calls, steps, warmup, rt_lib, stream):
     for _ in range(max(1, warmup // n_calls)):
         g.replay()
     torch.cuda.synchronize()
-    reps = (steps + n_calls - 1) // n_calls
-    ev = HipEvents(2)
+    reps = max(10, (steps + n_calls - 1) // n_calls)
+    ev = HipEvents(2 + 2 * reps)
     rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
     for _ in range(reps):
         g.replay()
     rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
     torch.cuda.synchronize()
     us = 1e3 * ev.elapsed_ms(ev.ev[0], ev.ev[1]) / (reps * n_calls)
+    for i in range(reps):
+        rt_lib.hipEventRecord(ev.ev[2 + 2 * i], C.c_void_p(stream))
+        g.replay()
+        rt_lib.hipEventRecord(ev.ev[3 + 2 * i], C.c_void_p(stream))
+    torch.cuda.synchronize()
+    each = np.array([1e3 * ev.elapsed_ms(ev.ev[2 + 2 * i], ev.ev[3 + 2 * i]) / n_calls for i in range(reps)])
     ev.close()
     del g
-    return us
+    p10, p50, p90 = (float(np.percentile(each, q)) for q in (10, 50, 90))
+    return us, p10, p50, p90
+
+
+def copy_gbs(torch, rt_lib, stream, mib=1024, reps=10):
+    """Plain device-to-device copy bandwidth (bytes read + bytes written per
+    second) of a MIB MiB buffer: the practical streaming ceiling measured on
+    the same GPU in the same run, beside the datasheet peak."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+    for _ in range(reps):
+        dst.copy_(src)
+    rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / reps
+    ev.close()
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n / (ms * 1e-3) / 1e9
 
 
 def rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, steps, warmup):
@@ -337,8 +373,52 @@ def tp8_rank_sweep(torch, moe, synth, rt_lib, stream, steps, warmup, replicas):
             "points": out}
 
 
-def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
-    """4096-token prefill chunk over `args.prefill_layers` stacked layers."""
+def gateup_tiled_bytes(nu, slots, d, m):
+    """Algorithmic HBM bytes of the tiled gate/up kernel (one launch): the
+    union experts' gate and up codes and block scales, the x codes and scales,
+    the shared expert's gate/up weights and its bf16 x rows, and the outputs
+    (h codes and scales of every slot, the shared expert's bf16 h)."""
+    H, I, Is = d.hidden, d.inter, d.shared_inter
+    weights = nu * (2 * I * H + 4 * 2 * (I // 128) * (H // 128)) + 2 * Is * H * 2
+    acts_in = m * H + m * (H // 128) * 4 + (m * H * 2 if Is else 0)
+    acts_out = slots * I + slots * (I // 128) * 4 + m * Is * 2
+    return weights + acts_in + acts_out
+
+
+def gateup_tiled_flops(slots, d, m):
+    """fp8 and bf16 MFMA flops of the tiled gate/up kernel."""
+    H, I, Is = d.hidden, d.inter, d.shared_inter
+    return 2.0 * slots * 2 * I * H, 2.0 * m * 2 * Is * H
+
+
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill4096_hbm_counters.md")
+PREFILL_MFMA = os.path.join(ROOT, "profiles", "prefill4096_mfma_counters.md")
+
+
+def traced_kernel_us(lib, torch, fn, calls, per_call=16):
+    """Mean us per launch of each library kernel over `calls` calls of fn,
+    from HIP events the library records around each launch on its stream."""
+    tev = HipEvents(2 * per_call * calls)
+    pairs = (C.c_void_p * (2 * per_call * calls))(*[h.value for h in tev.ev])
+    kid = (C.c_int32 * (per_call * calls))()
+    cnt = C.c_int32(0)
+    assert lib.moe_trace_set(pairs, per_call * calls, kid, C.byref(cnt)) == 0
+    for i in range(calls):
+        fn(i)
+    torch.cuda.synchronize()
+    lib.moe_trace_set(None, 0, None, None)
+    per = {}
+    for i in range(cnt.value):
+        name = lib.moe_kernel_name(kid[i]).decode()
+        per.setdefault(name, []).append(tev.elapsed_ms(tev.ev[2 * i], tev.ev[2 * i + 1]))
+    tev.close()
+    return {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
+
+
+def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream, lib):
+    """4096-token prefill chunk through `args.prefill_layers` stacked layers:
+    layer l + 1 takes layer l's output rescaled per row to unit RMS (moe_add_rmsnorm
+    with a zero residual and unit gamma), the rescale timed on its own."""
     pcfg = synth.CONFIGS["prefill4096x4"]
     n_layers = args.prefill_layers
     layers = []
@@ -347,23 +427,40 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
         layers.append(device_layer(pcfg, l, torch, moe, replicas=1)[0])
         log(f"[bench] prefill layer {l} ready in {time.time() - t0:.1f}s")
     Mp = pcfg.rows
-    xs = [torch.from_numpy(synth.activations(pcfg, layer=l)[0].view(np.int16)).cuda() for l in range(n_layers)]
+    H = d.hidden
+    x0 = torch.from_numpy(synth.activations(pcfg, layer=0)[0].view(np.int16)).cuda()
+    xin = [x0] + [torch.empty_like(x0) for _ in range(n_layers - 1)]
     wsp = moe.workspace(md, Mp)
-    yp = torch.empty((Mp, d.hidden), dtype=torch.int16, device="cuda")
+    yp = torch.empty((Mp, H), dtype=torch.int16, device="cuda")
+    zero = torch.zeros_like(yp)
+    ones = torch.full((H,), 0x3F80, dtype=torch.int16, device="cuda")        # bf16 1.0
+    rscr = torch.empty_like(yp)
+    xtmp = torch.empty_like(yp)
     rts = [moe.Routing.empty(md, Mp) for _ in layers]
 
     def pstep():
         for l, L in enumerate(layers):
-            moe.layer(md, xs[l], None, L["router_w"], L["bias"], L["experts"], L["shared"], yp, rts[l], wsp)
+            moe.layer(md, xin[l], None, L["router_w"], L["bias"], L["experts"], L["shared"], yp, rts[l], wsp)
+            if l + 1 < n_layers:
+                moe.add_rmsnorm(yp, None, zero, ones, 1e-6, rscr, xin[l + 1])
 
-    pstep()
-    torch.cuda.synchronize()
-    rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
-    for _ in range(args.prefill_steps):
-        pstep()
-    rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
-    torch.cuda.synchronize()
-    ms_p = ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.prefill_steps
+    def rescales():
+        for _ in range(n_layers - 1):
+            moe.add_rmsnorm(yp, None, zero, ones, 1e-6, rscr, xtmp)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+        for _ in range(n):
+            fn()
+        rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+        torch.cuda.synchronize()
+        return ev.elapsed_ms(ev.ev[0], ev.ev[1]) / n
+
+    ms_chain = timed(pstep, args.prefill_steps)
+    ms_resc = timed(rescales, args.prefill_steps) if n_layers > 1 else 0.0
+    ms_layers = ms_chain - ms_resc
     f8 = f16 = fr = 0.0
     pbytes = 0
     loads = []
@@ -375,12 +472,15 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
         rb, fb = decode_bytes(nu_l, d, Mp)
         pbytes += rb + fb
         loads.append(np.diff(rts[l].offs[:nu_l + 1].cpu().numpy()))
-    t_s = ms_p * 1e-3
+    t_s = ms_layers * 1e-3
     out = {
-        "workload": f"4096-token prefill chunk over {n_layers} stacked MoE layers (independent seeded weights, "
-                    "per-layer seeded inputs), Zipf(1.1) router bias, same layer shape",
+        "workload": f"4096-token prefill chunk through {n_layers} stacked MoE layers (independent seeded weights; "
+                    "layer l+1 takes layer l's output rescaled per row to unit RMS), Zipf(1.1) router bias, "
+                    "hidden 6144, 256 experts top-8, inter 2048 fp8 e4m3 128x128 scales, bf16 shared expert",
         "layers": n_layers,
-        "ms_per_step": round(ms_p, 4), "ms_per_layer": round(ms_p / n_layers, 4),
+        "ms_per_step": round(ms_chain, 4),
+        "ms_rescale_total": round(ms_resc, 4),
+        "ms_per_layer": round(ms_layers / n_layers, 4),
         "tflops_total": round((f8 + f16 + fr) / t_s / 1e12, 2),
         "tflops_fp8": round(f8 / t_s / 1e12, 2),
         "fp8_mfma_frac": round(f8 / t_s / 1e12 / FP8_PEAK_TFLOPS, 4),
@@ -388,8 +488,41 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
         "hbm_frac": round(pbytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
         "expert_rows_max": int(max(l.max() for l in loads)),
         "expert_rows_mean": round(float(np.mean([l.mean() for l in loads])), 1),
+        "timing": "chain of layers and rescales timed with HIP events; the rescales alone timed the same way "
+                  "and subtracted for the per-layer figures",
     }
-    log(f"[bench] prefill4096 x{n_layers} layers: {ms_p:.2f} ms/step, {out['tflops_total']} TFLOPS")
+    log(f"[bench] prefill4096 x{n_layers} layers: {ms_chain:.2f} ms/step ({ms_resc:.3f} ms of rescales), "
+        f"{out['tflops_total']} TFLOPS")
+
+    # per-kernel live timings of layer 0 (its input as in the chain)
+    L0 = layers[0]
+    nu0 = int(rts[0].n_union.item())
+    sl0 = int(rts[0].offs[nu0].item())
+
+    def call0(i):
+        moe.layer(md, xin[0], None, L0["router_w"], L0["bias"], L0["experts"], L0["shared"], yp, rts[0], wsp)
+    kus = traced_kernel_us(lib, torch, call0, max(2, args.prefill_steps))
+    out["kernel_us"] = {k: round(v, 2) for k, v in kus.items()}
+    gb = gateup_tiled_bytes(nu0, sl0, d, Mp)
+    g8, g16 = gateup_tiled_flops(sl0, d, Mp)
+    gus = kus["gateup"]
+    from sparse_moe_ffn_02_amd.profile_summary import load_mfma, load_traffic
+    tr = load_traffic(PREFILL_COUNTERS)
+    tk = tr["kernels"].get("gateup_tiled") if tr else None
+    mf = load_mfma(PREFILL_MFMA)
+    mk = mf["kernels"].get("gateup_tiled") if mf else None
+    out["roofline"] = {"kernel": "gateup_tiled", "bound": "hbm", "achieved": round(gb / (gus * 1e-6) / 1e9, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "traffic": (tk["read_bytes"] + tk["write_bytes"]) if tk else None,
+                       "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                       "algorithmic_bytes": gb, "kernel_us": round(gus, 2),
+                       "flops_fp8": g8, "flops_bf16": g16,
+                       "tflops": round((g8 + g16) / (gus * 1e-6) / 1e12, 1),
+                       "fp8_mfma_frac": round(g8 / (gus * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                       "mfma_busy_frac": mk["busy_frac"] if mk else None,
+                       "why_hbm": "256 flop per byte at this shape, below the fp8 ridge of 625 (5 PFLOP/s / 8 TB/s)"}
+    log(f"[bench] prefill gateup_tiled: {gus:.1f} us, {gb / 1e9:.2f} GB -> {gb / (gus * 1e-6) / 1e9:.0f} GB/s, "
+        f"{(g8 + g16) / (gus * 1e-6) / 1e12:.0f} TFLOP/s")
 
     # layer 0 followed by the next layer's residual add + RMSNorm, unfused and fused
     res_np, gam_np = synth.norm_inputs(pcfg, rows=Mp)
@@ -397,30 +530,19 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
     gam = torch.from_numpy(gam_np.view(np.int16)).cuda()
     r_out = torch.empty_like(res)
     n_out = torch.empty_like(res)
-    L0 = layers[0]
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
-        for _ in range(args.prefill_steps):
-            fn()
-        rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
-        torch.cuda.synchronize()
-        return ev.elapsed_ms(ev.ev[0], ev.ev[1]) / args.prefill_steps
 
     def unfused():
-        moe.layer(md, xs[0], None, L0["router_w"], L0["bias"], L0["experts"], L0["shared"], yp, rts[0], wsp)
+        call0(0)
         moe.add_rmsnorm(yp, None, res, gam, 1e-6, r_out, n_out)
 
     def fused():
-        moe.layer_add_rmsnorm(md, xs[0], None, L0["router_w"], L0["bias"], L0["experts"], L0["shared"], res, gam,
+        moe.layer_add_rmsnorm(md, xin[0], None, L0["router_w"], L0["bias"], L0["experts"], L0["shared"], res, gam,
                               1e-6, yp, r_out, n_out, rts[0], wsp)
     # alternate the two so that clock drift does not favour either; medians of 3
     t_unf, t_fus = [], []
     for _ in range(3):
-        t_unf.append(timed(unfused))
-        t_fus.append(timed(fused))
+        t_unf.append(timed(unfused, args.prefill_steps))
+        t_fus.append(timed(fused, args.prefill_steps))
     ms_unf, ms_fus = float(np.median(t_unf)), float(np.median(t_fus))
     out["add_rmsnorm"] = {"unfused_ms": round(ms_unf, 4), "fused_ms": round(ms_fus, 4),
                           "timing": "median of 3 alternating runs of --prefill-steps calls each",
@@ -428,6 +550,51 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream):
                                       "(bf16 residual [4096, 6144], gamma [6144], eps 1e-6)"}
     log(f"[bench] prefill layer + add/RMSNorm: unfused {ms_unf:.3f} ms, fused {ms_fus:.3f} ms")
     return out
+
+
+def cpu_oracle_baseline(synth, cfg, x_np, mask_np, nu, total_b, M, union):
+    """The CPU oracle, as it stands, on the span-8 step (the JSON line's
+    baseline, on every host core the process may use), and its wall time on
+    the tiny, span-8 and DP8 steps with one thread and with all of them.
+    Expert weights come from the seeded generator in their row-major
+    checkpoint layout, as the oracle takes them."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    threads, model = cpu_info()
+
+    def run(c, union_hint=None):
+        d = c.dims
+        x, mk = synth.activations(c)
+        host = {}
+        if union_hint is not None:
+            synth.for_each_expert(c, 0, lambda e, t: host.__setitem__(e, t), experts=union_hint)
+
+        def expert(e):
+            if e not in host:
+                host[e] = synth.routed_expert(c, 0, e)
+            return host[e]
+        wr, b, sh = synth.router_weight(c, 0), synth.router_bias(c, 0), synth.shared_expert(c, 0)
+        # the experts a step needs are generated before the timed part
+        ids, _, _ = oracle.route(x, mk, wr, b, d.top_k, d.routed_scale)
+        for e in sorted(set(int(v) for v in ids[mk != 0].ravel())):
+            expert(e)
+        t1 = {}
+        for label, lim in (("threads_all", threads), ("threads_1", 1)):
+            with threadpool_limits(lim):
+                c0 = time.time()
+                oracle.layer(x, mk, wr, b, d.top_k, d.routed_scale, expert, sh)
+                t1[label] = round(time.time() - c0, 3)
+        return t1
+
+    log(f"[bench] CPU oracle ({threads} threads and 1 thread): tiny, span8, dp8")
+    secs = {"tiny": run(synth.CONFIGS["tiny"]), "span8": run(cfg, union), "dp8": run(synth.CONFIGS["dp8"])}
+    cpu_s = secs["span8"]["threads_all"]
+    base = {"value": round(total_b / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"one whole span-8 step ({M} rows, |U|={nu}) in {cpu_s:.2f} s on {model}; float64 numpy; "
+                      "the same algorithmic bytes as the GPU line over the oracle's wall time",
+            "seconds": cpu_s}
+    log(f"[bench] oracle seconds: {secs}")
+    return base, {"cores_all": threads, "cpu_model": model, **secs}
 
 
 # ----------------------------------------------------------------------------- main
@@ -475,7 +642,8 @@ def main():
         pmd = moe.Dims(pd.hidden, pd.n_experts, pd.top_k, pd.inter, pd.shared_inter, pd.routed_scale)
         pev = HipEvents(2)
         pev.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
-        out = prefill_bench(args, torch, moe, synth, pmd, pd, pev, pev.rt, torch.cuda.current_stream().cuda_stream)
+        out = prefill_bench(args, torch, moe, synth, pmd, pd, pev, pev.rt, torch.cuda.current_stream().cuda_stream,
+                            lib)
         pev.close()
         print(json.dumps({"prefill": out}), flush=True)
         return
@@ -528,29 +696,20 @@ def main():
         f"{us_p10:.1f}/{us_p50:.1f}/{us_p90:.1f})")
     # a graph of consecutive layer calls (replicas in rotation), as a decode graph holds them
     n_chain = 4 * len(reps)
-    us_chain = graph_chain_us(torch, step, n_chain, args.steps, args.warmup, rt_lib, stream)
-    log(f"[bench] span8 graph replay, {n_chain} consecutive calls per graph: {us_chain:.1f} us/step")
+    us_chain, ch_p10, ch_p50, ch_p90 = graph_chain_us(torch, step, n_chain, args.steps, args.warmup, rt_lib, stream)
+    log(f"[bench] span8 graph replay, {n_chain} consecutive calls per graph: {us_chain:.1f} us/step "
+        f"(per replay p10/p50/p90 {ch_p10:.1f}/{ch_p50:.1f}/{ch_p90:.1f})")
+    # hot weights: the same chain on one replica only (its weights partly held in the caches between calls)
+    us_hot = graph_chain_us(torch, lambda i: step(0), n_chain, args.steps, args.warmup, rt_lib, stream)[0]
+    log(f"[bench] span8 hot weights (one replica): {us_hot:.1f} us/step")
+    copy_bw = copy_gbs(torch, rt_lib, stream)
+    log(f"[bench] device copy: {copy_bw:.0f} GB/s")
     ms_step = min(us_step, us_chain) * 1e-3
     gbs = total_b / (ms_step * 1e-3) / 1e9
     log(f"[bench] span8: {ms_step * 1e3:.1f} us/step -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak)")
 
     # traced pass: per-kernel HIP events, same steps, same stream
-    nk = 16
-    tev = HipEvents(2 * nk * args.steps)
-    pairs = (C.c_void_p * (2 * nk * args.steps))(*[h.value for h in tev.ev])
-    kid = (C.c_int32 * (nk * args.steps))()
-    cnt = C.c_int32(0)
-    assert lib.moe_trace_set(pairs, nk * args.steps, kid, C.byref(cnt)) == 0
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    lib.moe_trace_set(None, 0, None, None)
-    per = {}
-    for i in range(cnt.value):
-        name = lib.moe_kernel_name(kid[i]).decode()
-        per.setdefault(name, []).append(tev.elapsed_ms(tev.ev[2 * i], tev.ev[2 * i + 1]))
-    kern_us = {k: 1e3 * float(np.mean(v)) for k, v in per.items()}
-    tev.close()
+    kern_us = traced_kernel_us(lib, torch, step, args.steps)
     streaming = {k: v for k, v in kern_us.items() if kernel_bytes(k, nu, d, M) is not None}
     dom = max(streaming, key=lambda k: streaming[k])
     dom_bytes = kernel_bytes(dom, nu, d, M)
@@ -582,11 +741,16 @@ def main():
         "layer_us_graph_one_call": round(us_step, 2),
         "layer_us_graph_chain": round(us_chain, 2),
         "layer_us_single_replay_p10_p50_p90": [round(us_p10, 2), round(us_p50, 2), round(us_p90, 2)],
+        "layer_us_graph_chain_p10_p50_p90": [round(ch_p10, 2), round(ch_p50, 2), round(ch_p90, 2)],
+        "layer_us_hot_weights": round(us_hot, 2),
         "timing": (f"hipGraph replay, the faster of one moe_layer call per graph and {n_chain} consecutive "
                    "calls per graph (weight replicas in rotation, as a decode graph over consecutive layers "
                    "holds them); every call reads its replica's weights from HBM; eager launches also "
                    "reported"),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "copy_gbs": round(copy_bw, 1),
+        "frac_of_copy": round(gbs / copy_bw, 4),
+        "copy_note": "torch device-to-device copy of 1 GiB, bytes read + written per second, same GPU, same run",
         "bytes_per_step": total_b,
         "routed_weight_bytes": routed_b,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
@@ -594,7 +758,8 @@ def main():
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(dom),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes": dom_bytes, "kernel_us": round(kern_us[dom], 2)},
+                     "algorithmic_bytes": dom_bytes, "kernel_us": round(kern_us[dom], 2),
+                     "frac_of_copy": round(dom_gbs / copy_bw, 4)},
     }
 
     # ---------------- the layer with the next layer's residual add + RMSNorm, unfused and fused
@@ -671,32 +836,8 @@ def main():
 
     # ---------------- CPU oracle baseline on the same decode step
     if not args.no_cpu_baseline:
-        import oracle
-        threads, model = cpu_info()
-        host = {}
-
-        def expert(e):
-            if e not in host:
-                r = reps[0]["experts"]
-                host[e] = {k: getattr(r, a)[e].cpu().numpy() for k, a in
-                           (("gate", "w_gate"), ("up", "w_up"), ("down", "w_down"),
-                            ("s_gate", "s_gate"), ("s_up", "s_up"), ("s_down", "s_down"))}
-            return host[e]
-        sh = synth.shared_expert(cfg, 0)
-        wr = synth.router_weight(cfg, 0)
-        b = synth.router_bias(cfg, 0)
-        for e in rt.union_ids[:nu].cpu().numpy():
-            expert(int(e))
-        log(f"[bench] CPU oracle on the span8 step ({threads} threads)")
-        c0 = time.time()
-        oracle.layer(x_np, mask_np, wr, b, d.top_k, d.routed_scale, expert, sh)
-        cpu_s = time.time() - c0
-        result["cpu_baseline"] = {"value": round(total_b / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-                                  "kind": "oracle",
-                                  "sample": f"one whole span-8 step ({M} rows, |U|={nu}) in {cpu_s:.2f} s on "
-                                            f"{model}; float64 numpy",
-                                  "seconds": round(cpu_s, 3)}
-        log(f"[bench] oracle: {cpu_s:.2f} s")
+        result["cpu_baseline"], result["cpu_oracle_seconds"] = cpu_oracle_baseline(
+            synth, cfg, x_np, mask_np, nu, total_b, M, [int(e) for e in rt.union_ids[:nu].cpu().numpy()])
     if not args.no_sweeps:
         result["rows_sweep"] = rows_sweep(torch, moe, synth, md, d, reps, rt_lib, stream, min(args.steps, 100),
                                           args.warmup)
@@ -707,7 +848,7 @@ def main():
                                                   args.warmup, args.replicas)
 
     if not args.no_prefill:
-        result["prefill"] = prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream)
+        result["prefill"] = prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream, lib)
     ev.close()
     print(json.dumps(result), flush=True)
 

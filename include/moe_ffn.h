@@ -90,12 +90,24 @@ typedef struct {
   const float* bias;  /* fp32 [E], e_score_correction_bias, used for selection only */
 } moe_router_w;
 
+/* Layout tags of the weight structs below.  The expert kernels read
+ * weights only in the packed tile layout that moe_pack_weights writes; a
+ * caller states which layout its pointers hold, so that checkpoint-layout
+ * (row-major) weights are refused instead of being read as tiles (the pages
+ * require that an fp8 checkpoint missing its scales is refused rather than
+ * loaded as unscaled weights: mstar PR #388, fp8 checkpoint commit).  A
+ * zero-initialized struct carries MOE_WEIGHTS_ROW_MAJOR. */
+#define MOE_WEIGHTS_ROW_MAJOR 0u          /* checkpoint layout: refused with MOE_EUNSUPPORTED */
+#define MOE_WEIGHTS_PACKED 0x4B43504Du    /* every matrix rearranged by moe_pack_weights */
+
 /* Routed experts (device): e4m3 codes of the output-major matrices below
  * (K contiguous in the checkpoint), each packed by moe_pack_weights
  * (is_bf16 = 0), and one fp32 scale per 128x128 block (scales stay
  * row-major).  The [gate_proj, up_proj, down_proj] triple is consumed by
  * position (MoE-Infinity PR #140, expert-node commit).  All six pointers are
- * required: an fp8 expert without its scales is refused (MOE_EINVAL). */
+ * required: an fp8 expert without its scales is refused (MOE_EINVAL).
+ * layout must be MOE_WEIGHTS_PACKED (MOE_WEIGHTS_ROW_MAJOR: MOE_EUNSUPPORTED;
+ * any other value: MOE_EINVAL). */
 typedef struct {
   const uint8_t* w_gate; /* [E, I, H], packed */
   const uint8_t* w_up;   /* [E, I, H], packed */
@@ -103,14 +115,16 @@ typedef struct {
   const float* s_gate;   /* [E, I/128, H/128] */
   const float* s_up;     /* [E, I/128, H/128] */
   const float* s_down;   /* [E, H/128, I/128] */
+  uint32_t layout;       /* MOE_WEIGHTS_PACKED */
 } moe_expert_w;
 
 /* Shared expert (device): bf16, output-major, each matrix packed by
- * moe_pack_weights (is_bf16 = 1). */
+ * moe_pack_weights (is_bf16 = 1); layout as in moe_expert_w. */
 typedef struct {
   const uint16_t* w_gate; /* [I_s, H], packed */
   const uint16_t* w_up;   /* [I_s, H], packed */
   const uint16_t* w_down; /* [H, I_s], packed */
+  uint32_t layout;        /* MOE_WEIGHTS_PACKED */
 } moe_shared_w;
 
 /* Routing of one step (device buffers, written by moe_route / moe_layer and
@@ -150,15 +164,21 @@ int moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
  * phases): quantize x, gate/up GEMMs, SiLU*up with 1x128 requantization,
  * down GEMM, fixed-order weighted combine.  `in` may come from moe_route or
  * from any producer of the same layout; a malformed routing (n_union or
- * offsets out of range, union not ascending) contributes nothing.
+ * offsets out of range, union not ascending, an expert's rows not strictly
+ * ascending, a row outside [0, M) or a pad row in a row list) contributes
+ * nothing: y is then the zero-routing output (+0.0 for every row).
  * y: bf16 [M, H], routed part only (no shared expert); pad rows +0.0. */
 int moe_ffn_fp8(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
                 const moe_routing* in, const moe_expert_w* experts, uint16_t* y, moe_taps* taps, void* ws,
                 size_t ws_bytes, void* stream);
 
-/* The whole layer: moe_route, then the routed experts and the bf16 shared
- * expert (shared may be NULL only when dims->shared_inter == 0).
- * y: bf16 [M, H]; the routing is written to *out. */
+/* The whole layer (openinfer PR #610, "What": one layer of a step runs the
+ * expert union, the gate/up GEMMs, SiLU and the down GEMM over the step's
+ * rows, then combines in a fixed order; mstar PR #388, decode table note:
+ * one layer's routed and shared experts timed per call): moe_route, then the
+ * routed experts and the bf16 shared expert (shared may be NULL only when
+ * dims->shared_inter == 0).  y: bf16 [M, H]; the routing is written to
+ * *out. */
 int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
               const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
               moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream);
@@ -220,9 +240,11 @@ int moe_pack_weights(const void* src, void* dst, int64_t rows, int32_t row_bytes
  * launch stream, kernel_ids[i] receives the kernel's id and *count is
  * incremented, until *count reaches capacity.  The events (hipEvent_t) and
  * the three arrays are the caller's and must outlive the traced calls.
- * pairs == NULL switches tracing off.  Process-wide, not thread-safe:
- * measurement only.  Returns MOE_EINVAL for capacity < 0 or a NULL ids or
- * count with a non-NULL table. */
+ * pairs == NULL switches tracing off.  The table belongs to the calling host
+ * thread: only calls made from that thread are traced, and the hook is for
+ * measurement only (it is the one piece of state the library keeps between
+ * calls).  Returns MOE_EINVAL for capacity < 0 or a NULL ids or count with a
+ * non-NULL table. */
 typedef struct {
   void* start; /* hipEvent_t */
   void* stop;  /* hipEvent_t */

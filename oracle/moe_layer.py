@@ -248,13 +248,16 @@ def quant_rows(x_bits: np.ndarray, row_mask: np.ndarray):
 def ffn(x_bits: np.ndarray, row_mask: np.ndarray, routing: Routing,
         expert: Callable[[int], Dict[str, np.ndarray]],
         shared: Optional[Dict[str, np.ndarray]] = None,
-        rows: Optional[Sequence[int]] = None) -> LayerOut:
+        rows: Optional[Sequence[int]] = None,
+        pmap: Callable = map) -> LayerOut:
     """Routed experts (+ shared expert when given) and the fixed-order combine.
 
     y[r] = bf16( (((0 + w_1 D_1) + w_2 D_2) + ... + w_k D_k) + S[r] ) with
     the row's experts in ascending id.  `rows` restricts the evaluation to a
     subset of rows (each row is independent of the others); pad rows are
-    always +0.0.
+    always +0.0.  `pmap` (a map-like callable, e.g. a thread pool's map)
+    evaluates the union experts; each expert's output depends on its own rows
+    only, so the order in which they are evaluated changes nothing.
     """
     m, hdim = x_bits.shape
     real = np.asarray(row_mask) != 0
@@ -266,13 +269,19 @@ def ffn(x_bits: np.ndarray, row_mask: np.ndarray, routing: Routing,
     dslot: Dict[int, np.ndarray] = {}
     hq: Dict[int, np.ndarray] = {}
     hs: Dict[int, np.ndarray] = {}
+    work = []
     for u, e in enumerate(routing.union_ids):
         lo, hi = int(routing.offs[u]), int(routing.offs[u + 1])
         slots = [s for s in range(lo, hi) if int(routing.rows[s]) in want_set]
-        if not slots:
-            continue
+        if slots:
+            work.append((int(e), slots))
+
+    def run(item):
+        e, slots = item
         r_of = routing.rows[slots]
-        out = routed_expert(xq[r_of], xs[r_of], expert(int(e)))
+        return slots, routed_expert(xq[r_of], xs[r_of], expert(e))
+
+    for slots, out in pmap(run, work):
         for i, s in enumerate(slots):
             dslot[s] = out.d[i]
             hq[s] = out.h_codes[i]
@@ -296,8 +305,8 @@ def ffn(x_bits: np.ndarray, row_mask: np.ndarray, routing: Routing,
 def layer(x_bits: np.ndarray, row_mask: np.ndarray, router_w_bits: np.ndarray, bias: np.ndarray,
           top_k: int, routed_scale: float, expert: Callable[[int], Dict[str, np.ndarray]],
           shared: Optional[Dict[str, np.ndarray]] = None,
-          rows: Optional[Sequence[int]] = None) -> LayerOut:
+          rows: Optional[Sequence[int]] = None, pmap: Callable = map) -> LayerOut:
     """The whole layer: route, union, routed experts, shared expert, combine."""
     ids, w, _ = route(x_bits, row_mask, router_w_bits, bias, top_k, routed_scale)
     rt = union(ids, w, row_mask)
-    return ffn(x_bits, row_mask, rt, expert, shared, rows)
+    return ffn(x_bits, row_mask, rt, expert, shared, rows, pmap)

@@ -18,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = range(5)
+WEIGHTS_ROW_MAJOR = 0            # checkpoint layout (refused by the layer calls)
+WEIGHTS_PACKED = 0x4B43504D      # rearranged by moe_pack_weights
 MAX_ROWS, MAX_EXPERTS, MAX_TOPK, MAX_INTER = 16384, 256, 16, 8192
 SMALL_ROWS = 24      # steps of up to this many rows take the split small-step kernels (inter <= 512)
 SMALL_ROWS_WIDE = 16 # the same for wider experts (inter > 512)
@@ -46,11 +48,11 @@ class CRouter(C.Structure):
 
 class CExperts(C.Structure):
     _fields_ = [("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
-                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p)]
+                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p), ("layout", C.c_uint32)]
 
 
 class CShared(C.Structure):
-    _fields_ = [("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p)]
+    _fields_ = [("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p), ("layout", C.c_uint32)]
 
 
 class CRouting(C.Structure):
@@ -159,26 +161,31 @@ class Routing:
 
 @dataclass
 class Experts:
-    w_gate: torch.Tensor   # uint8 [E, I, H], packed (pack_experts)
+    """Routed expert weights.  The layer calls take them packed (pack_experts
+    returns layout=WEIGHTS_PACKED); row-major checkpoint tensors are refused."""
+    w_gate: torch.Tensor   # uint8 [E, I, H]
     w_up: torch.Tensor
-    w_down: torch.Tensor   # uint8 [E, H, I], packed
+    w_down: torch.Tensor   # uint8 [E, H, I]
     s_gate: torch.Tensor   # f32 [E, I/128, H/128]
     s_up: torch.Tensor
     s_down: torch.Tensor
+    layout: int = WEIGHTS_ROW_MAJOR
 
     def c(self) -> CExperts:
         return CExperts(*(_ptr(t) for t in (self.w_gate, self.w_up, self.w_down, self.s_gate, self.s_up,
-                                            self.s_down)))
+                                            self.s_down)), self.layout)
 
 
 @dataclass
 class Shared:
-    w_gate: torch.Tensor   # bf16 bits (int16/uint16) [I_s, H], packed (pack_shared)
+    """Shared-expert weights (bf16 bits); packed by pack_shared."""
+    w_gate: torch.Tensor   # bf16 bits (int16/uint16) [I_s, H]
     w_up: torch.Tensor
-    w_down: torch.Tensor   # [H, I_s], packed
+    w_down: torch.Tensor   # [H, I_s]
+    layout: int = WEIGHTS_ROW_MAJOR
 
     def c(self) -> CShared:
-        return CShared(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down))
+        return CShared(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down), self.layout)
 
 
 @dataclass
@@ -286,13 +293,18 @@ def _packed(t: torch.Tensor, is_bf16: bool) -> torch.Tensor:
 
 def pack_experts(row_major: Experts) -> Experts:
     """Packed copies of row-major expert weights (scales are shared, not copied)."""
+    if row_major.layout != WEIGHTS_ROW_MAJOR:
+        raise MoeError(MOE_EINVAL, "pack_experts takes row-major weights")
     return Experts(_packed(row_major.w_gate, False), _packed(row_major.w_up, False), _packed(row_major.w_down, False),
-                   row_major.s_gate, row_major.s_up, row_major.s_down)
+                   row_major.s_gate, row_major.s_up, row_major.s_down, WEIGHTS_PACKED)
 
 
 def pack_shared(row_major: Shared) -> Shared:
     """Packed copies of row-major bf16 shared-expert weights."""
-    return Shared(_packed(row_major.w_gate, True), _packed(row_major.w_up, True), _packed(row_major.w_down, True))
+    if row_major.layout != WEIGHTS_ROW_MAJOR:
+        raise MoeError(MOE_EINVAL, "pack_shared takes row-major weights")
+    return Shared(_packed(row_major.w_gate, True), _packed(row_major.w_up, True), _packed(row_major.w_down, True),
+                  WEIGHTS_PACKED)
 
 
 def quant_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> None:

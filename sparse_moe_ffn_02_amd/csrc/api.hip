@@ -85,11 +85,23 @@ int check_routing(const moe_routing* r) {
   return MOE_OK;
 }
 
+// The kernels read weights only as packed tiles; a struct that does not say
+// so is refused before anything is enqueued.
+int check_layout(uint32_t layout) {
+  if (layout == MOE_WEIGHTS_PACKED) return MOE_OK;
+  return layout == MOE_WEIGHTS_ROW_MAJOR ? MOE_EUNSUPPORTED : MOE_EINVAL;
+}
+
 int check_experts(const moe_expert_w* w) {
   if (!w) return MOE_EINVAL;
   if (!ok_ptr(w->w_gate, 16) || !ok_ptr(w->w_up, 16) || !ok_ptr(w->w_down, 16)) return MOE_EINVAL;
   if (!ok_ptr(w->s_gate, 4) || !ok_ptr(w->s_up, 4) || !ok_ptr(w->s_down, 4)) return MOE_EINVAL;
-  return MOE_OK;
+  return check_layout(w->layout);
+}
+
+int check_shared(const moe_shared_w* w) {
+  if (!w || !ok_ptr(w->w_gate, 16) || !ok_ptr(w->w_up, 16) || !ok_ptr(w->w_down, 16)) return MOE_EINVAL;
+  return check_layout(w->layout);
 }
 
 int check_taps(const moe_taps* t) {
@@ -178,13 +190,15 @@ FfnArgs ffn_args(const moe_dims& d, int M, const uint16_t* x, const uint8_t* mas
   return a;
 }
 
+// The timing hook's table, per host thread: calls from other threads are
+// never traced.
 struct Tracer {
   moe_event_pair* pairs = nullptr;
   int32_t cap = 0;
   int32_t* ids = nullptr;
   int32_t* count = nullptr;
 };
-Tracer g_trace;
+thread_local Tracer g_trace;
 
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
@@ -304,8 +318,7 @@ int layer_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t
   if ((st = check_experts(experts)) != MOE_OK) return st;
   if ((st = check_taps(taps)) != MOE_OK) return st;
   if (dims->shared_inter > 0) {
-    if (!shared || !ok_ptr(shared->w_gate, 16) || !ok_ptr(shared->w_up, 16) || !ok_ptr(shared->w_down, 16))
-      return MOE_EINVAL;
+    if ((st = check_shared(shared)) != MOE_OK) return st;
   } else {
     shared = nullptr;
   }

@@ -67,26 +67,57 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* in, const uint8_t* 
 
 // ---------------------------------------------------------------- plan
 // Checks a caller-supplied routing and derives the column-tile schedule.
-// A malformed routing (n_union out of range, offsets not starting at 0 or
-// not ascending, union ids not ascending in [0, E), more slots than M*K)
-// schedules no routed work and sets sched[SCHED_BAD] = 1.
-__global__ __launch_bounds__(64) void k_plan(FfnArgs a) {
-  if (threadIdx.x != 0) return;
-  int nu = *a.n_union;
-  const int max_u = min(a.E, a.M * a.K);
-  bool bad = nu < 0 || nu > max_u;
-  int mt = 0, prev_e = -1;
-  if (!bad) {
-    if (a.offs[0] != 0) bad = true;
-    for (int u = 0; u < nu && !bad; ++u) {
-      const int e = a.union_ids[u];
-      const int lo = a.offs[u], hi = a.offs[u + 1];
-      if (e <= prev_e || e >= a.E || hi < lo || hi > a.M * a.K) { bad = true; break; }
-      prev_e = e;
-      a.mtile_offs[u] = mt;
-      mt += (hi - lo + kMTile - 1) / kMTile;
+// A malformed routing -- n_union out of range, offsets not starting at 0 or
+// not ascending, union ids not ascending in [0, E), more slots than M*K, an
+// expert's rows not strictly ascending, a row outside [0, M) or a pad row --
+// schedules no routed work and sets sched[SCHED_BAD] = 1.  (Strictly
+// ascending real rows are what the split kernels assume: each of an expert's
+// slots is found from its row, so a repeated row would leave a slot unwritten.)
+constexpr int kPlanThreads = 256;
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(FfnArgs a) {
+  __shared__ int s_bad, s_nu, s_mt;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int nu = *a.n_union;
+    const int max_u = min(a.E, a.M * a.K);
+    bool bad = nu < 0 || nu > max_u;
+    int mt = 0, prev_e = -1;
+    if (!bad) {
+      if (a.offs[0] != 0) bad = true;
+      for (int u = 0; u < nu && !bad; ++u) {
+        const int e = a.union_ids[u];
+        const int lo = a.offs[u], hi = a.offs[u + 1];
+        if (e <= prev_e || e >= a.E || hi < lo || hi > a.M * a.K) { bad = true; break; }
+        prev_e = e;
+        a.mtile_offs[u] = mt;
+        mt += (hi - lo + kMTile - 1) / kMTile;
+      }
+    }
+    s_bad = bad ? 1 : 0;
+    s_nu = bad ? 0 : nu;
+    s_mt = mt;
+  }
+  __syncthreads();
+  // rows of every slot: in range, real, strictly ascending inside an expert
+  // (the expert of slot s found by a binary search over the checked offsets)
+  int bad = s_bad;
+  const int nu = s_nu;
+  if (!bad && nu > 0) {
+    const int slots = a.offs[nu];
+    for (int s = tid; s < slots; s += kPlanThreads) {
+      const int r = a.rows[s];
+      if (r < 0 || r >= a.M || !row_real(a.mask, r)) { bad = 1; break; }
+      int lo = 0, hi = nu - 1;              // largest u with offs[u] <= s
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.offs[mid] <= s) lo = mid; else hi = mid - 1;
+      }
+      if (s > a.offs[lo] && a.rows[s - 1] >= r) { bad = 1; break; }
     }
   }
+  bad = __syncthreads_or(bad);
+  if (tid != 0) return;
   if (bad) {
     a.sched[SCHED_NUNION] = 0;
     a.sched[SCHED_MTILES] = 0;
@@ -95,9 +126,9 @@ __global__ __launch_bounds__(64) void k_plan(FfnArgs a) {
     a.mtile_offs[0] = 0;
     return;
   }
-  a.mtile_offs[nu] = mt;
+  a.mtile_offs[nu] = s_mt;
   a.sched[SCHED_NUNION] = nu;
-  a.sched[SCHED_MTILES] = mt;
+  a.sched[SCHED_MTILES] = s_mt;
   a.sched[SCHED_SLOTS] = a.offs[nu];
   a.sched[SCHED_BAD] = 0;
 }
@@ -572,7 +603,7 @@ hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int
 }
 
 hipError_t launch_plan(const FfnArgs& a, hipStream_t s) {
-  MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(64), 0, s, a);
+  MOE_LAUNCH(KID_PLAN, k_plan, dim3(1), dim3(kPlanThreads), 0, s, a);
   return hipSuccess;
 }
 

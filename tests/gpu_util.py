@@ -2,12 +2,16 @@
 through the C ABI, and compare against the CPU oracle."""
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
+from contextlib import contextmanager
 from dataclasses import dataclass
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import oracle
 import sparse_moe_ffn_02_amd as moe
@@ -123,11 +127,55 @@ def run_ffn(gl: GpuLayer, x_bits: np.ndarray, mask: Optional[np.ndarray], rt: or
                 x_codes=tp.x_codes.cpu().numpy(), x_scales=tp.x_scales.cpu().numpy())
 
 
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+@contextmanager
+def expert_pool():
+    """A map over union experts for the oracle: one thread per core, each with
+    single-threaded BLAS (the oracle's per-expert work is small matmuls and
+    table decodes, which scale better across experts than inside one)."""
+    with threadpool_limits(1), ThreadPoolExecutor(_workers()) as ex:
+        yield ex.map
+
+
 def run_oracle(gl: GpuLayer, x_bits, mask, rows=None, shared=True) -> oracle.LayerOut:
     d = gl.host.dims
-    return oracle.layer(x_bits, mask if mask is not None else np.ones(x_bits.shape[0], np.uint8), gl.host.router_w,
-                        gl.host.bias, d.top_k, d.routed_scale, gl.expert_fn(),
-                        gl.host.shared if (shared and gl.host.shared) else None, rows=rows)
+    with expert_pool() as pmap:
+        return oracle.layer(x_bits, mask if mask is not None else np.ones(x_bits.shape[0], np.uint8),
+                            gl.host.router_w, gl.host.bias, d.top_k, d.routed_scale, gl.expert_fn(),
+                            gl.host.shared if (shared and gl.host.shared) else None, rows=rows, pmap=pmap)
+
+
+def cover_rows(offs: np.ndarray, rows: np.ndarray, extra=()) -> List[int]:
+    """Rows to evaluate with the oracle at full size, chosen from a step's
+    routing (offs [n_union + 1], rows [slots]) so that every union expert and
+    every tile position class is checked: for each expert, the rows of its
+    first slot (first 16-slot group of its first 128-slot tile), its last slot
+    (the last live group of its last tile) and the first slot of its last
+    tile; for the expert with the most slots, also the first and last slot of
+    its second tile.  Plus `extra` rows."""
+    want = set(int(r) for r in extra)
+    nu = offs.size - 1
+    for u in range(nu):
+        lo, hi = int(offs[u]), int(offs[u + 1])
+        if hi <= lo:
+            continue
+        nt = (hi - lo + 127) // 128
+        for s in (lo, hi - 1, lo + 128 * (nt - 1)):
+            want.add(int(rows[s]))
+    if nu:
+        u = int(np.argmax(np.diff(offs)))
+        lo, hi = int(offs[u]), int(offs[u + 1])
+        for s in (lo + 128, lo + 255):
+            if s < hi:
+                want.add(int(rows[s]))
+    return sorted(want)
 
 
 # ---------------------------------------------------------------- comparisons
@@ -185,14 +233,17 @@ def h_value_bounds(out: oracle.LayerOut, gl: "GpuLayer"):
     codes with the sign bit cleared."""
     rt = out.routing
     ew = gl.expert_fn()
-    res = {}
+    work = []
     for u, e in enumerate(rt.union_ids):
         slots = [s for s in range(int(rt.offs[u]), int(rt.offs[u + 1])) if s in out.h_codes]
-        if not slots:
-            continue
+        if slots:
+            work.append((int(e), slots))
+
+    def one(item):
+        e, slots = item
         rows = rt.rows[slots]
         xq, xs = out.x_codes[rows], out.x_scales[rows]
-        w = ew(int(e))
+        w = ew(e)
         g = oracle.block_gemm(xq, xs, w["gate"], w["s_gate"])
         uu = oracle.block_gemm(xq, xs, w["up"], w["s_up"])
         ag = oracle.block_gemm(xq & 0x7F, xs, w["gate"] & 0x7F, w["s_gate"])
@@ -203,38 +254,86 @@ def h_value_bounds(out: oracle.LayerOut, gl: "GpuLayer"):
         sg = 1.0 / (1.0 + np.exp(-g))
         h = g * sg * uu
         dh = np.abs(uu * sg * (1.0 + g * (1.0 - sg))) * dg + np.abs(g * sg) * du + 2.0 ** -21 * np.abs(h)
-        for i, s in enumerate(slots):
-            res[s] = (h[i], dh[i])
+        return slots, h, dh
+
+    res = {}
+    with expert_pool() as pmap:
+        for slots, h, dh in pmap(one, work):
+            for i, s in enumerate(slots):
+                res[s] = (h[i], dh[i])
     return res
 
 
+def _e4m3_value(v: np.ndarray) -> np.ndarray:
+    """Value of the RNE-saturating e4m3 code of fl32(v) (v float64)."""
+    return oracle.decode_e4m3(oracle.encode_e4m3(np.asarray(v, dtype=np.float64).astype(np.float32)))
+
+
 def compare_h_codes(g_codes: np.ndarray, g_scales: np.ndarray, out: oracle.LayerOut, gl: "GpuLayer",
-                    max_frac=1e-2, scale_tol=2.0 ** -10):
+                    max_frac=5e-3, scale_tol=2.0 ** -13):
     """Layer-level h codes.
 
     The requantization itself is bit-exact (checked on its own against the
-    oracle's fl32(h)).  Upstream, G and U carry the MFMA error above, so an h
-    lying that close to a rounding midpoint lands on another code.  Allowed:
-    every decoded GPU value within (propagated error bound + one e4m3 step at
-    that magnitude) of the oracle's h, at most 1% of codes different, and
-    block scales (amax/448) within 2^-10 relative."""
+    oracle's fl32(h)).  Upstream, G and U carry the MFMA error bounded above,
+    so the GPU's h is known to lie in [h - dh, h + dh] around the oracle's
+    float64 h.  Every GPU result is then checked against what that interval
+    allows, with no further slack:
+      * a block's scale s_gpu = fl32(amax/448) must lie between the scales of
+        the smallest and the largest amax the interval allows (an all-zero
+        block must have s = 1 and zero codes);
+      * each code must decode to a value between the codes of fl32(lo / s_gpu)
+        and fl32(hi / s_gpu) (encoding is monotone), lo, hi = h -+ dh.
+    So a code can differ from the oracle's only where the oracle's h lies
+    within the MFMA error of an e4m3 rounding midpoint.  On top, at most
+    max_frac of the codes may differ and no scale may differ by more than
+    scale_tol relative (about 3x the observed rates: 0.10-0.15 % of codes,
+    scales within 4.3e-5)."""
     bounds = h_value_bounds(out, gl)
     n = 0
     bad = 0
     worst = 0.0
+    widen = 2.0 ** -30            # float64 division before the fp32 rounding
     for s, oc in out.h_codes.items():
         gc = g_codes[s]
         bad += int((gc != oc).sum())
         n += oc.size
         gs = g_scales[s].astype(np.float64)
         os_ = out.h_scales[s].astype(np.float64)
-        hg = (oracle.decode_e4m3(gc).reshape(gs.size, -1) * gs[:, None]).reshape(-1)
         h, dh = bounds[s]
-        step = _e4m3_step(h / np.repeat(os_, 128)) * np.repeat(os_, 128)
-        ok = np.abs(hg - h) <= dh + 1.01 * step
-        assert ok.all(), f"h values differ at slot {s}: worst excess {np.max(np.abs(hg - h) - dh - step):.3e}"
+        nb = gs.size
+        hb, db = h.reshape(nb, -1), dh.reshape(nb, -1)
+        a_lo = np.maximum(np.abs(hb) - db, 0.0).max(axis=1) * (1.0 - widen)
+        a_hi = (np.abs(hb) + db).max(axis=1) * (1.0 + widen)
+        s_lo = np.where(a_lo > 0, (a_lo / 448.0).astype(np.float32), 0.0).astype(np.float64)
+        s_hi = np.where(a_hi > 0, (a_hi / 448.0).astype(np.float32), 1.0).astype(np.float64)
+        zero = a_hi == 0
+        assert np.all(gs[zero] == 1.0) and not gc.reshape(nb, -1)[zero].any(), f"slot {s}: zero block"
+        assert np.all((gs >= s_lo) & (gs <= s_hi) | zero | ((a_lo == 0) & (gs == 1.0))), (
+            f"slot {s}: h scale outside the interval the MFMA error allows: gpu {gs}, allowed [{s_lo}, {s_hi}]")
+        sg = np.repeat(gs, oc.size // nb)
+        lo = (h - dh) * np.where(h - dh > 0, 1.0 - widen, 1.0 + widen)
+        hi = (h + dh) * np.where(h + dh > 0, 1.0 + widen, 1.0 - widen)
+        v_lo, v_hi = _e4m3_value(lo / sg), _e4m3_value(hi / sg)
+        vg = oracle.decode_e4m3(gc)
+        ok = (vg >= v_lo) & (vg <= v_hi)
+        assert ok.all(), (f"slot {s}: {int((~ok).sum())} h codes outside what the MFMA error allows "
+                          f"(first at column {int(np.flatnonzero(~ok)[0])})")
         worst = max(worst, float(np.max(np.abs(gs - os_) / os_)))
-    say(f"h codes: {bad} of {n} differ; worst scale rel diff {worst:.2e}")
-    assert worst <= scale_tol, f"h scales differ by {worst:.2e}"
-    assert bad <= max(2, max_frac * n), f"{bad} of {n} h codes differ"
+    say(f"h codes: {bad} of {n} differ ({bad / max(n, 1):.2e}); worst scale rel diff {worst:.2e}")
+    assert worst <= scale_tol, f"h scales differ by {worst:.2e} > {scale_tol:.2e}"
+    assert bad <= max(2, max_frac * n), f"{bad} of {n} h codes differ (> {max_frac:.0e})"
     return bad, n
+
+
+def rescale_rows(y: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """The stacked-layer link of the 4096-token prefill config: the layer's
+    bf16 output rescaled per row to unit RMS, bf16(y / sqrt(mean(y^2) + eps)),
+    by moe_add_rmsnorm with a zero residual and unit gamma (fl32(0) + fl32(y)
+    is y, so the sum is the layer output itself)."""
+    m, h = y.shape
+    zero = torch.zeros_like(y)
+    ones = torch.full((h,), 0x3F80, dtype=torch.int16, device=y.device)     # bf16 1.0
+    r_new = torch.empty_like(y)
+    out = torch.empty_like(y)
+    moe.add_rmsnorm(y, None, zero, ones, eps, r_new, out)
+    return out

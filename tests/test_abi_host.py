@@ -4,6 +4,8 @@ The library must load, export every function include/moe_ffn.h declares,
 and reject bad arguments with the documented status before enqueuing any
 work.  Only error paths and M == 0 are exercised here, so no kernel is ever
 launched and the fake (aligned, non-null) device addresses are never used.
+The module is skipped wherever a GPU is visible: should a validation check
+ever regress, a call here would launch kernels on those fake addresses.
 """
 import ctypes as C
 import os
@@ -11,6 +13,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import sparse_moe_ffn_02_amd as moe
 from sparse_moe_ffn_02_amd import _lib as L
@@ -19,6 +22,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
 
 FAKE = 0x7f0000000000          # 256-byte aligned, never dereferenced
+
+# device_count() does not initialise the GPU runtime
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake device addresses are only passed where no GPU is visible")
 
 
 def declared_functions():
@@ -82,16 +89,20 @@ def _routing():
 
 
 def _experts(**kw):
-    f = dict(w_gate=FAKE, w_up=FAKE, w_down=FAKE, s_gate=FAKE, s_up=FAKE, s_down=FAKE)
+    f = dict(w_gate=FAKE, w_up=FAKE, w_down=FAKE, s_gate=FAKE, s_up=FAKE, s_down=FAKE, layout=L.WEIGHTS_PACKED)
     f.update(kw)
     return L.CExperts(**f)
+
+
+def _shared(layout=L.WEIGHTS_PACKED):
+    return L.CShared(FAKE, FAKE, FAKE, layout)
 
 
 def _layer(lib, d, m, *, x=FAKE, router=None, experts=None, shared=None, y=FAKE, ws=FAKE, ws_bytes=1 << 40,
            routing=None, taps=None):
     router = router or L.CRouter(FAKE, FAKE)
     experts = experts or _experts()
-    shared = shared if shared is not None else L.CShared(FAKE, FAKE, FAKE)
+    shared = shared if shared is not None else _shared()
     routing = routing or _routing()
     return lib.moe_layer(C.byref(d), m, x, None, C.byref(router), C.byref(experts), C.byref(shared), y,
                          C.byref(routing), C.byref(taps) if taps is not None else None, ws, ws_bytes, None)
@@ -215,9 +226,11 @@ def _norm(lib, m=8, h=512, y=FAKE, res=FAKE, gamma=FAKE, eps=1e-6, res_out=FAKE,
     return lib.moe_add_rmsnorm(m, h, y, None, res, gamma, eps, res_out, out, None)
 
 
-def _layer_norm(lib, d, m, y=FAKE, res=FAKE, gamma=FAKE, eps=1e-6, res_out=FAKE, out=FAKE, ws_bytes=1 << 40):
-    return lib.moe_layer_add_rmsnorm(C.byref(d), m, FAKE, None, C.byref(L.CRouter(FAKE, FAKE)), C.byref(_experts()),
-                                     C.byref(L.CShared(FAKE, FAKE, FAKE)), res, gamma, eps, y, res_out, out, C.byref(_routing()), None,
+def _layer_norm(lib, d, m, y=FAKE, res=FAKE, gamma=FAKE, eps=1e-6, res_out=FAKE, out=FAKE, ws_bytes=1 << 40,
+                experts=None):
+    experts = experts or _experts()
+    return lib.moe_layer_add_rmsnorm(C.byref(d), m, FAKE, None, C.byref(L.CRouter(FAKE, FAKE)), C.byref(experts),
+                                     C.byref(_shared()), res, gamma, eps, y, res_out, out, C.byref(_routing()), None,
                                      FAKE, ws_bytes, None)
 
 
@@ -247,3 +260,25 @@ def test_layer_add_rmsnorm_rejects(lib):
     assert _layer_norm(lib, d, 8, ws_bytes=16) == L.MOE_EWORKSPACE
     assert _layer_norm(lib, _dims(hidden=6000), 8) == L.MOE_EINVAL
     assert _layer_norm(lib, _dims(top_k=17), 8) == L.MOE_EUNSUPPORTED
+
+
+def test_weight_layout_tag_is_required(lib):
+    """Checkpoint-layout (row-major) or untagged weights are refused before any
+    launch, never read as packed tiles."""
+    d = _dims()
+    untagged = L.CExperts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)          # zero-initialized layout field
+    assert untagged.layout == L.WEIGHTS_ROW_MAJOR
+    assert _layer(lib, d, 8, experts=untagged) == L.MOE_EUNSUPPORTED
+    assert _layer(lib, d, 8, experts=_experts(layout=L.WEIGHTS_ROW_MAJOR)) == L.MOE_EUNSUPPORTED
+    assert _layer(lib, d, 8, experts=_experts(layout=12345)) == L.MOE_EINVAL
+    assert _layer(lib, d, 8, shared=_shared(L.WEIGHTS_ROW_MAJOR)) == L.MOE_EUNSUPPORTED
+    assert _layer(lib, d, 8, shared=L.CShared(FAKE, FAKE, FAKE)) == L.MOE_EUNSUPPORTED
+    assert _layer(lib, d, 8, shared=_shared(7)) == L.MOE_EINVAL
+    rt = _routing()
+    assert lib.moe_ffn_fp8(C.byref(d), 8, FAKE, None, C.byref(rt), C.byref(untagged), FAKE, None, FAKE, 1 << 40,
+                           None) == L.MOE_EUNSUPPORTED
+    assert _layer_norm(lib, d, 8, experts=untagged) == L.MOE_EUNSUPPORTED
+    # the binding tags only what pack_experts / pack_shared produced
+    t = torch.zeros(16, dtype=torch.uint8)
+    assert moe.Experts(t, t, t, t, t, t).layout == L.WEIGHTS_ROW_MAJOR
+    assert moe.Shared(t, t, t).layout == L.WEIGHTS_ROW_MAJOR

@@ -2,9 +2,10 @@
 I=2048, shared I=2048), in the launch configuration the benchmark times.
 
 Routing, union, compaction and x codes are compared bit-exactly on every row.
-Output rows and h codes are compared on every row for the 8-row steps and on
-sampled rows for the prefill chunks (the oracle evaluates a row from its
-experts alone, so a sample is exact for that row).
+Output rows and h codes are compared on every row for the 8-row steps and, for
+the prefill chunks, on rows chosen to cover every union expert and every tile
+position class (the oracle evaluates a row from its experts alone, so a
+sample is exact for that row).
 """
 import numpy as np
 import pytest
@@ -12,7 +13,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (GpuLayer, assert_routing_equal, assert_y_close, compare_h_codes, run_layer, run_oracle, say)
+from gpu_util import (GpuLayer, assert_routing_equal, assert_y_close, compare_h_codes, cover_rows, np16,
+                      rescale_rows, run_layer, run_oracle, say, t16)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -77,7 +79,8 @@ def test_prefill512_chunk():
     x, mask = synth.activations(cfg)
     say("prefill512: M=512")
     g = run_layer(glz, x, mask)
-    sample = [0, 1, 255, 511]
+    sample = cover_rows(g["offs"], g["rows"], extra=(0, 1, 255, 511))
+    say(f"prefill512: oracle on {len(sample)} rows covering all {g['n_union']} union experts")
     o = run_oracle(glz, x, mask, rows=sample)
     assert_routing_equal(g, o.routing, mask)
     assert np.array_equal(g["x_codes"], o.x_codes) and np.array_equal(g["x_scales"], o.x_scales)
@@ -87,22 +90,47 @@ def test_prefill512_chunk():
     say(f"prefill512: |U|={g['n_union']}, loads min/mean/max {loads.min()}/{loads.mean():.1f}/{loads.max()}, "
         f"sampled max row rel err {err:.3e}")
     # the sampled rows equal the same rows run as an 8-row decode step
-    d = run_layer(glz, x[sample + [2, 3, 4, 5]], mask[sample + [2, 3, 4, 5]])
-    assert np.array_equal(d["y"][:4], g["y"][sample])
+    pick = [0, 1, 255, 511, 2, 3, 4, 5]
+    d = run_layer(glz, x[pick], mask[pick])
+    assert np.array_equal(d["y"][:4], g["y"][[0, 1, 255, 511]])
     # a repeat gives the same bits everywhere (no read of unsettled or racing data)
     g2 = run_layer(glz, x, mask)
     assert np.array_equal(g2["y"], g["y"]) and np.array_equal(g2["h_codes"], g["h_codes"])
 
 
-def test_prefill4096_layer0():
-    cfg, gl = glm_layer("prefill4096x4")
+def test_prefill4096_chain_of_4_layers():
+    """The 4096-token chunk through 4 stacked layers with independent seeded
+    weights: layer l + 1 takes layer l's GPU output rescaled per row to unit
+    RMS.  Each layer is compared with the oracle run on the GPU's own input to
+    that layer: routing, union and x codes on every row; y and h codes on rows
+    covering every union expert and tile position class."""
+    cfg = synth.CONFIGS["prefill4096x4"]
     x, mask = synth.activations(cfg, layer=0)
-    say("prefill4096: layer 0, M=4096")
-    g = run_layer(gl, x, mask)
-    sample = [7, 2048, 4095]
-    o = run_oracle(gl, x, mask, rows=sample)
-    assert_routing_equal(g, o.routing, mask)
-    assert np.array_equal(g["x_codes"], o.x_codes)
-    compare_h_codes(g["h_codes"], g["h_scales"], o, gl)
-    err = assert_y_close(g["y"], o, rows=sample)
-    say(f"prefill4096: |U|={g['n_union']}, sampled max row rel err {err:.3e}")
+    for l in range(cfg.n_layers):
+        _cache.clear()
+        torch.cuda.empty_cache()
+        say(f"prefill4096 layer {l}: generating weights")
+        gl = GpuLayer(synth.make_layer(cfg, layer=l))
+        g = run_layer(gl, x, mask)
+        sample = cover_rows(g["offs"], g["rows"], extra=(7, 2048, 4095))
+        say(f"prefill4096 layer {l}: |U|={g['n_union']}, oracle on {len(sample)} rows")
+        o = run_oracle(gl, x, mask, rows=sample)
+        assert_routing_equal(g, o.routing, mask)
+        assert np.array_equal(g["x_codes"], o.x_codes) and np.array_equal(g["x_scales"], o.x_scales)
+        compare_h_codes(g["h_codes"], g["h_scales"], o, gl)
+        err = assert_y_close(g["y"], o, rows=sample)
+        loads = np.diff(o.routing.offs)
+        say(f"prefill4096 layer {l}: sampled max row rel err {err:.3e}, expert rows max {loads.max()}")
+        del gl
+        if l + 1 < cfg.n_layers:
+            yb = t16(g["y"])
+            xn = np16(rescale_rows(yb))
+            # the link itself: r_new is y, out is y at unit RMS (oracle in float64, bf16 rounding + fp32 sums)
+            r_new, ref = oracle.add_rmsnorm(g["y"], np.zeros_like(g["y"]), np.full(g["y"].shape[1], 0x3F80, np.uint16),
+                                            1e-6, mask)
+            assert np.array_equal(r_new, np.where(g["y"] == 0x8000, 0, g["y"]))
+            got = oracle.decode_bf16(xn)
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+            rms = np.sqrt(np.mean(got * got, axis=1))
+            assert np.all(np.abs(rms - 1.0) < 1e-2)
+            x = xn

@@ -251,13 +251,35 @@ def test_zero_rows_tie_to_lower_ids(tiny):
     assert np.allclose(g["w"], cfg.dims.routed_scale / k, rtol=0, atol=1e-7)
 
 
-def test_malformed_routing_contributes_nothing(tiny):
-    cfg, gl, x, mask = tiny
-    o = run_oracle(gl, x, mask, shared=False)
-    bad = oracle.Routing(o.routing.ids, o.routing.w, o.routing.union_ids[::-1].copy(), o.routing.offs,
-                         o.routing.rows, o.routing.slot_of)          # union not ascending
-    g = run_ffn(gl, x, mask, bad)
+@pytest.mark.parametrize("m", [8, 40])            # split and tiled paths
+@pytest.mark.parametrize("flaw", ["union_order", "repeated_row", "row_out_of_range", "pad_row", "rows_descending"])
+def test_malformed_routing_contributes_nothing(tiny, m, flaw):
+    """A caller routing that breaks the layout moe_ffn_fp8 documents is
+    detected on the device and schedules no routed work: y is +0.0."""
+    cfg, gl, _, _ = tiny
+    x = _rows(cfg, m, 77 + m)
+    mask = np.ones(m, np.uint8)
+    o = run_oracle(gl, x, mask, shared=False).routing
+    union_ids, rows, use_mask = o.union_ids.copy(), o.rows.copy(), mask.copy()
+    lo, hi = int(o.offs[0]), int(o.offs[1])
+    assert hi - lo >= 2
+    if flaw == "union_order":
+        union_ids = union_ids[::-1].copy()
+    elif flaw == "repeated_row":
+        rows[lo + 1] = rows[lo]
+    elif flaw == "row_out_of_range":
+        rows[hi - 1] = m
+    elif flaw == "pad_row":
+        use_mask[int(rows[lo])] = 0                       # a pad row left in the expert's list
+    else:
+        rows[lo], rows[lo + 1] = rows[lo + 1], rows[lo]
+    bad = oracle.Routing(o.ids, o.w, union_ids, o.offs, rows, o.slot_of)
+    say(f"malformed routing ({flaw}), M={m}")
+    g = run_ffn(gl, x, use_mask, bad)
     assert not g["y"].any()
+    # the well-formed routing on the same call shape does produce output
+    good = run_ffn(gl, x, mask, o)
+    assert good["y"].any()
 
 
 def test_workspace_reuse_across_sizes(tiny):
