@@ -183,6 +183,23 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
               const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
               moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: moe_layer
+ * without a workspace argument.  The call runs in a static device array of
+ * MOE_STATIC_WS_BYTES inside the library, one per GPU (the GPU current on the
+ * calling thread), held until the process ends; the call allocates nothing.
+ * Steps whose moe_workspace_bytes(dims, M) exceeds MOE_STATIC_WS_BYTES are
+ * refused with MOE_EWORKSPACE before anything is enqueued (at GLM-5.2's
+ * hidden 6144, 256 experts top-8, inter 2048: every step of up to 265
+ * rows).  Every call on
+ * a GPU shares that GPU's array, so calls that overlap on one GPU (on any
+ * streams) race; the array needs no clearing (each call writes every word it
+ * reads).  Other arguments and statuses as moe_layer. */
+#define MOE_STATIC_WS_BYTES (64u << 20)
+int moe_layer_static(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+                     const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared,
+                     uint16_t* y, moe_routing* out, moe_taps* taps, void* stream);
+
 /* Residual add + RMSNorm, the epilogue that feeds the next layer (mstar PR
  * #388: the "kernel switches" note fuses each all-reduce with the next add +
  * RMSNorm; its "Tests" list checks that the fused wiring emits what the

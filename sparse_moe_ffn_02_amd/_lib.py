@@ -65,8 +65,10 @@ class CTaps(C.Structure):
                 ("h_scales", C.c_void_p)]
 
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights",
-           "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_trace_set", "moe_kernel_name", "moe_status_str")
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_layer_static", "moe_quant_fp8",
+           "moe_pack_weights", "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_trace_set", "moe_kernel_name",
+           "moe_status_str")
+STATIC_WS_BYTES = 64 << 20       # MOE_STATIC_WS_BYTES: the static workspace of moe_layer_static
 
 _lib = None
 
@@ -88,6 +90,8 @@ def load() -> C.CDLL:
                                 C.POINTER(CTaps), P, C.c_size_t, P]
     lib.moe_layer.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter), C.POINTER(CExperts),
                               C.POINTER(CShared), P, C.POINTER(CRouting), C.POINTER(CTaps), P, C.c_size_t, P]
+    lib.moe_layer_static.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter), C.POINTER(CExperts),
+                                     C.POINTER(CShared), P, C.POINTER(CRouting), C.POINTER(CTaps), P]
     lib.moe_add_rmsnorm.argtypes = [C.c_int32, C.c_int32, P, P, P, P, C.c_float, P, P, P]
     lib.moe_layer_add_rmsnorm.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter),
                                           C.POINTER(CExperts), C.POINTER(CShared), P, P, C.c_float, P, P, P,
@@ -100,8 +104,8 @@ def load() -> C.CDLL:
     lib.moe_kernel_name.restype = C.c_char_p
     lib.moe_status_str.argtypes = [C.c_int]
     lib.moe_status_str.restype = C.c_char_p
-    for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_quant_fp8", "moe_pack_weights", "moe_add_rmsnorm",
-              "moe_layer_add_rmsnorm"):
+    for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_layer_static", "moe_quant_fp8", "moe_pack_weights",
+              "moe_add_rmsnorm", "moe_layer_add_rmsnorm"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib
@@ -250,6 +254,22 @@ def layer(dims: Dims, x: torch.Tensor, row_mask: Optional[torch.Tensor], router_
     _check(load().moe_layer(C.byref(d), x.shape[0], _ptr(x), _ptr(row_mask), C.byref(r), C.byref(ew),
                             C.byref(sw) if sw is not None else None, _ptr(y), C.byref(rt),
                             C.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream()))
+
+
+def layer_static(dims: Dims, x: torch.Tensor, row_mask: Optional[torch.Tensor], router_w: torch.Tensor,
+                 bias: torch.Tensor, experts: Experts, shared: Optional[Shared], y: torch.Tensor, routing: Routing,
+                 taps: Optional[Taps] = None) -> None:
+    """moe_layer_static: the layer in the library's static per-GPU workspace
+    (no workspace argument, nothing allocated by the call)."""
+    d = dims.c()
+    r = CRouter(_ptr(router_w), _ptr(bias))
+    ew = experts.c()
+    sw = shared.c() if shared is not None else None
+    rt = routing.c()
+    tp = taps.c() if taps is not None else None
+    _check(load().moe_layer_static(C.byref(d), x.shape[0], _ptr(x), _ptr(row_mask), C.byref(r), C.byref(ew),
+                                   C.byref(sw) if sw is not None else None, _ptr(y), C.byref(rt),
+                                   C.byref(tp) if tp is not None else None, _stream()))
 
 
 def add_rmsnorm(y: torch.Tensor, row_mask: Optional[torch.Tensor], residual: torch.Tensor, gamma: torch.Tensor,

@@ -3,6 +3,7 @@
 // synchronizes; every check happens before the first launch.
 #include <math.h>
 #include <algorithm>
+#include <mutex>
 #include <string.h>
 
 #include "moe_ffn.h"
@@ -307,9 +308,14 @@ int check_norm(const uint16_t* residual, const uint16_t* gamma, float eps, const
 
 // moe_layer, with the combine optionally running the add + RMSNorm epilogue
 // (nm != nullptr; y may then be null).
+int static_scratch(void** out);
+
+// ws == nullptr with use_static: the call runs in this GPU's static scratch
+// array (resolved only after every other check has passed).
 int layer_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
                const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
-               const NormArgs* nm, moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+               const NormArgs* nm, moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream,
+               bool use_static = false) {
   int st = check_dims(dims);
   if (st != MOE_OK) return st;
   if ((st = check_rows(M)) != MOE_OK) return st;
@@ -322,11 +328,12 @@ int layer_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t
   } else {
     shared = nullptr;
   }
-  if (!ok_ptr(x, 16) || !ok_ptr(ws, 16)) return MOE_EINVAL;
+  if (!ok_ptr(x, 16) || (!use_static && !ok_ptr(ws, 16))) return MOE_EINVAL;
   if (nm ? !ok_opt(y, 16) : !ok_ptr(y, 16)) return MOE_EINVAL;
   if (M == 0) return MOE_OK;
   const Layout L = make_layout(*dims, M);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (use_static && (st = static_scratch(&ws)) != MOE_OK) return st;
   char* w = static_cast<char*>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const RouteArgs ra = route_args(*dims, M, x, row_mask, *router, *out, w, L);
@@ -342,6 +349,35 @@ int layer_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t
   return to_status(launch_ffn(a, s, nm));
 }
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of moe_layer_static: one array of MOE_STATIC_WS_BYTES per GPU,
+// part of the library's device code, so it exists on every GPU the library
+// runs on until the process ends and no call ever allocates.  Host code must
+// not use the symbol itself (on the host it is only a stand-in for the device
+// address): the device address is looked up once per device, with that device
+// current, and kept.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WS_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array (MOE_ELAUNCH if the HIP
+// runtime cannot report the device or the symbol).
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ELAUNCH;
+  if (dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,6 +386,13 @@ int moe_layer(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t*
               const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared, uint16_t* y,
               moe_routing* out, moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
   return layer_impl(dims, M, x, row_mask, router, experts, shared, y, nullptr, out, taps, ws, ws_bytes, stream);
+}
+
+int moe_layer_static(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,
+                     const moe_router_w* router, const moe_expert_w* experts, const moe_shared_w* shared,
+                     uint16_t* y, moe_routing* out, moe_taps* taps, void* stream) {
+  return layer_impl(dims, M, x, row_mask, router, experts, shared, y, nullptr, out, taps, nullptr,
+                    MOE_STATIC_WS_BYTES, stream, true);
 }
 
 int moe_layer_add_rmsnorm(const moe_dims* dims, int32_t M, const uint16_t* x, const uint8_t* row_mask,

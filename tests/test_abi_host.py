@@ -282,3 +282,23 @@ def test_weight_layout_tag_is_required(lib):
     t = torch.zeros(16, dtype=torch.uint8)
     assert moe.Experts(t, t, t, t, t, t).layout == L.WEIGHTS_ROW_MAJOR
     assert moe.Shared(t, t, t).layout == L.WEIGHTS_ROW_MAJOR
+
+
+def test_layer_static_rejects(lib):
+    """moe_layer_static checks everything before it touches the GPU: steps too
+    large for its static workspace and bad arguments are refused, M == 0 is a
+    no-op."""
+    d = _dims()
+
+    def call(m, x=FAKE, y=FAKE, experts=None):
+        experts = experts or _experts()
+        return lib.moe_layer_static(C.byref(d), m, x, None, C.byref(L.CRouter(FAKE, FAKE)), C.byref(experts),
+                                    C.byref(_shared()), y, C.byref(_routing()), None, None)
+    assert call(0) == L.MOE_OK
+    assert call(266) == L.MOE_EWORKSPACE          # GLM dims: 265 rows is the most that fits in 64 MiB
+    assert call(4096) == L.MOE_EWORKSPACE
+    assert lib.moe_workspace_bytes(C.byref(d), 265) <= L.STATIC_WS_BYTES
+    assert call(8, x=None) == L.MOE_EINVAL
+    assert call(8, y=FAKE + 2) == L.MOE_EINVAL
+    assert call(8, experts=_experts(layout=L.WEIGHTS_ROW_MAJOR)) == L.MOE_EUNSUPPORTED
+    assert call(-1) == L.MOE_EINVAL
