@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_moe_ffn_02_amd as moe
 import synth
 from gpu_util import (GpuLayer, assert_routing_equal, assert_y_close, compare_h_codes, cover_rows, np16,
                       rescale_rows, run_layer, run_oracle, say, t16)
@@ -134,3 +135,20 @@ def test_prefill4096_chain_of_4_layers():
             rms = np.sqrt(np.mean(got * got, axis=1))
             assert np.all(np.abs(rms - 1.0) < 1e-2)
             x = xn
+
+
+def test_span8_and_dp8_steps_share_a_workspace():
+    """The span-8 and the DP8 step (different unions) alternate on one
+    workspace, as consecutive decode steps do; each equals its own fresh run."""
+    cfg, gl = glm_layer("span8")
+    xs, ms = synth.activations(cfg)
+    xd, md = synth.activations(synth.CONFIGS["dp8"])
+    ref = {"s": run_layer(gl, xs, ms)["y"], "d": run_layer(gl, xd, md)["y"]}
+    d = gl.dims
+    ws = moe.workspace(d, 8)
+    rt = moe.Routing.empty(d, 8)
+    y = torch.empty((8, d.hidden), dtype=torch.int16, device="cuda")
+    for k, x, mk in (("s", xs, ms), ("d", xd, md), ("s", xs, ms), ("d", xd, md)):
+        moe.layer(d, t16(x), torch.from_numpy(mk).cuda(), gl.router_w, gl.bias, gl.experts, gl.shared, y, rt, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(np16(y), ref[k]), k

@@ -345,3 +345,30 @@ def test_logit_kernels_give_identical_routing(tiny):
     assert np.array_equal(a["y"], b["y"][:100])
     o = run_oracle(gl, x, mask)
     assert_routing_equal(a, o.routing, mask)
+
+
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_reused_workspace_with_changing_inputs(tiny, m):
+    """One workspace and routing buffers reused by consecutive steps whose
+    inputs differ (A, B, A, B): every step equals the same step run alone on a
+    fresh workspace, bit for bit.  The small-step launch passes data between
+    workgroups through the workspace within one launch, so a value left over
+    from the previous step (a stale cache line) would show up here."""
+    cfg, gl, _, _ = tiny
+    d = gl.dims
+    xa = _rows(cfg, m, 3100 + m)
+    xb = _rows(cfg, m, 3200 + m)
+    mask = np.ones(m, np.uint8)
+    if m > 4:
+        mask[m // 2] = 0
+        xb[m // 2] = 0x7FC0
+    fresh = {k: run_layer(gl, x, mask) for k, x in (("a", xa), ("b", xb))}
+    ws = moe.workspace(d, m)
+    rt = moe.Routing.empty(d, m)
+    y = torch.empty((m, d.hidden), dtype=torch.int16, device="cuda")
+    mk = t8(mask)
+    for k, x in (("a", xa), ("b", xb), ("a", xa), ("b", xb)):
+        moe.layer(d, t16(x), mk, gl.router_w, gl.bias, gl.experts, gl.shared, y, rt, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), fresh[k]["y"]), k
+        assert np.array_equal(rt.topk_ids.cpu().numpy(), fresh[k]["ids"]), k
