@@ -15,10 +15,13 @@ the top-k, written without the union or row compaction; and the layer
 invariants (row slot permutation, companion rows, pad rows zero under NaN
 poison, repeat determinism); the residual add + RMSNorm epilogue against its
 closed form on constant rows, scale invariance, a library RMSNorm and
-library bf16 casts.  No function is left unpinned.
+library bf16 casts; the fixed-order sum of tensor-parallel partials against
+exact integer sums, a float64 sum within the rounding bound, a case whose
+result depends on the order, and pad rows.  No function is left unpinned.
 """
 from .codec import (E4M3_TABLE, decode_bf16, decode_e4m3, encode_bf16, encode_e4m3)
 from .norm import add_residual, add_rmsnorm, rmsnorm
+from .tp import sum_partials
 from .moe_layer import (BLOCK, ExpertOut, LayerOut, Routing, block_gemm, ffn, layer, quant_1x128,
                     quant_rows, route, routed_expert, shared_expert, sigmoid, silu, union)
 
@@ -26,5 +29,5 @@ __all__ = [
     "E4M3_TABLE", "decode_bf16", "decode_e4m3", "encode_bf16", "encode_e4m3",
     "BLOCK", "ExpertOut", "LayerOut", "Routing", "block_gemm", "ffn", "layer", "quant_1x128",
     "quant_rows", "route", "routed_expert", "shared_expert", "sigmoid", "silu", "union",
-    "add_residual", "add_rmsnorm", "rmsnorm",
+    "add_residual", "add_rmsnorm", "rmsnorm", "sum_partials",
 ]
