@@ -365,9 +365,16 @@ def tp8_rank_sweep(torch, moe, synth, rt_lib, stream, steps, warmup, replicas):
         out.append({"tokens": m, "union_experts": nu, "us": round(us, 2), "us_p10": round(p10, 2),
                     "us_p90": round(p90, 2), "gbs": round((rb + fb) / (us * 1e-6) / 1e9, 1)})
         log(f"[bench] tp8-rank M={m}: {us:.1f} us, |U|={nu}, {(rb + fb) / (us * 1e-6) / 1e9:.0f} GB/s")
+    # the fixed-order sum of the 8 ranks' partial outputs for an 8-row step ([row][src][H] region)
+    parts = torch.randint(-2000, 2000, (8, 8, d.hidden), dtype=torch.int16, device="cuda")
+    ysum = torch.empty((8, d.hidden), dtype=torch.int16, device="cuda")
+    sum_us = graph_replay_us(torch, lambda i: moe.sum_partials(parts, None, ysum), 1, steps, warmup, rt_lib,
+                             stream)[0]
+    log(f"[bench] tp8 fixed-order sum of 8 partials (8 rows): {sum_us:.1f} us")
     del reps
     torch.cuda.empty_cache()
-    return {"workload": "one TP8 rank's share on one GPU: hidden 6144, 256 experts top-8, expert inter 256 "
+    return {"sum_partials_8x8_us": round(sum_us, 2),
+            "workload": "one TP8 rank's share on one GPU: hidden 6144, 256 experts top-8, expert inter 256 "
                         "(I/8) fp8 e4m3 128x128 scales, shared expert inter 256 bf16, span-decode rows "
                         "(1 committed + drafts), weights rotated over device replicas, no collective",
             "points": out}

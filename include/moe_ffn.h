@@ -228,6 +228,20 @@ int moe_layer_add_rmsnorm(const moe_dims* dims, int32_t M, const uint16_t* x, co
                           uint16_t* residual_out, uint16_t* out, moe_routing* routing, moe_taps* taps, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* Fixed-order sum of tensor-parallel partial outputs (openinfer PR #610,
+ * description and "How": under TP8 each rank produces a partial layer
+ * output for every row into one region laid out [row][src][hidden], shared by
+ * the Dp8 and span row mappings, and the partials are summed in a fixed
+ * order; "Gates": the same rows through both mappings give the same bits).
+ * Per real row r and column n:
+ *   y[r, n] = bf16( (((0 + fl32(parts[r, 0, n])) + fl32(parts[r, 1, n])) + ...) )
+ * float32 additions in ascending source order, one RNE rounding; pad rows
+ * (row_mask 0) get +0.0 and their partials are never read.
+ * parts: bf16 [M, nsrc, H] (device); y: bf16 [M, H] (device, must not overlap
+ * parts); 1 <= nsrc <= 64; H a multiple of 4. */
+int moe_sum_partials(int32_t M, int32_t H, int32_t nsrc, const uint16_t* parts, const uint8_t* row_mask, uint16_t* y,
+                     void* stream);
+
 /* The 1x128 activation quantization step on its own (mstar PR #388,
  * FlashInfer crossover note): rows x cols values (fp32 if is_bf16 == 0, else
  * bf16 bits) -> e4m3 codes [rows, cols] and fp32 scales [rows, cols/128].

@@ -7,11 +7,11 @@ pack_weights, add_rmsnorm, layer_add_rmsnorm).
 """
 from ._lib import (EXPORTS, STATIC_WS_BYTES, MAX_EXPERTS, MAX_ROWS, MAX_TOPK, SMALL_ROWS, SMALL_ROWS_WIDE, split_rows, MOE_EINVAL, MOE_ELAUNCH, MOE_EUNSUPPORTED,
                    MOE_EWORKSPACE, MOE_OK, WEIGHTS_PACKED, WEIGHTS_ROW_MAJOR, Dims, Experts, MoeError, Routing, Shared, Taps, add_rmsnorm, ffn_fp8,
-                   layer, layer_add_rmsnorm, layer_static, load, pack_experts, pack_shared, pack_weights, quant_fp8, route,
+                   layer, layer_add_rmsnorm, layer_static, load, pack_experts, pack_shared, pack_weights, quant_fp8, route, sum_partials,
                    workspace, workspace_bytes)
 
 __all__ = [
     "EXPORTS", "STATIC_WS_BYTES", "MAX_EXPERTS", "MAX_ROWS", "MAX_TOPK", "SMALL_ROWS", "SMALL_ROWS_WIDE", "split_rows", "MOE_EINVAL", "MOE_ELAUNCH", "MOE_EUNSUPPORTED",
     "MOE_EWORKSPACE", "MOE_OK", "WEIGHTS_PACKED", "WEIGHTS_ROW_MAJOR", "Dims", "Experts", "MoeError", "Routing", "Shared", "Taps", "add_rmsnorm",
-    "ffn_fp8", "layer", "layer_add_rmsnorm", "layer_static", "load", "pack_experts", "pack_shared", "pack_weights", "quant_fp8", "route", "workspace", "workspace_bytes",
+    "ffn_fp8", "layer", "layer_add_rmsnorm", "layer_static", "load", "pack_experts", "pack_shared", "pack_weights", "quant_fp8", "route", "sum_partials", "workspace", "workspace_bytes",
 ]

@@ -66,8 +66,8 @@ class CTaps(C.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_layer_static", "moe_quant_fp8",
-           "moe_pack_weights", "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_trace_set", "moe_kernel_name",
-           "moe_status_str")
+           "moe_pack_weights", "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_sum_partials", "moe_trace_set",
+           "moe_kernel_name", "moe_status_str")
 STATIC_WS_BYTES = 64 << 20       # MOE_STATIC_WS_BYTES: the static workspace of moe_layer_static
 
 _lib = None
@@ -93,6 +93,7 @@ def load() -> C.CDLL:
     lib.moe_layer_static.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter), C.POINTER(CExperts),
                                      C.POINTER(CShared), P, C.POINTER(CRouting), C.POINTER(CTaps), P]
     lib.moe_add_rmsnorm.argtypes = [C.c_int32, C.c_int32, P, P, P, P, C.c_float, P, P, P]
+    lib.moe_sum_partials.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
     lib.moe_layer_add_rmsnorm.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter),
                                           C.POINTER(CExperts), C.POINTER(CShared), P, P, C.c_float, P, P, P,
                                           C.POINTER(CRouting), C.POINTER(CTaps), P, C.c_size_t, P]
@@ -105,7 +106,7 @@ def load() -> C.CDLL:
     lib.moe_status_str.argtypes = [C.c_int]
     lib.moe_status_str.restype = C.c_char_p
     for f in ("moe_route", "moe_ffn_fp8", "moe_layer", "moe_layer_static", "moe_quant_fp8", "moe_pack_weights",
-              "moe_add_rmsnorm", "moe_layer_add_rmsnorm"):
+              "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_sum_partials"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib
@@ -295,6 +296,13 @@ def layer_add_rmsnorm(dims: Dims, x: torch.Tensor, row_mask: Optional[torch.Tens
                                         C.byref(sw) if sw is not None else None, _ptr(residual), _ptr(gamma), eps,
                                         _ptr(y), _ptr(residual_out), _ptr(out), C.byref(rt),
                                         C.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream()))
+
+
+def sum_partials(parts: torch.Tensor, row_mask: Optional[torch.Tensor], y: torch.Tensor) -> None:
+    """moe_sum_partials: parts bf16 bits [M, nsrc, H] -> y [M, H], float32 sum in
+    ascending source order, one bf16 rounding."""
+    m, nsrc, h = parts.shape
+    _check(load().moe_sum_partials(m, h, nsrc, _ptr(parts), _ptr(row_mask), _ptr(y), _stream()))
 
 
 def pack_weights(src: torch.Tensor, dst: torch.Tensor, is_bf16: bool) -> None:

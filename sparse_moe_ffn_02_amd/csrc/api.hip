@@ -204,6 +204,7 @@ thread_local Tracer g_trace;
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
     "down", "combine", "quant", "select_union", "front", "pack", "combine_norm", "add_rmsnorm",
+    "sum_partials",
 };
 
 }  // namespace
@@ -426,6 +427,20 @@ int moe_add_rmsnorm(int32_t M, int32_t H, const uint16_t* y, const uint8_t* row_
   nm.res_out = residual_out;
   nm.out = out;
   return to_status(launch_add_rmsnorm(y, row_mask, M, H, nm, static_cast<hipStream_t>(stream)));
+}
+
+int moe_sum_partials(int32_t M, int32_t H, int32_t nsrc, const uint16_t* parts, const uint8_t* row_mask, uint16_t* y,
+                     void* stream) {
+  if (H <= 0 || H % 4 || nsrc < 1) return MOE_EINVAL;
+  if (nsrc > 64) return MOE_EUNSUPPORTED;
+  int st = check_rows(M);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(parts, 8) || !ok_ptr(y, 8)) return MOE_EINVAL;
+  const uintptr_t a = (uintptr_t)parts, b = (uintptr_t)y;
+  const uintptr_t na = (uintptr_t)M * nsrc * H * 2, nb = (uintptr_t)M * H * 2;
+  if (M > 0 && a < b + nb && b < a + na) return MOE_EINVAL;     // overlapping buffers
+  if (M == 0) return MOE_OK;
+  return to_status(launch_sum_partials(parts, row_mask, M, H, nsrc, y, static_cast<hipStream_t>(stream)));
 }
 
 int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, uint8_t* codes, float* scales,

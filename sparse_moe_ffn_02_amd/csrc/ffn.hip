@@ -573,6 +573,47 @@ hipError_t launch_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int M, int
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------- tensor-parallel partials
+// y[r, n..n+3] = bf16 of the float32 sum of parts[r, s, n..n+3] over s
+// ascending (one thread per row and 4 columns); pad rows +0.0.
+__global__ __launch_bounds__(256) void k_sum_partials(const uint16_t* parts, const uint8_t* mask, int M, int H,
+                                                      int nsrc, uint16_t* y) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int q = H / 4;
+  const int r = (int)(idx / q);
+  if (r >= M) return;
+  const int n = (int)(idx % q) * 4;
+  uint16_t* yp = y + (size_t)r * H + n;
+  if (!row_real(mask, r)) {
+    *reinterpret_cast<uint2*>(yp) = make_uint2(0u, 0u);
+    return;
+  }
+  const uint16_t* p = parts + (size_t)r * nsrc * H + n;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsrc; s0 += 8) {
+    uint2 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint2*>(p + (size_t)min(s0 + i, nsrc - 1) * H);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i >= nsrc) break;
+      float f[4];
+      unpack_bf16x4(v[i], f);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + f[k];
+    }
+  }
+  *reinterpret_cast<uint2*>(yp) = pack_bf16x4(acc);
+}
+
+hipError_t launch_sum_partials(const uint16_t* parts, const uint8_t* mask, int M, int H, int nsrc, uint16_t* y,
+                               hipStream_t s) {
+  const long threads = (long)M * (H / 4);
+  MOE_LAUNCH(KID_SUM_PARTIALS, k_sum_partials, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, parts, mask,
+             M, H, nsrc, y);
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- weight packing
 // Row-major [rows, row_bytes] -> packed tiles (see tile_row).  One thread per
 // 16-byte chunk of the destination: tile t = (row group, stage), half h and

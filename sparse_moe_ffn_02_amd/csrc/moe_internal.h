@@ -102,7 +102,7 @@ struct NormArgs {
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
   KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COMBINE_NORM, KID_ADD_NORM,
-  KID_COUNT
+  KID_SUM_PARTIALS, KID_COUNT
 };
 
 void trace_before(hipStream_t s);
@@ -132,6 +132,8 @@ hipError_t launch_add_rmsnorm(const uint16_t* y, const uint8_t* mask, int M, int
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s);
 bool use_split(int M, int H, int I);   // M <= split_rows(I)
 hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int is_bf16, hipStream_t s);
+hipError_t launch_sum_partials(const uint16_t* parts, const uint8_t* mask, int M, int H, int nsrc, uint16_t* y,
+                               hipStream_t s);
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);
 

@@ -10,11 +10,9 @@
 // straight into MFMA operand registers two K stages ahead, and applies them to
 // all 128 slots (eight 16-column MFMA tiles).  The tile's activation rows,
 // which all eight waves read, are staged through a double-buffered LDS ring.
-// The weight rows of one (expert, column tile) are shared by the expert's
-// slot tiles; their blocks are numbered so that they land on the same XCD
-// (blocks are dealt to the 8 XCDs round-robin and the column-tile count is a
-// multiple of 8), where the L2 serves the re-reads.  The routed down tiles
-// (12 of them at H = 6144) do not have that alignment.
+// All column tiles of one slot (or row) tile are numbered to run on one XCD,
+// one after another, so the tile's activation rows are read from HBM once and
+// from that XCD's L2 by the other column tiles (xcd_tile below).
 //
 // Every output element follows the same procedure as in the small-step
 // kernels: one fp8 16x16x128 MFMA per 128-deep K-block scaled into a fp32
@@ -39,6 +37,24 @@ constexpr int kNB = kTM / 16;              // 16-column slot tiles per wave
 // t / 8 + kBRowStep * i.
 constexpr int kBVec = kStageBytes * kTM / kTileThreads / 16;   // 16-byte loads per thread per stage
 constexpr int kBRowStep = kTileThreads / 8;                    // rows between a thread's loads
+
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8), each XCD with its own L2.  A range of workgroups starting at a
+// multiple of 8 maps its index r to (row tile, column tile) so that all column
+// tiles of one row tile share r % 8, i.e. one XCD, and follow each other on
+// it: r = 8 (q ncols + n) + x is row tile 8 q + x, column tile n.  The row
+// tile's activations are then read from HBM once and from that L2 by the
+// other column tiles.  Ranges are sized for a multiple of 8 row tiles; indices
+// past the real row tiles return row tile >= nrows.
+constexpr int kXcds = 8;
+
+__host__ __device__ inline int xcd_rows(int nrows) { return (nrows + kXcds - 1) / kXcds * kXcds; }
+
+__device__ __forceinline__ void xcd_tile(int r, int ncols, int& row, int& col) {
+  const int x = r % kXcds, rest = r / kXcds;
+  col = rest % ncols;
+  row = (rest / ncols) * kXcds + x;
+}
 
 struct TileIn {
   const uint8_t* a[kNA]; // per lane: packed-tile address (tile_row) of each of the wave's A tiles, stage 0
@@ -499,14 +515,17 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   __shared__ TileLds L;
   __shared__ float samax[kWaves][kTM];
   const int ntI = a.I / kBlk, ntS = a.Is / kBlk;
-  const int n_sh = a.Is > 0 ? ((a.M + kTM - 1) / kTM) * ntS : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntI;
+  const int nrow_sh = a.Is > 0 ? (a.M + kTM - 1) / kTM : 0;
+  const int n_sh = xcd_rows(nrow_sh) * ntS;          // a multiple of 8
+  const int mtiles = a.sched[SCHED_MTILES];
   const int bid = blockIdx.x;
-  if (bid >= total) return;
+  if (bid >= n_sh + xcd_rows(mtiles) * ntI) return;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
   Acc tot;
   if (bid < n_sh) {
-    const int mt = bid / ntS, nt = bid % ntS;
+    int mt, nt;
+    xcd_tile(bid, ntS, mt, nt);
+    if (mt >= nrow_sh) return;
     // the row tile's 16-row groups holding rows, rounded up to 2, 4 or 8
     const int live = (min(kTM, a.M - mt * kTM) + 15) / 16;
     if (live <= 2)
@@ -517,9 +536,10 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
       shared_gateup_tile<kNB>(a, L, mt, nt);
     return;
   }
-  const int rb = bid - n_sh;
-  const int nt = rb % ntI;
-  const Tile tl = routed_tile(a, rb / ntI);
+  int it, nt;
+  xcd_tile(bid - n_sh, ntI, it, nt);
+  if (it >= mtiles) return;
+  const Tile tl = routed_tile(a, it);
   const int n0 = nt * kBlk + 16 * w;
   const int nkb = a.H / kBlk;
   TileIn in;
@@ -656,14 +676,17 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   TileLds& L = *reinterpret_cast<TileLds*>(smem);
   const int ntH = (a.H + kDnCols - 1) / kDnCols;
   const int ntW = (a.H + kDnColsW - 1) / kDnColsW;
-  const int n_sh = a.Is > 0 ? ((a.M + kTM - 1) / kTM) * ntH : 0;
-  const int total = n_sh + a.sched[SCHED_MTILES] * ntW;
+  const int nrow_sh = a.Is > 0 ? (a.M + kTM - 1) / kTM : 0;
+  const int n_sh = xcd_rows(nrow_sh) * ntH;          // a multiple of 8
+  const int mtiles = a.sched[SCHED_MTILES];
   const int bid = blockIdx.x;
-  if (bid >= total) return;
+  if (bid >= n_sh + xcd_rows(mtiles) * ntW) return;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, q = lane >> 4, c = lane & 15;
   Acc tot;
   if (bid < n_sh) {
-    const int mt = bid / ntH, nt = bid % ntH;
+    int mt, nt;
+    xcd_tile(bid, ntH, mt, nt);
+    if (mt >= nrow_sh) return;
     // the row tile's 16-row groups holding rows, rounded up to 2, 4 or 8
     const int live = (min(kTM, a.M - mt * kTM) + 15) / 16;
     if (live <= 2)
@@ -674,9 +697,10 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
       shared_down_tile<kNB>(a, L, mt, nt);
     return;
   }
-  const int rb = bid - n_sh;
-  const int nt = rb % ntW;
-  const Tile tl = routed_tile(a, rb / ntW);
+  int it, nt;
+  xcd_tile(bid - n_sh, ntW, it, nt);
+  if (it >= mtiles) return;
+  const Tile tl = routed_tile(a, it);
   const int n0 = nt * kDnColsW + 16 * kWA * w;
   const int nkb = a.I / kBlk;
   // waves past H compute on in-range rows and store nothing
@@ -709,12 +733,13 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
 }
 
 hipError_t launch_tiled(const FfnArgs& a, long mtiles_max, hipStream_t s) {
-  const long sh_tiles = a.Is > 0 ? (a.M + kTM - 1) / kTM : 0;
-  const long gu = sh_tiles * (a.Is / kBlk) + mtiles_max * (a.I / kBlk);
+  const long sh_tiles = a.Is > 0 ? xcd_rows((a.M + kTM - 1) / kTM) : 0;
+  const long mt8 = xcd_rows((int)mtiles_max);
+  const long gu = sh_tiles * (a.Is / kBlk) + mt8 * (a.I / kBlk);
   MOE_LAUNCH(KID_GATEUP, k_gateup_tiled, dim3((unsigned)gu), dim3(kTileThreads), 0, s, a);
   const long ntH = (a.H + kDnCols - 1) / kDnCols;
   const long ntW = (a.H + kDnColsW - 1) / kDnColsW;
-  const long dn = sh_tiles * ntH + mtiles_max * ntW;
+  const long dn = sh_tiles * ntH + mt8 * ntW;
   MOE_LAUNCH(KID_DOWN, k_down_tiled, dim3((unsigned)dn), dim3(kTileThreads), 0, s, a);
   return hipSuccess;
 }

@@ -302,3 +302,15 @@ def test_layer_static_rejects(lib):
     assert call(8, y=FAKE + 2) == L.MOE_EINVAL
     assert call(8, experts=_experts(layout=L.WEIGHTS_ROW_MAJOR)) == L.MOE_EUNSUPPORTED
     assert call(-1) == L.MOE_EINVAL
+
+
+def test_sum_partials_rejects(lib):
+    P = lambda m, h, n, parts=FAKE, y=FAKE + (1 << 30): lib.moe_sum_partials(m, h, n, parts, None, y, None)
+    assert P(0, 512, 8) == L.MOE_OK
+    assert P(-1, 512, 8) == L.MOE_EINVAL
+    assert P(8, 510, 8) == L.MOE_EINVAL            # H not a multiple of 4
+    assert P(8, 512, 0) == L.MOE_EINVAL
+    assert P(8, 512, 65) == L.MOE_EUNSUPPORTED
+    assert P(8, 512, 8, parts=None) == L.MOE_EINVAL
+    assert P(8, 512, 8, y=FAKE + 1024) == L.MOE_EINVAL   # overlaps parts
+    assert P(L.MAX_ROWS + 1, 512, 8) == L.MOE_EUNSUPPORTED
