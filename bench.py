@@ -559,6 +559,177 @@ def prefill_bench(args, torch, moe, synth, md, d, ev, rt_lib, stream, lib):
     return out
 
 
+def route_ahead_bench(torch, moe, synth, cfg, md, d, reps, rt_lib, stream, n_layers=8, reps_timed=30):
+    """Route-ahead experiment on a chain of span-8 decode layers.
+
+    Residual stream: h_0 = x_0 (the span rows); layer l maps x_l to y_l and
+    h_{l+1} = bf16(h_l + y_l), x_{l+1} = RMSNorm(h_{l+1}) (gamma 1, eps 1e-6),
+    moe_add_rmsnorm.  Layer l has its own router (seeded by l) and takes the
+    weights of replica l mod 4.  The plan for layer l+1 is the union of
+    routing x_l with layer l+1's router (pre-gating, formed on a second
+    stream while layer l runs); its experts' gate/up bytes are then read by
+    moe_prefetch_experts, either while layer l runs ("during") or once layer
+    l is done, beside the residual epilogue and layer l+1's routing chain
+    ("next").  A "perfect" plan (the union layer l+1 really uses, recorded
+    from an earlier pass) bounds what any predictor could gain.  Reported:
+    the plan's coverage / waste / per-row agreement per layer, and the
+    chain's us per layer for each variant against the chain without it."""
+    from sparse_moe_ffn_02_amd import route_ahead as ra
+    M, H = cfg.rows, d.hidden
+    i16 = dict(dtype=torch.int16, device="cuda")
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    routers = [(t16(synth.router_weight(cfg, l)), torch.from_numpy(synth.router_bias(cfg, l)).cuda())
+               for l in range(n_layers)]
+    x0_np, mask_np = synth.activations(cfg)
+    mask = torch.from_numpy(mask_np).cuda()
+    xs = [torch.empty((M, H), **i16) for _ in range(n_layers + 1)]
+    hs = [torch.empty((M, H), **i16) for _ in range(n_layers + 1)]
+    ys = [torch.empty((M, H), **i16) for _ in range(n_layers)]
+    xs[0].copy_(t16(x0_np))
+    hs[0].copy_(xs[0])
+    gamma = torch.full((H,), 0x3F80, **i16)
+    rt = [moe.Routing.empty(md, M) for _ in range(n_layers)]
+    rp = [moe.Routing.empty(md, M) for _ in range(n_layers)]
+    ws, ws_side = moe.workspace(md, M), moe.workspace(md, M)
+    aux = torch.cuda.Stream()
+    exp = lambda l: reps[l % len(reps)]
+    perfect = [None] * n_layers
+
+    def chain(plan=None, when="next", cap=1 << 40, wg=0, serial=False):
+        main = torch.cuda.current_stream()
+        for l in range(n_layers):
+            ahead = plan is not None and l + 1 < n_layers
+            if ahead and not serial:
+                ready = torch.cuda.Event()
+                ready.record(main)
+                aux.wait_event(ready)
+                with torch.cuda.stream(aux):
+                    if plan == "pregate":
+                        r = rp[l + 1]
+                        moe.route(md, xs[l], mask, routers[l + 1][0], routers[l + 1][1], r, ws_side)
+                        src = (r.n_union, r.union_ids)
+                    else:
+                        src = perfect[l + 1]
+                    if when == "during":
+                        moe.prefetch_experts(md, src[0], src[1], exp(l + 1)["experts"], moe.PREFETCH_GATE_UP, cap, wg)
+            moe.layer(md, xs[l], mask, routers[l][0], routers[l][1], exp(l)["experts"], exp(l)["shared"], ys[l],
+                      rt[l], ws)
+            moe.add_rmsnorm(ys[l], mask, hs[l], gamma, 1e-6, hs[l + 1], xs[l + 1])
+            if ahead and serial:
+                src = perfect[l + 1]
+                moe.prefetch_experts(md, src[0], src[1], exp(l + 1)["experts"], moe.PREFETCH_GATE_UP, cap, wg)
+            elif ahead and when == "next":
+                done = torch.cuda.Event()
+                done.record(main)
+                aux.wait_event(done)
+                with torch.cuda.stream(aux):
+                    moe.prefetch_experts(md, src[0], src[1], exp(l + 1)["experts"], moe.PREFETCH_GATE_UP, cap, wg)
+        if plan is not None and not serial:
+            joined = torch.cuda.Event()
+            joined.record(aux)
+            main.wait_event(joined)
+
+    def prefetch_only(cap=1 << 40, wg=0):
+        for l in range(1, n_layers):
+            moe.prefetch_experts(md, perfect[l][0], perfect[l][1], exp(l)["experts"], moe.PREFETCH_GATE_UP, cap, wg)
+
+    def prefetch_twice(cap):
+        for l in range(1, n_layers):
+            for _ in range(2):
+                moe.prefetch_experts(md, perfect[l][0], perfect[l][1], exp(l)["experts"], moe.PREFETCH_GATE_UP, cap,
+                                     0)
+
+    def timed(fn):
+        return graph_chain_us(torch, lambda i: fn(), 1, reps_timed, 5, rt_lib, stream)[0]
+
+    def timed_eager(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = HipEvents(2)
+        rt_lib.hipEventRecord(ev.ev[0], C.c_void_p(stream))
+        for _ in range(reps_timed):
+            fn()
+        rt_lib.hipEventRecord(ev.ev[1], C.c_void_p(stream))
+        torch.cuda.synchronize()
+        us = 1e3 * ev.elapsed_ms(ev.ev[0], ev.ev[1]) / reps_timed
+        ev.close()
+        return us
+
+    chain()
+    torch.cuda.synchronize()
+    ref_out = xs[n_layers].clone()
+    for l in range(n_layers):
+        perfect[l] = (rt[l].n_union.clone(), rt[l].union_ids.clone())
+    unions = [ra.union_of(rt[l].topk_ids.cpu().numpy(), mask_np) for l in range(n_layers)]
+    chain("pregate")
+    torch.cuda.synchronize()
+    same = bool(torch.equal(xs[n_layers], ref_out))
+    per_layer = []
+    for l in range(1, n_layers):
+        planned = ra.union_of(rp[l].topk_ids.cpu().numpy(), mask_np)
+        per_layer.append({"layer": l, "union": len(unions[l]), "planned": len(planned),
+                          "coverage": round(ra.coverage(planned, unions[l]), 4),
+                          "waste": round(ra.waste(planned, unions[l]), 4),
+                          "row_agreement": round(ra.row_agreement(rp[l].topk_ids.cpu().numpy(),
+                                                                  rt[l].topk_ids.cpu().numpy(), mask_np), 4)})
+    base = timed(chain) / n_layers
+    gu_expert = 2 * d.inter * d.hidden
+    base_eager = timed_eager(chain) / n_layers
+    variants = []
+    for mode, tfn, b in (("graph", timed, base), ("eager", timed_eager, base_eager)):
+        for plan in ("pregate", "perfect"):
+            for when in ("during", "next"):
+                for cap_mb in (64, 128, 256):
+                    for wg in (256, 1024):
+                        us = tfn(lambda: chain(plan, when, cap_mb << 20, wg)) / n_layers
+                        variants.append({"launch": mode, "plan": plan, "when": when, "cap_mb": cap_mb,
+                                         "workgroups": wg, "us_per_layer": round(us, 2),
+                                         "saved_us_per_layer": round(b - us, 2)})
+                        log(f"[bench] route-ahead {mode} {plan}/{when} cap {cap_mb} MB wg {wg}: {us:.1f} us/layer "
+                            f"(without: {b:.1f})")
+    # the cache effect alone: a prefetch serialized right before the layer it serves, against the
+    # chain plus the prefetches timed on their own; and a second read of the same bytes right after
+    # the first, against the first (per prefetched layer)
+    pf_bytes = sum(len(unions[l]) * gu_expert for l in range(1, n_layers)) / (n_layers - 1)
+    per_pf = n_layers / (n_layers - 1)
+    serial_rows, reread_rows = [], []
+    for cap_mb in (32, 64, 128, 192, 1 << 20):
+        cap = cap_mb << 20
+        serial = timed(lambda: chain("perfect", cap=cap, serial=True)) / n_layers
+        alone = timed(lambda: prefetch_only(cap)) / n_layers * per_pf
+        twice = timed(lambda: prefetch_twice(cap)) / n_layers * per_pf
+        nbytes = float(np.mean([min(len(unions[l]) * gu_expert, cap) for l in range(1, n_layers)]))
+        gain = (base * n_layers + alone * (n_layers - 1) - serial * n_layers) / (n_layers - 1)
+        label = "all" if cap_mb >= 1 << 20 else cap_mb
+        serial_rows.append({"cap_mb": label, "bytes_per_layer": int(nbytes), "prefetch_alone_us": round(alone, 2),
+                            "serial_us_per_layer": round(serial, 2), "warm_layer_gain_us": round(gain, 2)})
+        reread_rows.append({"cap_mb": label, "first_read_gbs": round(nbytes / (alone * 1e-6) / 1e9, 1),
+                            "second_read_gbs": round(nbytes / max(twice - alone, 1e-3) / 1e3, 1)})
+        log(f"[bench] route-ahead serial cap {label} MB: prefetch {alone:.1f} us ({nbytes / 1e6:.0f} MB), "
+            f"layer gain when warm {gain:.1f} us; re-read {reread_rows[-1]['second_read_gbs']:.0f} GB/s vs first "
+            f"{reread_rows[-1]['first_read_gbs']:.0f} GB/s")
+    wide = timed(lambda: prefetch_only(1 << 40, 1024)) / n_layers * per_pf
+    log(f"[bench] route-ahead: coverage {np.mean([p['coverage'] for p in per_layer]):.3f}")
+    del ws, ws_side
+    return {"workload": f"{n_layers} chained span-8 decode layers (own router per layer, weights of replica l mod "
+                        f"{len(reps)}), residual stream h_(l+1) = h_l + y_l, x_(l+1) = RMSNorm(h_(l+1)); plan for "
+                        "layer l+1 = union of x_l routed by layer l+1's router (pre-gating), gate/up bytes prefetched",
+            "chain_outputs_identical": same,
+            "plan_quality": per_layer,
+            "mean_coverage": round(float(np.mean([p["coverage"] for p in per_layer])), 4),
+            "mean_waste": round(float(np.mean([p["waste"] for p in per_layer])), 4),
+            "us_per_layer_without": round(base, 2),
+            "us_per_layer_without_eager": round(base_eager, 2),
+            "variants": variants,
+            "serial_perfect": serial_rows,
+            "reread": reread_rows,
+            "union_gate_up_bytes_per_layer": int(pf_bytes),
+            "prefetch_all_1024_workgroups_us": round(wide, 2),
+            "timing": "us per layer: hipGraph replay of the whole chain (both streams captured), and eager "
+                      "launches on two streams (the side stream joined at the end of each chain)"}
+
+
 def cpu_oracle_baseline(synth, cfg, x_np, mask_np, nu, total_b, M, union):
     """The CPU oracle, as it stands, on the span-8 step (the JSON line's
     baseline, on every host core the process may use), and its wall time on
@@ -618,6 +789,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweeps", action="store_true",
                     help="skip the row-count and TP8-rank sweeps and the DP8 and 512-token legs")
+    ap.add_argument("--route-ahead-only", action="store_true", help="only the span-8 step and the route-ahead leg")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -793,6 +965,14 @@ def main():
                              "unfused_us": round(us_unf, 2), "fused_us": round(us_fus, 2),
                              "layer_only_us": round(us_step, 2),
                              "timing": "hipGraph replay, weights rotated as above"}
+
+    # ---------------- route-ahead prefetch of the next layer's predicted union
+    if args.route_ahead_only or not args.no_sweeps:
+        result["route_ahead"] = route_ahead_bench(torch, moe, synth, cfg, md, d, reps, rt_lib, stream)
+    if args.route_ahead_only:
+        ev.close()
+        print(json.dumps(result), flush=True)
+        return
 
     # ---------------- the other decode and chunk workloads on the same layer
     if not args.no_sweeps:

@@ -242,6 +242,34 @@ int moe_layer_add_rmsnorm(const moe_dims* dims, int32_t M, const uint16_t* x, co
 int moe_sum_partials(int32_t M, int32_t H, int32_t nsrc, const uint16_t* parts, const uint8_t* row_mask, uint16_t* y,
                      void* stream);
 
+/* Route-ahead prefetch (MoE-Infinity PR #140, route-ahead expert prefetch
+ * commit: the per-token union of the routed experts of a coming block is
+ * fetched ahead of use while other work runs).  With every expert resident in
+ * HBM, what is fetched ahead is the experts' packed weight bytes, read once so
+ * that they pass into the memory-side Infinity Cache for a later layer call.
+ * Reads, for u = 0 .. *n_union - 1 in order, the matrices of expert
+ * union_ids[u] selected by parts (MOE_PREFETCH_GATE_UP: w_gate then w_up;
+ * MOE_PREFETCH_DOWN: w_down; gate/up first when both), each in address
+ * order, stopping after max_bytes rounded down to whole 16 KiB chunks
+ * (max_bytes 0: nothing is launched).  n_union and union_ids are device
+ * buffers in moe_routing's layout (e.g. the fields of a moe_route result):
+ * n_union is read on the device and clamped to [0, E]; entries outside
+ * [0, E) are skipped.  Scales are not read.  checksum (device, optional):
+ * the wrapping 32-bit sum of every little-endian 32-bit word read is added
+ * to *checksum (the caller clears it first); NULL: nothing is written.
+ * workgroups: grid size, 0 = 256 (one per compute unit); fewer leave more of
+ * the chip to kernels running beside it on other streams.  The call has no
+ * effect on any result of the library.  Errors: MOE_EINVAL for bad dims,
+ * weights (as moe_layer), null or misaligned n_union / union_ids, parts 0 or
+ * with unknown bits, negative max_bytes or workgroups; MOE_EUNSUPPORTED for
+ * workgroups above MOE_PREFETCH_MAX_WORKGROUPS. */
+#define MOE_PREFETCH_GATE_UP 1u
+#define MOE_PREFETCH_DOWN 2u
+#define MOE_PREFETCH_MAX_WORKGROUPS 4096
+int moe_prefetch_experts(const moe_dims* dims, const int32_t* n_union, const int32_t* union_ids,
+                         const moe_expert_w* experts, uint32_t parts, int64_t max_bytes, int32_t workgroups,
+                         uint32_t* checksum, void* stream);
+
 /* The 1x128 activation quantization step on its own (mstar PR #388,
  * FlashInfer crossover note): rows x cols values (fp32 if is_bf16 == 0, else
  * bf16 bits) -> e4m3 codes [rows, cols] and fp32 scales [rows, cols/128].

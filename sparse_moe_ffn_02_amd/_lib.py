@@ -66,7 +66,7 @@ class CTaps(C.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_ffn_fp8", "moe_layer", "moe_layer_static", "moe_quant_fp8",
-           "moe_pack_weights", "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_sum_partials", "moe_trace_set",
+           "moe_pack_weights", "moe_add_rmsnorm", "moe_layer_add_rmsnorm", "moe_sum_partials", "moe_prefetch_experts", "moe_trace_set",
            "moe_kernel_name", "moe_status_str")
 STATIC_WS_BYTES = 64 << 20       # MOE_STATIC_WS_BYTES: the static workspace of moe_layer_static
 
@@ -94,6 +94,8 @@ def load() -> C.CDLL:
                                      C.POINTER(CShared), P, C.POINTER(CRouting), C.POINTER(CTaps), P]
     lib.moe_add_rmsnorm.argtypes = [C.c_int32, C.c_int32, P, P, P, P, C.c_float, P, P, P]
     lib.moe_sum_partials.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
+    lib.moe_prefetch_experts.argtypes = [C.POINTER(CDims), P, P, C.POINTER(CExperts), C.c_uint32, C.c_int64,
+                                         C.c_int32, P, P]
     lib.moe_layer_add_rmsnorm.argtypes = [C.POINTER(CDims), C.c_int32, P, P, C.POINTER(CRouter),
                                           C.POINTER(CExperts), C.POINTER(CShared), P, P, C.c_float, P, P, P,
                                           C.POINTER(CRouting), C.POINTER(CTaps), P, C.c_size_t, P]
@@ -303,6 +305,22 @@ def sum_partials(parts: torch.Tensor, row_mask: Optional[torch.Tensor], y: torch
     ascending source order, one bf16 rounding."""
     m, nsrc, h = parts.shape
     _check(load().moe_sum_partials(m, h, nsrc, _ptr(parts), _ptr(row_mask), _ptr(y), _stream()))
+
+
+PREFETCH_GATE_UP = 1     # MOE_PREFETCH_GATE_UP
+PREFETCH_DOWN = 2        # MOE_PREFETCH_DOWN
+
+
+def prefetch_experts(dims: Dims, n_union: torch.Tensor, union_ids: torch.Tensor, experts: Experts, parts: int,
+                     max_bytes: int, workgroups: int = 0, checksum: Optional[torch.Tensor] = None) -> None:
+    """moe_prefetch_experts: read the listed experts' packed matrices (the
+    first *n_union entries of union_ids, device int32) ahead of use; checksum
+    (int32 [1], cleared by the caller) receives the 32-bit word sum of the
+    bytes read."""
+    d = dims.c()
+    ew = experts.c()
+    _check(load().moe_prefetch_experts(C.byref(d), _ptr(n_union), _ptr(union_ids), C.byref(ew), parts, max_bytes,
+                                       workgroups, _ptr(checksum), _stream()))
 
 
 def pack_weights(src: torch.Tensor, dst: torch.Tensor, is_bf16: bool) -> None:

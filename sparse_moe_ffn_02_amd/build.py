@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
-SOURCES = ["route.hip", "ffn.hip", "tiled.hip", "api.hip"]
+SOURCES = ["route.hip", "ffn.hip", "tiled.hip", "prefetch.hip", "api.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -204,7 +204,7 @@ thread_local Tracer g_trace;
 const char* const kKernelNames[KID_COUNT] = {
     "router_logits", "route_select", "union", "quant_x", "plan", "gateup", "post_gateup",
     "down", "combine", "quant", "select_union", "front", "pack", "combine_norm", "add_rmsnorm",
-    "sum_partials",
+    "sum_partials", "prefetch",
 };
 
 }  // namespace
@@ -441,6 +441,30 @@ int moe_sum_partials(int32_t M, int32_t H, int32_t nsrc, const uint16_t* parts, 
   if (M > 0 && a < b + nb && b < a + na) return MOE_EINVAL;     // overlapping buffers
   if (M == 0) return MOE_OK;
   return to_status(launch_sum_partials(parts, row_mask, M, H, nsrc, y, static_cast<hipStream_t>(stream)));
+}
+
+int moe_prefetch_experts(const moe_dims* dims, const int32_t* n_union, const int32_t* union_ids,
+                         const moe_expert_w* experts, uint32_t parts, int64_t max_bytes, int32_t workgroups,
+                         uint32_t* checksum, void* stream) {
+  int st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if ((st = check_experts(experts)) != MOE_OK) return st;
+  if (!ok_ptr(n_union, 4) || !ok_ptr(union_ids, 4) || !ok_opt(checksum, 4)) return MOE_EINVAL;
+  if (parts == 0 || (parts & ~(MOE_PREFETCH_GATE_UP | MOE_PREFETCH_DOWN)) != 0) return MOE_EINVAL;
+  if (max_bytes < 0 || workgroups < 0) return MOE_EINVAL;
+  if (workgroups > MOE_PREFETCH_MAX_WORKGROUPS) return MOE_EUNSUPPORTED;
+  const uint8_t* mats[3];
+  int nmat = 0;
+  if (parts & MOE_PREFETCH_GATE_UP) {
+    mats[nmat++] = experts->w_gate;
+    mats[nmat++] = experts->w_up;
+  }
+  if (parts & MOE_PREFETCH_DOWN) mats[nmat++] = experts->w_down;
+  const long mat_bytes = (long)dims->inter * dims->hidden;
+  const long max_chunks = (long)(max_bytes / prefetch_chunk_bytes());
+  if (max_chunks == 0) return MOE_OK;
+  return to_status(launch_prefetch(n_union, union_ids, dims->n_experts, mats, nmat, mat_bytes, max_chunks,
+                                   workgroups ? workgroups : 256, checksum, static_cast<hipStream_t>(stream)));
 }
 
 int moe_quant_fp8(const void* in, int32_t is_bf16, int32_t rows, int32_t cols, uint8_t* codes, float* scales,

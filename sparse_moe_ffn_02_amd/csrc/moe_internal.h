@@ -102,7 +102,7 @@ struct NormArgs {
 enum KernelId {
   KID_ROUTER_LOGITS = 0, KID_ROUTE_SELECT, KID_UNION, KID_QUANT_X, KID_PLAN, KID_GATEUP, KID_POST_GATEUP,
   KID_DOWN, KID_COMBINE, KID_QUANT, KID_ROUTE_SMALL, KID_FRONT, KID_PACK, KID_COMBINE_NORM, KID_ADD_NORM,
-  KID_SUM_PARTIALS, KID_COUNT
+  KID_SUM_PARTIALS, KID_PREFETCH, KID_COUNT
 };
 
 void trace_before(hipStream_t s);
@@ -134,6 +134,14 @@ bool use_split(int M, int H, int I);   // M <= split_rows(I)
 hipError_t launch_pack(const void* src, void* dst, long rows, int row_bytes, int is_bf16, hipStream_t s);
 hipError_t launch_sum_partials(const uint16_t* parts, const uint8_t* mask, int M, int H, int nsrc, uint16_t* y,
                                hipStream_t s);
+// Route-ahead prefetch: read the packed matrices mats[0..nmat) (each [E] x
+// mat_bytes) of the experts union_ids[0 .. *n_union) in union order, at most
+// max_chunks chunks of prefetch_chunk_bytes(); checksum (optional) += the
+// 32-bit word sum of every byte read.
+long prefetch_chunk_bytes();
+hipError_t launch_prefetch(const int32_t* n_union, const int32_t* union_ids, int E, const uint8_t* const* mats,
+                           int nmat, long mat_bytes, long max_chunks, int workgroups, uint32_t* checksum,
+                           hipStream_t s);
 hipError_t launch_quant_generic(const void* in, int is_bf16, int R, int C, uint8_t* codes, float* scales,
                                 hipStream_t s);
 

@@ -314,3 +314,28 @@ def test_sum_partials_rejects(lib):
     assert P(8, 512, 8, parts=None) == L.MOE_EINVAL
     assert P(8, 512, 8, y=FAKE + 1024) == L.MOE_EINVAL   # overlaps parts
     assert P(L.MAX_ROWS + 1, 512, 8) == L.MOE_EUNSUPPORTED
+
+
+def test_prefetch_rejects(lib):
+    """Every refusal returns before a launch; a cap under one 16 KiB chunk is
+    a valid call that launches nothing (so fake addresses stay unread)."""
+    def P(*, d=None, n=FAKE, ids=FAKE, experts=None, parts=1, max_bytes=16383, wg=0, cs=None):
+        dd = d or _dims()
+        ew = experts or _experts()
+        return lib.moe_prefetch_experts(C.byref(dd), n, ids, C.byref(ew), parts, max_bytes, wg, cs, None)
+    assert P() == L.MOE_OK
+    assert P(max_bytes=0, parts=3, cs=FAKE) == L.MOE_OK
+    assert P(d=_dims(hidden=6100)) == L.MOE_EINVAL
+    assert P(n=None) == L.MOE_EINVAL
+    assert P(ids=None) == L.MOE_EINVAL
+    assert P(ids=FAKE + 2) == L.MOE_EINVAL          # misaligned
+    assert P(cs=FAKE + 1) == L.MOE_EINVAL
+    assert P(parts=0) == L.MOE_EINVAL
+    assert P(parts=4) == L.MOE_EINVAL
+    assert P(parts=7) == L.MOE_EINVAL
+    assert P(max_bytes=-1) == L.MOE_EINVAL
+    assert P(wg=-1) == L.MOE_EINVAL
+    assert P(wg=4097) == L.MOE_EUNSUPPORTED
+    assert P(experts=_experts(layout=L.WEIGHTS_ROW_MAJOR)) == L.MOE_EUNSUPPORTED
+    assert P(experts=_experts(layout=7)) == L.MOE_EINVAL
+    assert P(experts=_experts(s_down=None)) == L.MOE_EINVAL

@@ -14,6 +14,7 @@ import torch
 import oracle
 import sparse_moe_ffn_02_amd as moe
 import synth
+from prefetch_util import expected_checksum, prefetch_checksum
 from gpu_util import (GpuLayer, assert_routing_equal, assert_y_close, compare_h_codes, cover_rows, np16,
                       rescale_rows, run_layer, run_oracle, say, t16)
 
@@ -47,6 +48,25 @@ def test_span8_decode_step():
     bad, n = compare_h_codes(g["h_codes"], g["h_scales"], o, gl)
     err = assert_y_close(g["y"], o)
     say(f"span8: |U|={g['n_union']}, max row rel err {err:.3e}, h flips {bad}/{n}")
+
+
+def test_span8_route_ahead_prefetch_reads_the_union():
+    """At full size, in the grid the benchmark uses: the prefetch of a routed
+    span-8 union reads exactly those experts' packed gate/up (and down)
+    bytes, capped as asked, checked through its word-sum checksum."""
+    cfg, gl = glm_layer("span8")
+    x, mask = synth.activations(cfg)
+    d = gl.dims
+    rt = moe.Routing.empty(d, cfg.rows)
+    moe.route(d, t16(x), torch.from_numpy(mask).cuda(), gl.router_w, gl.bias, rt, moe.workspace(d, cfg.rows))
+    torch.cuda.synchronize()
+    ids = [int(e) for e in rt.union_ids[:int(rt.n_union.item())].cpu()]
+    say(f"span8 prefetch: |U|={len(ids)}")
+    both = moe.PREFETCH_GATE_UP | moe.PREFETCH_DOWN
+    for parts, cap, wg in ((moe.PREFETCH_GATE_UP, 1 << 40, 256), (moe.PREFETCH_GATE_UP, 128 << 20, 64),
+                           (both, 300 << 20, 0)):
+        got = prefetch_checksum(d, rt.n_union, rt.union_ids, gl.experts, parts, cap, wg)
+        assert got == expected_checksum(gl.experts, ids, parts, cap, d.n_experts), (parts, cap, wg)
 
 
 def test_dp8_decode_step_pads_and_placement():
