@@ -122,35 +122,28 @@ __device__ __forceinline__ void topk_rounds(const double (&c)[4], bool (&ok)[4],
   }
 }
 
-__device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_bits) {
+// A pad row: ids -1, weights 0, slot_of -1, an empty expert bitmask.
+__device__ void select_pad(const RouteArgs& a, int row, int lane, uint32_t* lds_bits) {
   const int nwords = (a.E + 31) / 32;
-  const bool real = (a.mask == nullptr || a.mask[row] != 0);
-  if (!real) {
-    if (lane < a.K) {
-      a.ids[(size_t)row * a.K + lane] = -1;
-      a.w[(size_t)row * a.K + lane] = 0.0f;
-      a.slot_of[(size_t)row * a.K + lane] = -1;
-    }
-    if (lane < nwords) {
-      a.rowbits[(size_t)row * nwords + lane] = 0u;
-      if (lds_bits) lds_bits[lane] = 0u;
-    }
-    return;
+  if (lane < a.K) {
+    a.ids[(size_t)row * a.K + lane] = -1;
+    a.w[(size_t)row * a.K + lane] = 0.0f;
+    a.slot_of[(size_t)row * a.K + lane] = -1;
   }
-  double c[4], sg[4];
-  bool ok[4], picked[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    ok[q] = e < a.E;
-    picked[q] = false;
-    c[q] = -INFINITY;
-    sg[q] = 0.0;
-    if (ok[q]) {
-      const double l = a.logits[(size_t)row * a.E + e];
-      route_score(l, a.bias[e], sg[q], c[q]);
-    }
+  if (lane < nwords) {
+    a.rowbits[(size_t)row * nwords + lane] = 0u;
+    if (lds_bits) lds_bits[lane] = 0u;
   }
+}
+
+// The selection of a real row from its scores: c (biased score) and sg
+// (sigmoid of the logit) of expert lane + 64 q, ok[q] = expert q may be
+// picked.  The k largest c among the ok experts win (ties to the lower id);
+// ids ascending, weights scale * sg / sum(sg) summed in ascending id order.
+__device__ void select_scored(const RouteArgs& a, int row, int lane, const double (&c)[4], const double (&sg)[4],
+                              bool (&ok)[4], uint32_t* lds_bits) {
+  const int nwords = (a.E + 31) / 32;
+  bool picked[4] = {false, false, false, false};
   topk_rounds(c, ok, picked, a.K, lane);
   // Ascending id order: id = lane + 64 q, so positions follow q, then lane.
   // Each pick is pushed to lane `position` (ds_permute); lane 63 is never a
@@ -192,11 +185,395 @@ __device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_
   }
 }
 
+__device__ void select_row(const RouteArgs& a, int row, int lane, uint32_t* lds_bits) {
+  if (!(a.mask == nullptr || a.mask[row] != 0)) {
+    select_pad(a, row, lane, lds_bits);
+    return;
+  }
+  double c[4], sg[4];
+  bool ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    ok[q] = e < a.E;
+    c[q] = -INFINITY;
+    sg[q] = 0.0;
+    if (ok[q]) {
+      const double l = a.logits[(size_t)row * a.E + e];
+      route_score(l, a.bias[e], sg[q], c[q]);
+    }
+  }
+  select_scored(a, row, lane, c, sg, ok, lds_bits);
+}
+
 __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= a.M) return;
   select_row(a, row, lane, nullptr);
+}
+
+// ---------------------------------------------------------------- certified selection
+// Larger steps (mstar PR #388 router notes: only the top-k decision and the
+// picked experts' sigmoids leave the router).  The float64 logit is needed
+// only where it can change the decision, so the selection is certified:
+//
+// 1. bf16 MFMA (fp32 accumulation) gives an estimate L of every logit and
+//    S = sum |x_h| |w_h| (the same MFMA on the operands' magnitudes).  bf16
+//    products are exact in fp32; any order of fp32 additions with faithful
+//    rounding (error at most 2u per addition, twice round-to-nearest's)
+//    leaves |L - sum x_h w_h| <= gamma S with gamma = 2 n u / (1 - 2 n u),
+//    u = 2^-24, n <= H + 1 additions (the K halves are added at the end).
+//    The certified path runs for H <= kCertMaxH = 8192, where
+//    gamma <= 2^-10 (1 + 2^-9); the computed S is at least S / (1 + gamma).
+//    So Delta = S (2^-10 (1 + 2^-8) + 2^-30) + 2^-100 covers the estimate,
+//    the float64 procedure's own rounding (2^-30 S) and products below
+//    fp32's normal range (2^-100).
+// 2. c is non-decreasing in l, so each expert's score lies between the
+//    float32 scores of L - Delta and L + Delta (float32 sigmoid, within
+//    2^-22 of the float64 one), widened by 2^-19.  T = the k-th largest lower
+//    end; an expert whose upper end is below T has k experts strictly above
+//    it and cannot be picked.  The others are the candidates (at least k).
+// 3. The candidates' logits are computed by the fixed float64 procedure of
+//    k_router_logits (same bits), and the selection runs on them alone.
+//    A row with a non-finite L or S takes every expert as a candidate.
+// The ids and weights are therefore those of a float64 logit for every
+// expert; only the number of float64 dot products changes.
+//
+// Two kernels: k_route_est writes L and S for 64-row x 64-expert tiles, the
+// two halves of K in separate workgroups (K half 0 into the logit
+// workspace, half 1 into the sigmoid workspace, each as float L [M, E] then
+// float S [M, E]); k_route_cert adds the halves, certifies and selects one
+// row per wave.
+constexpr int kEstRows = 64;
+constexpr int kEstExperts = 64;
+constexpr int kEstK = 128;          // K per staged chunk
+constexpr int kCertGroup = 4;       // candidate logits per pass over the row
+constexpr int kCertMaxH = 8192;
+
+__device__ __forceinline__ double cert_delta(float S) {
+  return (double)S * (0x1p-10 * (1.0 + 0x1p-8) + 0x1p-30) + 0x1p-100;
+}
+
+// LDS slot of 16-byte column c (0..15) of tile row r: columns are rotated
+// by the row so that the 16 rows an MFMA operand read touches, at one
+// column, fall in 16 different bank groups.
+__device__ __forceinline__ int est_slot(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+
+// Workgroup (row tile, expert tile): 4 waves, wave w owns rows 16 w .. 16 w + 15
+// of the tile against all 64 experts (4 MFMA column blocks, L and S each).
+// Operand chunks of 128 K are staged through LDS (two buffers); global loads
+// run three chunks ahead in registers, so several chunks' round trips
+// overlap.
+
+// one chunk's operand pieces of a thread: 4 of x, then 4 of the router weight
+struct EstStage {
+  v4i p[8];
+};
+
+// Loads past the last chunk re-read the last chunk (never staged): every
+// load is issued unconditionally, so the compiler's wait counts can leave the
+// newer chunks in flight while an older one is staged.
+__device__ __forceinline__ void est_load(EstStage& r, const uint16_t* const (&xs)[4], const uint16_t* const (&ws)[4],
+                                         int ch, int nch) {
+  const int c = min(ch, nch - 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.p[j] = *reinterpret_cast<const v4i*>(xs[j] + c * kEstK);
+    r.p[4 + j] = *reinterpret_cast<const v4i*>(ws[j] + c * kEstK);
+  }
+}
+
+__device__ __forceinline__ void est_stage(const EstStage& r, v4i* sx, v4i* sw, const int (&slot)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sx[slot[j]] = r.p[j];
+    sw[slot[j]] = r.p[4 + j];
+  }
+}
+
+__device__ __forceinline__ void est_chunk(const v4i* sx, const v4i* sw, int ar, int kc, int lane, v4f (&accL)[4],
+                                          v4f (&accS)[4]) {
+  const v4i mag = {0x7FFF7FFF, 0x7FFF7FFF, 0x7FFF7FFF, 0x7FFF7FFF};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const v4i xa = sx[est_slot(ar, 4 * st + kc)];
+    const v4i xm = xa & mag;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const v4i wb = sw[est_slot(16 * b + (lane & 15), 4 * st + kc)];
+      accL[b] = mfma_bf16_k32(xa, wb, accL[b]);
+      accS[b] = mfma_bf16_k32(xm, wb & mag, accS[b]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_est(RouteArgs a) {
+  __shared__ v4i sx[2][kEstRows * 16];
+  __shared__ v4i sw[2][kEstExperts * 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  // jobs j = (K half, row tile); the expert tiles of one job take workgroup
+  // indices of one residue mod 8, so they run on one XCD and share its L2
+  // for the x rows (workgroup b runs on XCD b % 8)
+  const int nte = (a.E + kEstExperts - 1) / kEstExperts;
+  const int nrt = (a.M + kEstRows - 1) / kEstRows;
+  const int rest = blockIdx.x >> 3;
+  const int job = 8 * (rest / nte) + (int)(blockIdx.x & 7);
+  if (job >= 2 * nrt) return;
+  const int half = job / nrt;                                // K half
+  if (half == 1 && a.H / kEstK < 2) return;
+  const int r0 = (job - half * nrt) * kEstRows;
+  const int e0 = (rest % nte) * kEstExperts;
+  const int nall = a.H / kEstK;
+  const int cb = half == 0 ? 0 : (nall + 1) / 2;            // first chunk of this half
+  const int nch = (nall >= 2 ? (half == 0 ? (nall + 1) / 2 : nall / 2) : nall);
+  // staging: thread t moves 16-byte pieces i = t + 256 j (j < 4) of each
+  // operand: tile row i / 16, column i % 16 (rows past M read row M - 1 and
+  // experts past E read expert E - 1; their results are never stored)
+  const uint16_t* xsrc[4];
+  const uint16_t* wsrc[4];
+  int slot[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int r = i >> 4, c = i & 15;
+    xsrc[j] = a.x + (size_t)min(r0 + r, a.M - 1) * a.H + cb * kEstK + 8 * c;
+    wsrc[j] = a.wr + (size_t)min(e0 + r, a.E - 1) * a.H + cb * kEstK + 8 * c;
+    slot[j] = est_slot(r, c);
+  }
+  // chunk c travels in stage c % 3 (three named register sets, so that no
+  // set is ever indexed at run time)
+  EstStage q0, q1, q2;
+  est_load(q0, xsrc, wsrc, 0, nch);
+  est_load(q1, xsrc, wsrc, 1, nch);
+  est_load(q2, xsrc, wsrc, 2, nch);
+  est_stage(q0, sx[0], sw[0], slot);
+  est_load(q0, xsrc, wsrc, 3, nch);
+  __syncthreads();
+  v4f accL[4], accS[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    accL[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    accS[b] = accL[b];
+  }
+  const int ar = 16 * wave + (lane & 15);      // A row of this lane in the tile
+  const int kc = lane >> 4;                    // 8-element K column within a 32-step
+  // chunk ch: multiply the staged buffer, stage chunk ch + 1 (held in NXT),
+  // refill NXT with chunk ch + 4.  In the main loop every step runs whole,
+  // with no branch around its loads (so the compiler's wait counts leave two
+  // chunks in flight); staging past the last chunk writes the buffer nobody
+  // reads any more.  The last nch % 3 chunks take guarded steps.
+#define MOE_EST_STEP(ch, NXT)                                                  \
+  est_chunk(sx[(ch) & 1], sw[(ch) & 1], ar, kc, lane, accL, accS);             \
+  est_stage(NXT, sx[((ch) + 1) & 1], sw[((ch) + 1) & 1], slot);                \
+  est_load(NXT, xsrc, wsrc, (ch) + 4, nch);                                    \
+  __syncthreads();
+  const int nmain = nch - nch % 3;
+  for (int c0 = 0; c0 < nmain; c0 += 3) {
+    MOE_EST_STEP(c0, q1)
+    MOE_EST_STEP(c0 + 1, q2)
+    MOE_EST_STEP(c0 + 2, q0)
+  }
+  if (nmain < nch) {
+    MOE_EST_STEP(nmain, q1)
+  }
+  if (nmain + 1 < nch) {
+    MOE_EST_STEP(nmain + 1, q2)
+  }
+#undef MOE_EST_STEP
+  float* estL = reinterpret_cast<float*>(half == 0 ? a.logits : a.sig);
+  float* estS = estL + (size_t)a.M * a.E;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const v4f l = settle_bf16(accL[b]);
+    const v4f sm = settle_bf16(accS[b]);
+    const int e = e0 + 16 * b + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + 16 * wave + 4 * (lane >> 4) + i;
+      if (r < a.M && e < a.E) {
+        estL[(size_t)r * a.E + e] = l[i];
+        estS[(size_t)r * a.E + e] = sm[i];
+      }
+    }
+  }
+}
+
+// id of the p-th set bit over the four 64-bit masks (q-major), or -1
+__device__ __forceinline__ int nth_candidate(const uint64_t (&m)[4], int p) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = __popcll(m[q]);
+    if (p < c) {
+      uint64_t b = m[q];
+      for (int i = 0; i < p; ++i) b &= b - 1ull;
+      return 64 * q + __ffsll((long long)b) - 1;
+    }
+    p -= c;
+  }
+  return -1;
+}
+
+// The k-th largest of v over the ok entries (expert lane + 64 q), counted
+// with multiplicity: k rounds of a wave maximum, each removing one holder.
+__device__ __forceinline__ float kth_largest(const float (&v)[4], const bool (&ok)[4], int k, int lane) {
+  bool left[4] = {ok[0], ok[1], ok[2], ok[3]};
+  float m = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (left[q]) mm = fmaxf(mm, v[q]);
+    m = wave_max(mm);
+    bool done = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t b = __ballot(left[q] && v[q] == m);
+      if (!done && b != 0ull) {
+        if (lane == __ffsll((long long)b) - 1) left[q] = false;
+        done = true;
+      }
+    }
+  }
+  return m;
+}
+
+// One wave per row: the score intervals from L and S, the threshold, the
+// candidates' float64 logits, then the selection over the candidates.  The
+// row x is parked in LDS (each lane keeps the 16-byte pieces it reads back,
+// so no wave sync is needed); the candidates' weight chunks are loaded three
+// chunks ahead, every load unconditional (clamped addresses) so that the
+// compiler's wait counts keep the next chunks in flight.
+__device__ __forceinline__ void cert_wload(uint4 (&w)[kCertGroup], const uint16_t* const (&wrow)[kCertGroup], int i,
+                                           int lane, int H) {
+  const int h = min(512 * i + 8 * lane, H - 8);
+#pragma unroll
+  for (int j = 0; j < kCertGroup; ++j) w[j] = *reinterpret_cast<const uint4*>(wrow[j] + h);
+}
+
+__device__ __forceinline__ void cert_chunk(double (&acc)[kCertGroup], const uint4 (&w)[kCertGroup], const uint4* sxr,
+                                           int i, int lane, int H, int ng) {
+  if (512 * i + 8 * lane >= H) return;
+  const uint4 xv = sxr[64 * i + lane];
+  double xd[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) xd[t] = (double)bf16_to_f32(u16_of(xv, t));
+#pragma unroll
+  for (int j = 0; j < kCertGroup; ++j) {
+    if (j >= ng) break;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[j] = __builtin_fma(xd[t], (double)bf16_to_f32(u16_of(w[j], t)), acc[j]);
+  }
+}
+
+__global__ __launch_bounds__(256, 3) void k_route_cert(RouteArgs a) {
+  extern __shared__ uint4 cert_x[];          // [4 waves][H / 8]
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= a.M) return;
+  if (!(a.mask == nullptr || a.mask[row] != 0)) {
+    select_pad(a, row, lane, nullptr);
+    return;
+  }
+  const int nch = (a.H + 511) / 512;
+  uint4* sxr = cert_x + (size_t)wave * (a.H / 8);
+  {
+    // all chunks of the row in one round trip (addresses clamped into the row)
+    constexpr int kMaxCh = kCertMaxH / 512;
+    const uint16_t* xrow = a.x + (size_t)row * a.H;
+    uint4 xv[kMaxCh];
+#pragma unroll
+    for (int i = 0; i < kMaxCh; ++i)
+      xv[i] = *reinterpret_cast<const uint4*>(xrow + min(512 * i + 8 * lane, a.H - 8));
+#pragma unroll
+    for (int i = 0; i < kMaxCh; ++i)
+      if (512 * i + 8 * lane < a.H) sxr[64 * i + lane] = xv[i];
+  }
+  const float* estL = reinterpret_cast<const float*>(a.logits) + (size_t)row * a.E;
+  const float* estS = estL + (size_t)a.M * a.E;
+  const bool halves = a.H / kEstK >= 2;
+  const float* estL1 = reinterpret_cast<const float*>(a.sig) + (size_t)row * a.E;
+  const float* estS1 = estL1 + (size_t)a.M * a.E;
+  // score bounds in float32: v = L -+ Delta rounded outward, sigmoid in
+  // float32 (within 2^-22 of the float64 sigmoid), the bias added, and the
+  // result widened by 2^-19 and rounded outward
+  float lo[4], hi[4];
+  bool ok[4];
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    ok[q] = e < a.E;
+    lo[q] = -INFINITY;
+    hi[q] = -INFINITY;
+    if (ok[q]) {
+      const float L = halves ? estL[e] + estL1[e] : estL[e];
+      const float S = halves ? estS[e] + estS1[e] : estS[e];
+      if (!(isfinite(L) && isfinite(S))) bad = true;
+      const double d = cert_delta(S);
+      const float vlo = __double2float_rd((double)L - d), vhi = __double2float_ru((double)L + d);
+      const float slo = 1.0f / (1.0f + expf(-vlo)), shi = 1.0f / (1.0f + expf(-vhi));
+      lo[q] = __double2float_rd((double)slo + (double)a.bias[e] - 0x1p-19);
+      hi[q] = __double2float_ru((double)shi + (double)a.bias[e] + 0x1p-19);
+    }
+  }
+  bad = __ballot(bad) != 0ull;
+  const float T = kth_largest(lo, ok, a.K, lane);      // the k-th largest lower end
+  uint64_t cm[4];
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    cm[q] = __ballot(ok[q] && (bad || hi[q] >= T));
+    n += __popcll(cm[q]);
+  }
+  // float64 logits of the candidates, kCertGroup per pass over the row, by
+  // the fixed procedure of k_router_logits
+  double c[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, sg[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int g0 = 0; g0 < n; g0 += kCertGroup) {
+    const int ng = min(kCertGroup, n - g0);
+    int eg[kCertGroup];
+    const uint16_t* wrow[kCertGroup];
+#pragma unroll
+    for (int j = 0; j < kCertGroup; ++j) {
+      eg[j] = j < ng ? nth_candidate(cm, g0 + j) : -1;
+      wrow[j] = a.wr + (size_t)(eg[j] >= 0 ? eg[j] : 0) * a.H;
+    }
+    double acc[kCertGroup];
+#pragma unroll
+    for (int j = 0; j < kCertGroup; ++j) acc[j] = 0.0;
+    // three chunks in flight: chunk i travels in stage i % 3
+    uint4 w0[kCertGroup], w1[kCertGroup], w2[kCertGroup];
+    cert_wload(w0, wrow, 0, lane, a.H);
+    cert_wload(w1, wrow, min(1, nch - 1), lane, a.H);
+    cert_wload(w2, wrow, min(2, nch - 1), lane, a.H);
+    for (int i = 0; i < nch; i += 3) {
+      cert_chunk(acc, w0, sxr, i, lane, a.H, ng);
+      cert_wload(w0, wrow, min(i + 3, nch - 1), lane, a.H);
+      if (i + 1 < nch) cert_chunk(acc, w1, sxr, i + 1, lane, a.H, ng);
+      cert_wload(w1, wrow, min(i + 4, nch - 1), lane, a.H);
+      if (i + 2 < nch) cert_chunk(acc, w2, sxr, i + 2, lane, a.H, ng);
+      cert_wload(w2, wrow, min(i + 5, nch - 1), lane, a.H);
+    }
+#pragma unroll
+    for (int j = 0; j < kCertGroup; ++j) {
+      if (j >= ng) break;
+      const double l = wave_sum_f64(acc[j]);
+      double sgj, cj;
+      route_score(l, a.bias[eg[j]], sgj, cj);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (eg[j] == lane + 64 * q) {
+          c[q] = cj;
+          sg[q] = sgj;
+        }
+    }
+  }
+  bool cand[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cand[q] = ((cm[q] >> lane) & 1ull) != 0ull;
+  select_scored(a, row, lane, c, sg, cand, nullptr);
 }
 
 // ---------------------------------------------------------------- union
@@ -639,13 +1016,19 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   }
   if (a.M <= kGroupedLogitRows) {
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_grouped<true>, dim3((unsigned)(a.E * ((a.M + 7) / 8))), dim3(512), 0, s, a);
-  } else {
+    MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
+  } else if (a.H > kCertMaxH) {
     const long groups8 = ((a.M + 7) / 8 + 7) / 8 * 8;     // row groups, padded to a multiple of 8
     constexpr int kEpw = 8;                                 // experts per wave (32 per workgroup)
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<kEpw>, dim3((unsigned)(groups8 * ((a.E + 4 * kEpw - 1) / (4 * kEpw)))),
                blk, 0, s, a);
+    MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
+  } else {
+    const int nte = (a.E + kEstExperts - 1) / kEstExperts;
+    const int jobs8 = (2 * ((a.M + kEstRows - 1) / kEstRows) + 7) / 8;     // (K half, row tile) jobs / 8
+    MOE_LAUNCH(KID_ROUTER_LOGITS, k_route_est, dim3((unsigned)(8 * jobs8 * nte)), blk, 0, s, a);
+    MOE_LAUNCH(KID_ROUTE_SELECT, k_route_cert, dim3((unsigned)((a.M + 3) / 4)), blk, (size_t)4 * a.H * 2, s, a);
   }
-  MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union_count, dim3(kUChunks), dim3(kMaxExperts), 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union_scan, dim3(1), dim3(kMaxExperts), 0, s, a);
   MOE_LAUNCH(KID_UNION, k_union_scatter, dim3(kUChunks), dim3(kMaxExperts), 0, s, a);
