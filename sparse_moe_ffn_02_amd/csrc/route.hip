@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- certified selection
-// Larger steps (mstar PR #388 router notes: only the top-k decision and the
+// Steps above kCertMinRows rows (mstar PR #388 router notes: only the top-k decision and the
 // picked experts' sigmoids leave the router).  The float64 logit is needed
 // only where it can change the decision, so the selection is certified:
 //
@@ -250,6 +250,10 @@ constexpr int kEstExperts = 64;
 constexpr int kEstK = 128;          // K per staged chunk
 constexpr int kCertGroup = 4;       // candidate logits per pass over the row
 constexpr int kCertMaxH = 8192;
+// Up to this many rows every logit in float64 is as fast (measured at hidden
+// 6144, 256 experts: 70 against 90 us at 256 rows, level at 384 and 512,
+// 114 against 95 at 768, 136 against 97 at 1024 for the whole routing).
+constexpr int kCertMinRows = 512;
 
 __device__ __forceinline__ double cert_delta(float S) {
   return (double)S * (0x1p-10 * (1.0 + 0x1p-8) + 0x1p-30) + 0x1p-100;
@@ -1017,7 +1021,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.M <= kGroupedLogitRows) {
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_logits_grouped<true>, dim3((unsigned)(a.E * ((a.M + 7) / 8))), dim3(512), 0, s, a);
     MOE_LAUNCH(KID_ROUTE_SELECT, k_route_select, dim3((a.M + 3) / 4), blk, 0, s, a);
-  } else if (a.H > kCertMaxH) {
+  } else if (a.H > kCertMaxH || a.M <= kCertMinRows) {
     const long groups8 = ((a.M + 7) / 8 + 7) / 8 * 8;     // row groups, padded to a multiple of 8
     constexpr int kEpw = 8;                                 // experts per wave (32 per workgroup)
     MOE_LAUNCH(KID_ROUTER_LOGITS, k_router_logits<kEpw>, dim3((unsigned)(groups8 * ((a.E + 4 * kEpw - 1) / (4 * kEpw)))),

@@ -10,9 +10,10 @@
 // straight into MFMA operand registers two K stages ahead, and applies them to
 // all 128 slots (eight 16-column MFMA tiles).  The tile's activation rows,
 // which all eight waves read, are staged through a double-buffered LDS ring.
-// All column tiles of one slot (or row) tile are numbered to run on one XCD,
-// one after another, so the tile's activation rows are read from HBM once and
-// from that XCD's L2 by the other column tiles (xcd_tile below).
+// With at least 8 slot (or row) tiles, all column tiles of one tile are
+// numbered to run on one XCD, one after another, so the tile's activation
+// rows are read from HBM once and from that XCD's L2 by the other column
+// tiles (xcd_tile, range_tile below).
 //
 // Every output element follows the same procedure as in the small-step
 // kernels: one fp8 16x16x128 MFMA per 128-deep K-block scaled into a fp32
@@ -54,6 +55,24 @@ __device__ __forceinline__ void xcd_tile(int r, int ncols, int& row, int& col) {
   const int x = r % kXcds, rest = r / kXcds;
   col = rest % ncols;
   row = (rest / ncols) * kXcds + x;
+}
+
+// The XCD grouping pays when every XCD gets row tiles of its own.  With
+// fewer than kXcdMinRows row tiles it would crowd the column tiles of the
+// few row tiles onto as many XCDs (a step of one row tile would run on one
+// XCD of eight), so the range is then dealt out in plain order: index r is
+// row tile r / ncols, column tile r % ncols, and the workgroups of one row
+// tile spread over all XCDs.  The range keeps its size (xcd_rows(nrows) *
+// ncols, a multiple of 8); indices past the real tiles return row >= nrows.
+constexpr int kXcdMinRows = 8;
+
+__device__ __forceinline__ void range_tile(int r, int nrows, int ncols, int& row, int& col) {
+  if (nrows >= kXcdMinRows) {
+    xcd_tile(r, ncols, row, col);
+  } else {
+    row = r / ncols;
+    col = r % ncols;
+  }
 }
 
 struct TileIn {
@@ -524,7 +543,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   Acc tot;
   if (bid < n_sh) {
     int mt, nt;
-    xcd_tile(bid, ntS, mt, nt);
+    range_tile(bid, nrow_sh, ntS, mt, nt);
     if (mt >= nrow_sh) return;
     // the row tile's 16-row groups holding rows, rounded up to 2, 4 or 8
     const int live = (min(kTM, a.M - mt * kTM) + 15) / 16;
@@ -537,7 +556,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
     return;
   }
   int it, nt;
-  xcd_tile(bid - n_sh, ntI, it, nt);
+  range_tile(bid - n_sh, mtiles, ntI, it, nt);
   if (it >= mtiles) return;
   const Tile tl = routed_tile(a, it);
   const int n0 = nt * kBlk + 16 * w;
@@ -685,7 +704,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
   Acc tot;
   if (bid < n_sh) {
     int mt, nt;
-    xcd_tile(bid, ntH, mt, nt);
+    range_tile(bid, nrow_sh, ntH, mt, nt);
     if (mt >= nrow_sh) return;
     // the row tile's 16-row groups holding rows, rounded up to 2, 4 or 8
     const int live = (min(kTM, a.M - mt * kTM) + 15) / 16;
@@ -698,7 +717,7 @@ __global__ __launch_bounds__(kTileThreads) void k_down_tiled(FfnArgs a) {
     return;
   }
   int it, nt;
-  xcd_tile(bid - n_sh, ntW, it, nt);
+  range_tile(bid - n_sh, mtiles, ntW, it, nt);
   if (it >= mtiles) return;
   const Tile tl = routed_tile(a, it);
   const int n0 = nt * kDnColsW + 16 * kWA * w;

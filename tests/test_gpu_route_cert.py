@@ -1,4 +1,4 @@
-"""The certified selection of larger steps (more than 128 rows: MFMA
+"""The certified selection of larger steps (more than 512 rows: MFMA
 estimates with an error bound, float64 logits only for the candidates) gives
 the ids and weights of the all-float64 selection bit for bit.
 
@@ -11,7 +11,8 @@ cancel (large sum |x| |w| against a small logit), rows holding an infinity
 routed once as one step (certified path) and again in 128-row steps (every
 logit in float64); ids and fp32 weights must match exactly, and the finite
 rows must also match the oracle (ids exactly, weights within one fp32
-rounding).
+rounding).  Three independent draws of the 256 rows below make one
+768-row step.
 """
 import numpy as np
 import pytest
@@ -90,7 +91,10 @@ def test_certified_selection_equals_float64_selection(name):
     rng = np.random.default_rng(4242 + h)
     d = moe.Dims(h, e, k, 256, 0)
     wr, b = router(h, e, rng)
-    x, mask, finite = rows(h, wr, rng)
+    parts = [rows(h, wr, rng) for _ in range(3)]           # 768 rows: the certified path
+    x = np.concatenate([p[0] for p in parts])
+    mask = np.concatenate([p[1] for p in parts])
+    finite = np.concatenate([p[2] for p in parts])
     say(f"certified routing {name}: M={x.shape[0]} H={h} E={e} k={k}")
     ids_c, w_c = route(d, x, mask, wr, b)
     ids_f, w_f = route(d, x, mask, wr, b, split=128)
@@ -102,6 +106,6 @@ def test_certified_selection_equals_float64_selection(name):
     ref = o_w.astype(np.float32)
     assert np.all(np.abs(w_c[keep].astype(np.float64) - o_w) <= np.spacing(np.abs(ref)).astype(np.float64))
     # the constructed ties really sit at the decision: some rows pick one expert of a tied pair only
-    split_pairs = sum(1 for r in ids_c[keep] for j in range(0, e, 4) if (j in r) != (j + 2 in r))
+    split_pairs = sum(1 for r in ids_c[keep] for j in range(0, e - 2, 4) if (j in r) != (j + 2 in r))
     say(f"  rows x tied pairs split by the k-th place: {split_pairs}")
     assert (ids_c[mask == 0] == -1).all()
