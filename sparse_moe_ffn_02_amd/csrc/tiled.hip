@@ -9,7 +9,8 @@
 // see the wide tiles below), streams them from global memory
 // straight into MFMA operand registers two K stages ahead, and applies them to
 // all 128 slots (eight 16-column MFMA tiles).  The tile's activation rows,
-// which all eight waves read, are staged through a double-buffered LDS ring.
+// which all eight waves read, are staged through a ring of LDS buffers (four
+// where the weight ring is two stages deep: one barrier per two K stages).
 // With at least 8 slot (or row) tiles, all column tiles of one tile are
 // numbered to run on one XCD, one after another, so the tile's activation
 // rows are read from HBM once and from that XCD's L2 by the other column
@@ -86,10 +87,24 @@ struct TileIn {
   int nseg;              // K segments (fp8: over K-blocks; bf16: over 32-deep K steps)
 };
 
+constexpr int kLdsStages = 4;              // LDS activation stage buffers
+
 struct TileLds {
-  uint8_t b[2][kTM * kLdsRow];
-  float s[2][kTM];
+  uint8_t b[kLdsStages][kTM * kLdsRow];
+  float s[kLdsStages][kTM];
 };
+
+// An LDS float pointer the compiler cannot see through.  Reads at constant
+// offsets from it become one base register with immediate offsets; from a
+// base it can see through, the compiler materializes one address register per
+// (stage buffer, slot tile) and spills them.
+typedef __attribute__((address_space(3))) const float lds_cf;
+
+__device__ __forceinline__ lds_cf* opaque_lds(const void* p) {
+  lds_cf* r = (lds_cf*)p;
+  asm volatile("" : "+v"(r));
+  return r;
+}
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -192,15 +207,16 @@ __device__ __forceinline__ void close_segments(SegState& g, int done, Acc& acc, 
 }
 
 // MFMA B fragments (and activation scales) of slot tiles b and b + 1 from an
-// LDS activation stage: lane (q, c) takes 32 bytes of row 16 b + c at 32 q.
-__device__ __forceinline__ void lds_frag_pair(const uint8_t* lb, const float* ls, int b, int c, int q, v8i (&x)[2],
+// LDS activation stage: lane (q, c) takes 32 bytes of row 16 b + c at 32 q;
+// ls points at the stage's scale of row c.
+__device__ __forceinline__ void lds_frag_pair(const uint8_t* lb, lds_cf* ls, int b, int c, int q, v8i (&x)[2],
                                               float (&s)[2]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint8_t* src = lb + (16 * (b + j) + c) * kLdsRow + q * 32;
     const uint4 lo = ld16(src), hi = ld16(src + 16);
     x[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    s[j] = ls[16 * (b + j) + c];
+    s[j] = ls[16 * (b + j)];
   }
 }
 
@@ -219,10 +235,11 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
     // per pair.
     v8i xb[2], xn[2];
     float sx[2], sxn[2];
-    lds_frag_pair(L.b[buf], L.s[buf], 0, c, q, xb, sx);
+    lds_cf* ls = opaque_lds(&L.s[0][c]) + buf * kTM;
+    lds_frag_pair(L.b[buf], ls, 0, c, q, xb, sx);
 #pragma unroll
     for (int b = 0; b < NL; b += 2) {
-      if (b + 2 < NL) lds_frag_pair(L.b[buf], L.s[buf], b + 2, c, q, xn, sxn);
+      if (b + 2 < NL) lds_frag_pair(L.b[buf], ls, b + 2, c, q, xn, sxn);
       v4f p0 = mfma_fp8_raw(a[0], xb[0]), p1 = mfma_fp8_raw(a[1], xb[0]);
       v4f p2 = mfma_fp8_raw(a[0], xb[1]), p3 = mfma_fp8_raw(a[1], xb[1]);
       settle4(p0, p1, p2, p3);
@@ -266,8 +283,15 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
 // The K loop of one tile: tot[t][b] = the element values of A tile t by slot
 // tile b (lane layout of the 16x16 MFMA output).  Weight fragments and their
 // block scales are loaded kRingA stages ahead into registers (3 where the
-// registers allow it, else 2); activation rows two stages ahead into
-// registers, then into the LDS double buffer one stage ahead.
+// registers allow it, else 2).
+//   kRingA = 3: activation rows are loaded two stages ahead into registers,
+//     then written to LDS buffer (s + 1) % 2 during stage s; one barrier per
+//     stage.
+//   kRingA = 2: four LDS buffers; stages s, s + 1 (s even) read buffers
+//     s % 4, (s + 1) % 4 and write stages s + 2, s + 3 into the other two,
+//     each stage loading the rows it writes at its start, then one barrier.
+//     The barrier count halves and a wave that finishes its stage early goes
+//     on to the next one instead of waiting.
 template <bool kFp8, int kRingA, int NL = kNB>
 __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
   static_assert(kRingA == 2 || kRingA == 3, "weight ring of 2 or 3 stages");
@@ -297,14 +321,45 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
   const int last = n - 1;
   load_a<kFp8>(ar0, in, 0);
   load_a<kFp8>(ar1, in, min(1, last));
-  if (kRingA == 3) load_a<kFp8>(ar2, in, min(2, last));
+  if (kRingA == 2) {
+    load_b<kFp8>(br0, in, 0);
+    load_b<kFp8>(br1, in, min(1, last));
+    store_b<kFp8>(L, 0, br0, in);
+    store_b<kFp8>(L, 1, br1, in);
+    __syncthreads();
+    // Stage st0 + D on buffer D (st0 a multiple of 4): load the activations
+    // of stage st + 2, compute, refill the weight register set AR two stages
+    // ahead, write stage st + 2 to buffer (D + 2) % 4; a barrier after odd D.
+#define MOE_TILE_STEP2(D, AR, SYNC)                            \
+  {                                                            \
+    const int st = st0 + (D);                                  \
+    load_b<kFp8>(br0, in, min(st + 2, last));                  \
+    tile_stage<kFp8, NL>(L, (D), AR, st, acc, tot, g);         \
+    load_a<kFp8>(AR, in, min(st + 2, last));                   \
+    store_b<kFp8>(L, ((D) + 2) & 3, br0, in);                  \
+    if (SYNC) __syncthreads();                                 \
+  }
+    int st0 = 0;
+    for (; st0 + 4 <= n; st0 += 4) {
+      MOE_TILE_STEP2(0, ar0, false)
+      MOE_TILE_STEP2(1, ar1, true)
+      MOE_TILE_STEP2(2, ar0, false)
+      MOE_TILE_STEP2(3, ar1, true)
+    }
+    if (st0 < n) MOE_TILE_STEP2(0, ar0, false)
+    if (st0 + 1 < n) MOE_TILE_STEP2(1, ar1, true)
+    if (st0 + 2 < n) MOE_TILE_STEP2(2, ar0, false)
+#undef MOE_TILE_STEP2
+    return;
+  }
+  load_a<kFp8>(ar2, in, min(2, last));
   load_b<kFp8>(br0, in, 0);
   store_b<kFp8>(L, 0, br0, in);
   load_b<kFp8>(br1, in, min(1, last));
   load_b<kFp8>(br0, in, min(2, last));
   __syncthreads();
   // One stage (st0 + D): compute on LDS buffer U with weights AR, refill AR
-  // kRingA stages ahead, write the next stage's activations (register set
+  // three stages ahead, write the next stage's activations (register set
   // BN) to the other buffer and refill BN three stages ahead.  The loop is
   // unrolled by 6 so that the weight ring (3) and the LDS / activation
   // rings (2) all use compile-time indices.
@@ -313,25 +368,18 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
     const int st = st0 + (D);                                  \
     if (st >= n) break;                                        \
     tile_stage<kFp8, NL>(L, (U), AR, st, acc, tot, g);         \
-    load_a<kFp8>(AR, in, min(st + kRingA, last));              \
+    load_a<kFp8>(AR, in, min(st + 3, last));                   \
     store_b<kFp8>(L, (U) ^ 1, BN, in);                         \
     load_b<kFp8>(BN, in, min(st + 3, last));                   \
     __syncthreads();                                           \
   }
-  if (kRingA == 3) {
-    for (int st0 = 0; st0 < n; st0 += 6) {
-      MOE_TILE_STEP(0, 0, ar0, br1)
-      MOE_TILE_STEP(1, 1, ar1, br0)
-      MOE_TILE_STEP(2, 0, ar2, br1)
-      MOE_TILE_STEP(3, 1, ar0, br0)
-      MOE_TILE_STEP(4, 0, ar1, br1)
-      MOE_TILE_STEP(5, 1, ar2, br0)
-    }
-  } else {
-    for (int st0 = 0; st0 < n; st0 += 2) {
-      MOE_TILE_STEP(0, 0, ar0, br1)
-      MOE_TILE_STEP(1, 1, ar1, br0)
-    }
+  for (int st0 = 0; st0 < n; st0 += 6) {
+    MOE_TILE_STEP(0, 0, ar0, br1)
+    MOE_TILE_STEP(1, 1, ar1, br0)
+    MOE_TILE_STEP(2, 0, ar2, br1)
+    MOE_TILE_STEP(3, 1, ar0, br0)
+    MOE_TILE_STEP(4, 0, ar1, br1)
+    MOE_TILE_STEP(5, 1, ar2, br0)
   }
 #undef MOE_TILE_STEP
 }
@@ -348,8 +396,8 @@ constexpr int kWA = 4;                                                // 16-row 
 constexpr int kWBV = kTM * kStageBytes / kTileThreads / 16;           // 16-byte activation loads per thread per K-block
 constexpr int kWBRow = kTileThreads / 8;                              // rows between a thread's loads
 constexpr int kWBuf = kTM * kLdsRow;                                  // one activation stage in LDS
-constexpr int kWLdsB = 2 * kWBuf;                                     // double buffer
-constexpr int kWLds = kWLdsB + 2 * kTM * (int)sizeof(float);         // + the activation scales
+constexpr int kWLdsB = kLdsStages * kWBuf;                           // stage buffers
+constexpr int kWLds = kWLdsB + kLdsStages * kTM * (int)sizeof(float); // + the activation scales
 
 struct WideIn {
   const uint8_t* a;       // per lane: packed-tile address of weight tile 0 at K-block 0
@@ -417,14 +465,14 @@ template <int NL>
 __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const WStage& as, WAcc& acc) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const uint8_t* lb = smem + buf * kWBuf;
-  const float* ls = reinterpret_cast<const float*>(smem + kWLdsB) + buf * kTM;
+  lds_cf* ls = opaque_lds(smem + kWLdsB + c * sizeof(float)) + buf * kTM;
   const float sw = as.s;
   // the next slot tile's fragment is read from LDS while this tile's MFMAs run
   auto frag = [&](int b, v8i& x, float& sx) {
     const uint8_t* src = lb + (16 * b + c) * kLdsRow + q * 32;
     const uint4 lo = ld16(src), hi = ld16(src + 16);
     x = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    sx = ls[16 * b + c];
+    sx = ls[16 * b];
   };
   v8i xb, xn;
   float sx, sxn;
@@ -451,10 +499,12 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
 }
 
 // The K loop of one wide tile: acc = the element chains over all K-blocks.
-// Weight fragments are loaded two K-blocks ahead into registers; a thread's
-// activation rows one K-block ahead into registers, then into the LDS double
-// buffer.  Loads past the last K-block reload it (valid, unused), so every
-// step issues the same loads with no branch around them.
+// Weight fragments are loaded two K-blocks ahead into registers.  Four LDS
+// stage buffers: K-blocks s, s + 1 (s even) read buffers s % 4, (s + 1) % 4
+// and write K-blocks s + 2, s + 3 into the other two, then one barrier; a
+// thread's activation rows are loaded into registers one K-block before
+// they are written.  Loads past the last K-block reload it (valid, unused),
+// so every step issues the same loads with no branch around them.
 template <int NL>
 __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc& acc) {
   const int n = in.nkb, last = n - 1;
@@ -473,22 +523,30 @@ __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc&
   wide_load_b(br, in, 0);
   wide_store_b(smem, 0, br, in);
   wide_load_b(br, in, min(1, last));
+  wide_store_b(smem, 1, br, in);
+  wide_load_b(br, in, min(2, last));
   __syncthreads();
-#define MOE_WIDE_STEP(S, D, AR)                         \
+  // K-block s0 + D on buffer D (s0 a multiple of 4); br holds K-block s0 + D + 2
+#define MOE_WIDE_STEP(D, AR, SYNC)                      \
   {                                                     \
+    const int st = s0 + (D);                            \
     wide_stage<NL>(smem, (D), AR, acc);                 \
-    wide_load_a(AR, in, min((S) + 2, last));            \
-    wide_store_b(smem, (D) ^ 1, br, in);                \
-    wide_load_b(br, in, min((S) + 2, last));            \
-    __syncthreads();                                    \
+    wide_load_a(AR, in, min(st + 2, last));             \
+    wide_store_b(smem, ((D) + 2) & 3, br, in);          \
+    wide_load_b(br, in, min(st + 3, last));             \
+    if (SYNC) __syncthreads();                          \
   }
-  // pairs of steps (the ring indices are compile-time), then an odd last step
+  // groups of four steps (the ring indices are compile-time), then the rest
   int s0 = 0;
-  for (; s0 + 2 <= n; s0 += 2) {
-    MOE_WIDE_STEP(s0, 0, ar0)
-    MOE_WIDE_STEP(s0 + 1, 1, ar1)
+  for (; s0 + 4 <= n; s0 += 4) {
+    MOE_WIDE_STEP(0, ar0, false)
+    MOE_WIDE_STEP(1, ar1, true)
+    MOE_WIDE_STEP(2, ar0, false)
+    MOE_WIDE_STEP(3, ar1, true)
   }
-  if (s0 < n) MOE_WIDE_STEP(s0, 0, ar0)
+  if (s0 < n) MOE_WIDE_STEP(0, ar0, false)
+  if (s0 + 1 < n) MOE_WIDE_STEP(1, ar1, true)
+  if (s0 + 2 < n) MOE_WIDE_STEP(2, ar0, false)
 #undef MOE_WIDE_STEP
 }
 
