@@ -76,27 +76,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Finite fp32 -> OCP e4m3 (bias 7, max 448) code, round to nearest even,
-// magnitudes at or above 448 saturate to 448.  Integer arithmetic only.
+// fp32 -> OCP e4m3 (bias 7, max 448) code, round to nearest even; magnitudes
+// at or above 448, infinities and NaN saturate to 448 with the sign kept.
+// gfx950's v_cvt_pk_fp8_f32 rounds to nearest even into OCP e4m3 and agrees
+// with the format's integer rounding (grid 2^-9 below 2^-6, 4 significant
+// bits above, ties to even) for every fp32 of magnitude below 464, both
+// signs, zeros and subnormals included (an exhaustive device check); the
+// saturated magnitudes take the explicit code.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   const uint32_t b = __float_as_uint(v);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t a = b & 0x7fffffffu;
-  uint32_t code;
-  if (a >= 0x43e00000u) {                 // |v| >= 448
-    code = 0x7eu;
-  } else if (a < 0x3c800000u) {           // |v| < 2^-6: grid of 2^-9
-    // |v| * 2^9 < 8 is exact; rintf rounds to nearest even.
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    const uint32_t e = (a >> 23) - 127u + 7u;          // biased e4m3 exponent, 1..15
-    const uint32_t mant = (a & 0x7fffffu) | 0x800000u; // 24-bit significand
-    uint32_t q = mant >> 20;                           // 4 significant bits, 8..15
-    const uint32_t rem = mant & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;   // may reach 16: carries
-    code = (e << 3) + q - 8u;
-  }
-  return code | sign;
+  const uint32_t sat = ((b >> 24) & 0x80u) | 0x7eu;
+  const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
+  return (b & 0x7fffffffu) >= 0x43e00000u ? sat : hw;
 }
 
 // Per-block quantization scale: s = fl32(amax / 448), s = 1 for a zero block.

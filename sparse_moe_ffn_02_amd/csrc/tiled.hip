@@ -502,8 +502,8 @@ __device__ __forceinline__ void wide_stage(const uint8_t* smem, int buf, const W
 // Weight fragments are loaded two K-blocks ahead into registers.  Four LDS
 // stage buffers: K-blocks s, s + 1 (s even) read buffers s % 4, (s + 1) % 4
 // and write K-blocks s + 2, s + 3 into the other two, then one barrier; a
-// thread's activation rows are loaded into registers one K-block before
-// they are written.  Loads past the last K-block reload it (valid, unused),
+// thread's activation rows for the K-block it writes are loaded into
+// registers at the start of the step, so the compute covers their latency.  Loads past the last K-block reload it (valid, unused),
 // so every step issues the same loads with no branch around them.
 template <int NL>
 __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc& acc) {
@@ -524,16 +524,16 @@ __device__ __forceinline__ void wide_gemm(const WideIn& in, uint8_t* smem, WAcc&
   wide_store_b(smem, 0, br, in);
   wide_load_b(br, in, min(1, last));
   wide_store_b(smem, 1, br, in);
-  wide_load_b(br, in, min(2, last));
   __syncthreads();
-  // K-block s0 + D on buffer D (s0 a multiple of 4); br holds K-block s0 + D + 2
+  // K-block s0 + D on buffer D (s0 a multiple of 4): load the activation rows
+  // of K-block st + 2, compute, refill AR, write st + 2 to buffer (D + 2) % 4
 #define MOE_WIDE_STEP(D, AR, SYNC)                      \
   {                                                     \
     const int st = s0 + (D);                            \
+    wide_load_b(br, in, min(st + 2, last));             \
     wide_stage<NL>(smem, (D), AR, acc);                 \
     wide_load_a(AR, in, min(st + 2, last));             \
     wide_store_b(smem, ((D) + 2) & 3, br, in);          \
-    wide_load_b(br, in, min(st + 3, last));             \
     if (SYNC) __syncthreads();                          \
   }
   // groups of four steps (the ring indices are compile-time), then the rest

@@ -63,6 +63,52 @@ def test_quant_unit_bit_exact():
     assert np.array_equal(gc.cpu().numpy(), oc2)
 
 
+def test_quant_code_sweep():
+    """The fp32 -> e4m3 code step over a dense sweep of the format's domain.
+
+    Every 128-value block holds 448 at its first position, so its scale is
+    exactly 1 and the other 127 values are coded as they are.  The values:
+    every 61st fp32 bit pattern of magnitude below 448, every pattern within
+    4 ulps of each e4m3 value and of each rounding midpoint, each with a
+    random sign.  Codes must equal the oracle's round-to-nearest-even rule.
+    """
+    rng = np.random.default_rng(33)
+    top = np.float32(448.0).view(np.uint32)
+    sweep = np.arange(0, top, 61, dtype=np.uint32)
+    grid = oracle.E4M3_TABLE[:0x7F].astype(np.float32)            # 0 .. 448
+    mids = ((oracle.E4M3_TABLE[:0x7E] + oracle.E4M3_TABLE[1:0x7F]) / 2).astype(np.float32)
+    near = np.concatenate([grid, mids]).view(np.uint32).astype(np.int64)
+    near = (near[:, None] + np.arange(-4, 5)[None, :]).ravel()
+    near = near[(near >= 0) & (near < top)].astype(np.uint32)
+    mags = np.concatenate([sweep, near]).view(np.float32)
+    vals = np.where(rng.random(mags.size) < 0.5, -mags, mags).astype(np.float32)
+    per = 127
+    nblk = -(-vals.size // per)
+    blocks = np.zeros((nblk, 128), np.float32)
+    blocks[:, 0] = 448.0
+    flat = np.zeros(nblk * per, np.float32)
+    flat[:vals.size] = vals
+    blocks[:, 1:] = flat.reshape(nblk, per)
+    cols = 8192
+    nb_row = cols // 128
+    nrow = -(-nblk // nb_row)
+    v = np.zeros((nrow * nb_row, 128), np.float32)
+    v[:, 0] = 448.0
+    v[:nblk] = blocks
+    v = v.reshape(nrow, cols)
+    say("quant sweep", v.shape, "values", vals.size)
+    gc = torch.empty((nrow, cols), dtype=torch.uint8, device="cuda")
+    gs = torch.empty((nrow, nb_row), dtype=torch.float32, device="cuda")
+    moe.quant_fp8(tf(v), gc, gs)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quant_1x128(v)
+    assert np.all(os_ == 1.0)
+    assert np.array_equal(gs.cpu().numpy(), os_)
+    got = gc.cpu().numpy()
+    bad = np.flatnonzero(got.ravel() != oc.ravel())
+    assert bad.size == 0, f"{bad.size} codes differ, first at value {v.ravel()[bad[0]]!r}"
+
+
 def _packed_reference(a: np.ndarray, is_bf16: bool) -> np.ndarray:
     """The documented tile layout, built index by index from row-major bytes."""
     b = np.ascontiguousarray(a).view(np.uint8).reshape(a.shape[0], -1)
