@@ -28,40 +28,82 @@
 
 namespace moe {
 
+// Eight consecutive values of a row as fp32 (bf16: one 16-byte load; fp32:
+// two).
 template <typename T>
-__device__ __forceinline__ float load_as_f32(const T* p);
+__device__ __forceinline__ void load8_f32(const T* p, float (&v)[8]);
 template <>
-__device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
+__device__ __forceinline__ void load8_f32<float>(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 template <>
-__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void load8_f32<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// max over the 16 lanes of a DPP row (every lane of the row gets it)
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+  return v;
+}
 
 // rows [0, R) of a [R, C] matrix; rows with mask 0 are skipped (never read).
-// One wave per (row, group of kQGroup 128-column blocks): the group's loads
-// are issued together, then each block is quantized as on its own.
+// One wave per (row, group of kQGroup 128-column blocks).  The 16 lanes of a
+// DPP row hold one block, 8 values each, so a wave covers 4 blocks per
+// step: one 16-byte load (bf16) and one 8-byte store of codes per lane, the
+// block maximum from 4 DPP steps.  Each block is quantized as on its own
+// (the same rule as quant_pair: s = fl32(amax / 448), codes of v / s, all
+// codes 0 for a zero block).
 constexpr int kQGroup = 8;
+constexpr int kQSteps = kQGroup / 4;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant_rows(const T* in, const uint8_t* mask, int R, int C, uint8_t* codes,
                                                     float* scales) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, part = lane & 15, sub = lane >> 4;
   const int nb = C / kBlk;
   const int ng = (nb + kQGroup - 1) / kQGroup;
   const long item = (long)blockIdx.x * 4 + wave_id();
   const int r = (int)(item / ng);
   const int b0 = (int)(item % ng) * kQGroup;
   if (r >= R || !row_real(mask, r)) return;
-  const T* p = in + (size_t)r * C + 2 * lane;
-  float v[kQGroup][2];
+  const T* p = in + (size_t)r * C + part * 8;
+  float v[kQSteps][8];
 #pragma unroll
-  for (int i = 0; i < kQGroup; ++i) {
-    const int b = min(b0 + i, nb - 1);          // past the row's end: reload its last block, not stored
-    v[i][0] = load_as_f32<T>(p + b * kBlk);
-    v[i][1] = load_as_f32<T>(p + b * kBlk + 1);
+  for (int i = 0; i < kQSteps; ++i) {
+    const int b = min(b0 + 4 * i + sub, nb - 1);   // past the row's end: reload its last block, not stored
+    load8_f32<T>(p + b * kBlk, v[i]);
   }
 #pragma unroll
-  for (int i = 0; i < kQGroup; ++i) {
-    const int b = b0 + i;
-    if (b < nb) quant_pair(v[i][0], v[i][1], codes + (size_t)r * C + b * kBlk, scales + (size_t)r * nb + b, lane);
+  for (int i = 0; i < kQSteps; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[i][k]));
+    const float amax = row16_max(m);
+    const float s = quant_scale(amax);
+    uint32_t lo = 0, hi = 0;
+    if (amax != 0.0f) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lo |= quant_code(v[i][k], s) << (8 * k);
+        hi |= quant_code(v[i][4 + k], s) << (8 * k);
+      }
+    }
+    const int b = b0 + 4 * i + sub;
+    if (b < nb) {
+      *reinterpret_cast<uint2*>(codes + (size_t)r * C + b * kBlk + part * 8) = make_uint2(lo, hi);
+      if (part == 0) scales[(size_t)r * nb + b] = s;
+    }
   }
 }
 
