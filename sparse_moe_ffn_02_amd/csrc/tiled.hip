@@ -646,9 +646,11 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
     tile_gemm<true, 2, 4>(in, L, tot);
   else
     tile_gemm<true, 2, kNB>(in, L, tot);
-  // h = silu(G) U in place of G; 1x128 requantization over the tile's 128 columns
+  // h = silu(G) U in place of G; 1x128 requantization over the tile's 128
+  // columns; slot tiles past the last one holding rows are skipped
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
+    if (b >= live) break;
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -665,6 +667,7 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   __syncthreads();
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
+    if (b >= live) break;
     const int i = 16 * b + c;
     if (i >= tl.mcnt) continue;
     const int slot = tl.s0 + i;
