@@ -9,8 +9,8 @@
 // see the wide tiles below), streams them from global memory
 // straight into MFMA operand registers two K stages ahead, and applies them to
 // all 128 slots (eight 16-column MFMA tiles).  The tile's activation rows,
-// which all eight waves read, are staged through a ring of LDS buffers (four
-// where the weight ring is two stages deep: one barrier per two K stages).
+// which all eight waves read, are staged through four LDS buffers with one
+// barrier per two K stages (tile_gemm, wide_gemm).
 // With at least 8 slot (or row) tiles, all column tiles of one tile are
 // numbered to run on one XCD, one after another, so the tile's activation
 // rows are read from HBM once and from that XCD's L2 by the other column
@@ -282,19 +282,15 @@ __device__ __forceinline__ void tile_stage(const TileLds& L, int buf, const ASta
 
 // The K loop of one tile: tot[t][b] = the element values of A tile t by slot
 // tile b (lane layout of the 16x16 MFMA output).  Weight fragments and their
-// block scales are loaded kRingA stages ahead into registers (3 where the
-// registers allow it, else 2).
-//   kRingA = 3: activation rows are loaded two stages ahead into registers,
-//     then written to LDS buffer (s + 1) % 2 during stage s; one barrier per
-//     stage.
-//   kRingA = 2: four LDS buffers; stages s, s + 1 (s even) read buffers
-//     s % 4, (s + 1) % 4 and write stages s + 2, s + 3 into the other two,
-//     each stage loading the rows it writes at its start, then one barrier.
-//     The barrier count halves and a wave that finishes its stage early goes
-//     on to the next one instead of waiting.
-template <bool kFp8, int kRingA, int NL = kNB>
+// block scales are loaded two stages ahead into registers.  The activation
+// rows go through four LDS stage buffers: stages s, s + 1 (s even) read
+// buffers s % 4, (s + 1) % 4 and write stages s + 2, s + 3 into the other
+// two, each stage loading the rows it writes at its start (its compute
+// covers their latency), then one barrier closes the pair.  With a double
+// buffer every stage needs a barrier, and the two waves of a SIMD run in
+// lockstep: the faster one idles at every barrier.
+template <bool kFp8, int NL = kNB>
 __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot) {
-  static_assert(kRingA == 2 || kRingA == 3, "weight ring of 2 or 3 stages");
   static_assert(NL % 2 == 0 && NL >= 2 && NL <= kNB, "slot tiles in pairs");
   // keeps the first loads below the caller's branch between instantiations
   // (hoisted above it they stretch live ranges across all of them)
@@ -314,23 +310,24 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
   g.end = seg_begin(g.nunits, 1, g.nseg);
   close_segments<kFp8>(g, 0, acc, tot);
   const int n = in.nstage;
-  AStage ar0, ar1, ar2;            // weight ring (kRingA stages)
-  BStage br0, br1;                 // activation register ring (two stages)
-  // Ring refills past the last stage reload stage n - 1 (in range, unused):
-  // the loop issues the same loads every stage, with no branch around them.
+  AStage ar0, ar1;                 // weight ring (two stages)
+  BStage br0, br1;
+  // Refills past the last stage reload stage n - 1 (in range, unused): every
+  // step issues the same loads, with no branch around them.
   const int last = n - 1;
   load_a<kFp8>(ar0, in, 0);
   load_a<kFp8>(ar1, in, min(1, last));
-  if (kRingA == 2) {
-    load_b<kFp8>(br0, in, 0);
-    load_b<kFp8>(br1, in, min(1, last));
-    store_b<kFp8>(L, 0, br0, in);
-    store_b<kFp8>(L, 1, br1, in);
-    __syncthreads();
-    // Stage st0 + D on buffer D (st0 a multiple of 4): load the activations
-    // of stage st + 2, compute, refill the weight register set AR two stages
-    // ahead, write stage st + 2 to buffer (D + 2) % 4; a barrier after odd D.
-#define MOE_TILE_STEP2(D, AR, SYNC)                            \
+  load_b<kFp8>(br0, in, 0);
+  load_b<kFp8>(br1, in, min(1, last));
+  store_b<kFp8>(L, 0, br0, in);
+  store_b<kFp8>(L, 1, br1, in);
+  __syncthreads();
+  // Stage st0 + D on buffer D (st0 a multiple of 4): load the activations of
+  // stage st + 2, compute, refill the weight register set AR two stages
+  // ahead, write stage st + 2 to buffer (D + 2) % 4; a barrier after odd D.
+  // Unrolled by four (compile-time buffer indices), the remaining steps
+  // guarded after the loop.
+#define MOE_TILE_STEP(D, AR, SYNC)                             \
   {                                                            \
     const int st = st0 + (D);                                  \
     load_b<kFp8>(br0, in, min(st + 2, last));                  \
@@ -339,48 +336,16 @@ __device__ __forceinline__ void tile_gemm(const TileIn& in, TileLds& L, Acc& tot
     store_b<kFp8>(L, ((D) + 2) & 3, br0, in);                  \
     if (SYNC) __syncthreads();                                 \
   }
-    int st0 = 0;
-    for (; st0 + 4 <= n; st0 += 4) {
-      MOE_TILE_STEP2(0, ar0, false)
-      MOE_TILE_STEP2(1, ar1, true)
-      MOE_TILE_STEP2(2, ar0, false)
-      MOE_TILE_STEP2(3, ar1, true)
-    }
-    if (st0 < n) MOE_TILE_STEP2(0, ar0, false)
-    if (st0 + 1 < n) MOE_TILE_STEP2(1, ar1, true)
-    if (st0 + 2 < n) MOE_TILE_STEP2(2, ar0, false)
-#undef MOE_TILE_STEP2
-    return;
+  int st0 = 0;
+  for (; st0 + 4 <= n; st0 += 4) {
+    MOE_TILE_STEP(0, ar0, false)
+    MOE_TILE_STEP(1, ar1, true)
+    MOE_TILE_STEP(2, ar0, false)
+    MOE_TILE_STEP(3, ar1, true)
   }
-  load_a<kFp8>(ar2, in, min(2, last));
-  load_b<kFp8>(br0, in, 0);
-  store_b<kFp8>(L, 0, br0, in);
-  load_b<kFp8>(br1, in, min(1, last));
-  load_b<kFp8>(br0, in, min(2, last));
-  __syncthreads();
-  // One stage (st0 + D): compute on LDS buffer U with weights AR, refill AR
-  // three stages ahead, write the next stage's activations (register set
-  // BN) to the other buffer and refill BN three stages ahead.  The loop is
-  // unrolled by 6 so that the weight ring (3) and the LDS / activation
-  // rings (2) all use compile-time indices.
-#define MOE_TILE_STEP(D, U, AR, BN)                            \
-  {                                                            \
-    const int st = st0 + (D);                                  \
-    if (st >= n) break;                                        \
-    tile_stage<kFp8, NL>(L, (U), AR, st, acc, tot, g);         \
-    load_a<kFp8>(AR, in, min(st + 3, last));                   \
-    store_b<kFp8>(L, (U) ^ 1, BN, in);                         \
-    load_b<kFp8>(BN, in, min(st + 3, last));                   \
-    __syncthreads();                                           \
-  }
-  for (int st0 = 0; st0 < n; st0 += 6) {
-    MOE_TILE_STEP(0, 0, ar0, br1)
-    MOE_TILE_STEP(1, 1, ar1, br0)
-    MOE_TILE_STEP(2, 0, ar2, br1)
-    MOE_TILE_STEP(3, 1, ar0, br0)
-    MOE_TILE_STEP(4, 0, ar1, br1)
-    MOE_TILE_STEP(5, 1, ar2, br0)
-  }
+  if (st0 < n) MOE_TILE_STEP(0, ar0, false)
+  if (st0 + 1 < n) MOE_TILE_STEP(1, ar1, true)
+  if (st0 + 2 < n) MOE_TILE_STEP(2, ar0, false)
 #undef MOE_TILE_STEP
 }
 
@@ -574,7 +539,7 @@ __device__ __forceinline__ void shared_gateup_tile(const FfnArgs& a, TileLds& L,
   in.nstage = a.H * 2 / kStageBytes;
   in.nseg = kSegSG;
   Acc tot;
-  tile_gemm<false, 3, NL>(in, L, tot);
+  tile_gemm<false, NL>(in, L, tot);
 #pragma unroll
   for (int b = 0; b < NL; ++b) {
     const int row = mt * kTM + 16 * b + c;
@@ -641,11 +606,11 @@ __global__ __launch_bounds__(kTileThreads) void k_gateup_tiled(FfnArgs a) {
   // the slot tiles holding real rows, rounded up to 2, 4 or 8
   const int live = (tl.mcnt + 15) / 16;
   if (live <= 2)
-    tile_gemm<true, 2, 2>(in, L, tot);
+    tile_gemm<true, 2>(in, L, tot);
   else if (live <= 4)
-    tile_gemm<true, 2, 4>(in, L, tot);
+    tile_gemm<true, 4>(in, L, tot);
   else
-    tile_gemm<true, 2, kNB>(in, L, tot);
+    tile_gemm<true, kNB>(in, L, tot);
   // h = silu(G) U in place of G; 1x128 requantization over the tile's 128
   // columns; slot tiles past the last one holding rows are skipped
 #pragma unroll
@@ -722,7 +687,7 @@ __device__ __forceinline__ void shared_down_tile(const FfnArgs& a, TileLds& L, i
   in.nstage = a.Is * 2 / kStageBytes;
   in.nseg = kSegSD;
   Acc tot;
-  tile_gemm<false, 2, NL>(in, L, tot);
+  tile_gemm<false, NL>(in, L, tot);
   if (n0 >= a.H) return;
 #pragma unroll
   for (int b = 0; b < NL; ++b) {
