@@ -20,7 +20,7 @@ inline int split_rows(int inter) { return inter <= kNarrowInter ? kSmallRows : k
 // as the 16 MFMA columns, in row halves of kColRows: rows 16 h .. 16 h + 15.
 constexpr int kColRows = 16;
 __host__ __device__ inline int row_halves(int m) { return (m + kColRows - 1) / kColRows; }
-constexpr int kUChunks = 64;        // row chunks of the larger-step union
+constexpr int kUChunks = 128;       // row chunks of the larger-step union (4096 rows: 36 us for the three kernels, 48 with 64 chunks)
 // Every GEMM element is the fixed-order sum of its K-segment chains:
 // routed gate/up over kSegGU segments of K = H, shared gate/up over kSegSG,
 // routed down over kSegDN and shared down over kSegSD segments of K = I.  Small steps run each segment as its own work
