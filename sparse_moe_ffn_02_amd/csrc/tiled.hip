@@ -131,7 +131,8 @@ struct BStage {
 // Loads are unconditional (rows out of range read a valid row) so that no
 // branch separates a load from its wait and the compiler's in-order load
 // counting stays exact; rows out of range are zeroed when the registers are
-// written to LDS, stages later, so the loaded values are not touched early.
+// written to LDS after the stage's compute, so the loaded values are not
+// touched early.
 template <bool kFp8>
 __device__ __forceinline__ void load_b(BStage& r, const TileIn& in, int st) {
 #pragma unroll
